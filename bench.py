@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark of the EFLA chunked forward (and the decode step) on one MI355X.
+
+A step is one pass of the whole forward (coefficients, UT transform, state
+scan -- or the fused kernel) over one batch of the lm1.3b-bf16 workload
+(B=4, H=16, L=4096, d_k=d_v=128, chunk 64, bf16 inputs, fp32 state, random
+S0), with every input resident in HBM before the timed region.  Prints one
+JSON line.  The decode step (256 sequences x 16 heads, d=128, fp32 state) is
+timed in the same run and reported under "decode".
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload lm1.3b-bf16]
+                  [--path auto|staged|fused] [--no-cpu-baseline] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import delta_rule_sequence_alpha_amd as efla  # noqa: E402
+from delta_rule_sequence_alpha_amd import _lib  # noqa: E402
+import efla_workloads as wl  # noqa: E402
+
+METRIC = "EFLA chunked fwd tokens/s + % bf16 MFMA peak; decode-step state GB/s"
+HBM_PEAK = 8.0e12                      # B/s, MI355X HBM3E
+MFMA_PEAK = {"bf16": 2.5e15, "f32": 157.3e12}   # dense FLOP/s
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "delta_rule_sequence_alpha_amd", "csrc")
+
+
+# --- algorithmic work (per token-head unless stated) ------------------------
+
+def flops_per_token(dk, dv, C):
+    """Whole forward: W S, Q S, K^T E (2 dk dv each), tril(QK^T) E (C dv),
+    Gram and Q K^T lower triangles (C dk each), W = T K (C dk), U = T V (C dv),
+    T by substitution (C^2/3)."""
+    return 6 * dk * dv + C * (3 * dk + 2 * dv) + C * C / 3.0
+
+
+def stage_work(w, esz):
+    """(flops, bytes) per launch of each kernel of the staged path: minimal
+    bytes each kernel must move (inputs read once, outputs written once)."""
+    B, H, L, dk, dv, C = w.B, w.H, w.L, w.d_k, w.d_v, w.chunk
+    n = B * H * L
+    nch = B * H * ((L + C - 1) // C)
+    s0 = 4 * B * H * dk * dv
+    coef = (2 * dk * n, n * (dk * esz + 4 + 4))
+    ut = ((C * (3 * dk + dv) + C * C / 3.0) * n,
+          n * ((2 * dk + dv) * esz + 4) + n * (dk + dv) * esz + nch * C * C * esz)
+    scan = ((6 * dk * dv + C * dv) * n,
+            n * (2 * dk + dk + dv) * esz + nch * C * C * esz + n * dv * esz + 2 * s0)
+    return {"coef": coef, "ut": ut, "scan": scan}
+
+
+def fused_work(w, esz, has_s0):
+    B, H, L, dk, dv, C = w.B, w.H, w.L, w.d_k, w.d_v, w.chunk
+    n = B * H * L
+    s = 4 * B * H * dk * dv
+    return (flops_per_token(dk, dv, C) * n,
+            n * ((2 * dk + dv) * esz + 4) + n * dv * esz + s * (2 if has_s0 else 1))
+
+
+def source_hash(name: str) -> str:
+    with open(os.path.join(CSRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str, src: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
+    taken on the current source of the kernel; else None."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_h = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_h or not m_b or m_h.group(1) != source_hash(src):
+        return None
+    return float(m_b.group(1))
+
+
+# --- timing helpers ---------------------------------------------------------
+
+class Timer:
+    """HIP events recorded on the stream the kernels are launched on."""
+
+    def __init__(self, stream, names):
+        self.stream = stream
+        self.names = names
+        self.ms = {n: [] for n in names}
+
+    def marks(self):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(len(self.names) + 1)]
+
+    def record(self, ev):
+        ev.record(self.stream)
+
+    def collect(self, pending):
+        for evs in pending:
+            for i, n in enumerate(self.names):
+                self.ms[n].append(evs[i].elapsed_time(evs[i + 1]))
+
+    def mean(self, n):
+        v = self.ms[n]
+        return sum(v) / len(v)
+
+
+def bench_forward(args, w, dev):
+    q, k, v, beta, S0 = wl.forward_inputs(w, seed=0)
+    host = (q, k, v, beta, S0)
+    qd, kd, vd, bd = (x.to(dev) for x in (q, k, v, beta))
+    s0d = None if S0 is None else S0.to(dev)
+    dt = _lib.EFLA_BF16 if w.dtype == "bf16" else _lib.EFLA_F32
+    esz = 2 if w.dtype == "bf16" else 4
+    path = args.path
+    if path == "auto":
+        path = "staged"
+    pcode = {"staged": _lib.EFLA_PATH_STAGED, "fused": _lib.EFLA_PATH_FUSED}[path]
+    B, H, L, dk, dv, C = w.B, w.H, w.L, w.d_k, w.d_v, w.chunk
+    o = torch.empty((B, H, L, dv), dtype=qd.dtype, device=dev)
+    S_L = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    if path == "staged":
+        nch = (L + C - 1) // C
+        alpha = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+        W = torch.empty_like(kd)
+        U = torch.empty_like(vd)
+        A = torch.empty((B, H, nch, C, C), dtype=qd.dtype, device=dev)
+        names = ["coef", "ut", "scan"]
+
+        def step(ev, timer):
+            p = lambda x: None if x is None else x.data_ptr()  # noqa: E731
+            timer.record(ev[0])
+            st = _lib.efla_coefficients(p(kd), p(bd), p(alpha), None, B * H * L, dk, dt, sp)
+            timer.record(ev[1])
+            st |= _lib.efla_ut_transform(p(qd), p(kd), p(vd), p(alpha), p(W), p(U), p(A), B, H, L,
+                                         dk, dv, C, dt, sp)
+            timer.record(ev[2])
+            st |= _lib.efla_chunk_scan(p(qd), p(kd), p(W), p(U), p(A), p(s0d), p(o), p(S_L), B, H,
+                                       L, dk, dv, C, dt, sp)
+            timer.record(ev[3])
+            if st:
+                raise RuntimeError("staged forward failed")
+        work = stage_work(w, esz)
+        srcs = {"coef": "coef_decode.hip", "ut": "ut_transform.hip", "scan": "chunk_scan.hip"}
+    else:
+        need = _lib.efla_forward_workspace_size_ex(B, H, L, dk, dv, C, dt, pcode)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        names = ["fused"]
+
+        def step(ev, timer):
+            p = lambda x: None if x is None else x.data_ptr()  # noqa: E731
+            timer.record(ev[0])
+            st = _lib.efla_forward_ex(p(qd), p(kd), p(vd), p(bd), p(s0d), p(o), p(S_L), B, H, L,
+                                      dk, dv, C, dt, p(ws), need, pcode, sp)
+            timer.record(ev[1])
+            if st:
+                raise RuntimeError(f"fused forward failed: {_lib.status_string(st)}")
+        work = {"fused": fused_work(w, esz, S0 is not None)}
+        srcs = {"fused": "fused_forward.hip"}
+
+    timer = Timer(stream, names)
+    for _ in range(args.warmup):
+        step(timer.marks(), timer)
+    torch.cuda.synchronize()
+    pending = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ev = timer.marks()
+        step(ev, timer)
+        pending.append(ev)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    timer.collect(pending)
+
+    ms_step = elapsed * 1e3 / args.steps
+    tokens = B * L
+    F = flops_per_token(dk, dv, C) * B * H * L
+    peak = MFMA_PEAK[w.dtype]
+    per_kernel = {n: timer.mean(n) for n in names}
+    dom = max(per_kernel, key=per_kernel.get)
+    fl, by = work[dom]
+    t_dom = per_kernel[dom] * 1e-3
+    ridge = peak / HBM_PEAK
+    bound = "mfma" if fl / by >= ridge else "hbm"
+    traffic = read_traffic(dom, w.name, srcs[dom])
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": by / t_dom / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": fl / t_dom / 1e12, "peak": peak / 1e12,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic
+    roof["kernel"] = dom
+    roof["kernel_ms"] = per_kernel[dom]
+    roof["algorithmic_flops"] = fl
+    roof["algorithmic_bytes"] = by
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "L": L, "d_k": dk, "d_v": dv, "chunk": C,
+                   "path": path, "S0": S0 is not None},
+        "tflops": F / (ms_step * 1e-3) / 1e12,
+        "mfma_frac": F / (ms_step * 1e-3) / peak,
+        "flops_per_token_head": flops_per_token(dk, dv, C),
+        "kernel_ms": per_kernel,
+        "roofline": roof,
+    }
+    return res, host
+
+
+def bench_decode(args, dev, n_distinct=8):
+    w = wl.DECODE_WORKLOADS["decode-f32"]
+    S = wl.decode_state(w, seed=0).to(dev)
+    toks = []
+    for s in range(n_distinct):
+        toks.append(tuple(x.to(dev) for x in wl.decode_tokens(w, s, seed=0)))
+    o = torch.empty((w.N, w.H, w.d_v), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    p = lambda x: x.data_ptr()  # noqa: E731
+
+    def step(i):
+        q, k, v, beta = toks[i % n_distinct]
+        st = _lib.efla_decode_step(p(q), p(k), p(v), p(beta), p(S), p(o), w.N, w.H, w.d_k, w.d_v,
+                                   _lib.EFLA_F32, sp)
+        if st:
+            raise RuntimeError("decode failed")
+
+    for i in range(10):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(w.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / w.steps
+    nh = w.N * w.H
+    by = nh * (2 * w.d_k * w.d_v * 4 + (2 * w.d_k + 2 * w.d_v) * 4 + 4)
+    return {"workload": w.name, "N": w.N, "H": w.H, "d_k": w.d_k, "d_v": w.d_v,
+            "steps": w.steps, "ms_per_step": ms, "GB_s": by / (ms * 1e-3) / 1e9,
+            "hbm_frac": by / (ms * 1e-3) / HBM_PEAK, "algorithmic_bytes": by,
+            "note": f"{n_distinct} distinct token sets cycled over the steps; the state "
+                    f"({nh * w.d_k * w.d_v * 4} B) equals the 256 MiB Infinity Cache size"}
+
+
+def cpu_baseline(w, host):
+    """The fp64 oracle on the host cores, timed on the whole workload."""
+    import oracle
+    q, k, v, beta, S0 = host
+    threads = oracle.max_threads()
+    heads = w.B * w.H
+    t0 = time.perf_counter()
+    oracle.forward(q, k, v, beta, S0)
+    t = time.perf_counter() - t0
+    return {"value": w.B * w.L / t, "unit": "tokens/s", "cores": min(threads, heads),
+            "kind": "oracle", "seconds": t,
+            "sample": f"whole {w.name} workload ({heads} heads x {w.L} tokens), fp64, "
+                      f"OpenMP over heads; inputs converted to fp64 before timing"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="lm1.3b-bf16", choices=sorted(wl.FORWARD_WORKLOADS))
+    ap.add_argument("--path", default="auto", choices=["auto", "staged", "fused"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the operator shards over sequences/heads with no communication; run one "
+              "process per GPU instead)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no HIP device visible", file=sys.stderr)
+        sys.exit(1)
+    _lib.lib()   # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    w = wl.FORWARD_WORKLOADS[args.workload]
+    print(f"[bench] forward {w.name} path={args.path}", file=sys.stderr, flush=True)
+    res, host = bench_forward(args, w, dev)
+    if not args.no_decode:
+        print("[bench] decode-f32", file=sys.stderr, flush=True)
+        res["decode"] = bench_decode(args, dev)
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, host)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+"""EFLA (Exact Flow Linear Attention) forward operator and decode step on MI355X.
+
+Torch-facing wrappers around the C ABI of libefla.so (include/efla.h).  torch
+supplies device memory and the current stream; every step of the operator
+runs in the library's HIP kernels.
+
+  forward(q, k, v, beta, S0=None, chunk=64, path="auto") -> (o, S_L)
+  decode_step(q, k, v, beta, S) -> o          (S updated in place)
+  coefficients(k, beta) -> (alpha, lambda)    stage 1 of the staged path
+  ut_transform(q, k, v, alpha, chunk) -> (W, U, A)   stage 2
+  chunk_scan(q, k, W, U, A, S0, chunk) -> (o, S_L)   stage 3
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (EFLA_BF16, EFLA_F32, EFLA_PATH_AUTO, EFLA_PATH_FUSED, EFLA_PATH_STAGED,
+                   EflaError, LIB_PATH)
+
+__all__ = ["forward", "decode_step", "coefficients", "ut_transform", "chunk_scan",
+           "workspace_size", "EflaError", "LIB_PATH"]
+
+_PATHS = {"auto": EFLA_PATH_AUTO, "staged": EFLA_PATH_STAGED, "fused": EFLA_PATH_FUSED}
+
+
+def _dt(x: torch.Tensor) -> int:
+    if x.dtype == torch.bfloat16:
+        return EFLA_BF16
+    if x.dtype == torch.float32:
+        return EFLA_F32
+    raise TypeError(f"unsupported dtype {x.dtype}; q, k, v must be bfloat16 or float32")
+
+
+def _check(x: torch.Tensor, name: str, shape, dtype=None):
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {tuple(shape)}")
+    if dtype is not None and x.dtype != dtype:
+        raise TypeError(f"{name} has dtype {x.dtype}, expected {dtype}")
+
+
+def _ptr(x):
+    return None if x is None else x.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _raise(status: int, what: str):
+    if status != _lib.EFLA_OK:
+        raise EflaError(status, what)
+
+
+def workspace_size(B, H, L, d_k, d_v, chunk, dtype, path="auto") -> int:
+    dt = EFLA_BF16 if dtype == torch.bfloat16 else EFLA_F32
+    return _lib.efla_forward_workspace_size_ex(B, H, L, d_k, d_v, chunk, dt, _PATHS[path])
+
+
+def forward(q, k, v, beta, S0=None, chunk: int = 64, path: str = "auto", workspace=None,
+            out=None, S_L=None):
+    """Chunked EFLA forward.  q, k: [B,H,L,d_k]; v: [B,H,L,d_v]; beta: [B,H,L] fp32.
+
+    Returns (o [B,H,L,d_v] in q's dtype, S_L [B,H,d_k,d_v] fp32).  ``workspace``
+    (uint8, >= workspace_size bytes), ``out`` and ``S_L`` may be preallocated.
+    """
+    B, H, L, dk = k.shape
+    dv = v.shape[-1]
+    dt = _dt(q)
+    _check(q, "q", (B, H, L, dk), q.dtype)
+    _check(k, "k", (B, H, L, dk), q.dtype)
+    _check(v, "v", (B, H, L, dv), q.dtype)
+    _check(beta, "beta", (B, H, L), torch.float32)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), torch.float32)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=q.dtype, device=dev)
+    if S_L is None:
+        S_L = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    p = _PATHS[path]
+    need = _lib.efla_forward_workspace_size_ex(B, H, L, dk, dv, chunk, dt, p)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.efla_forward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(out),
+                              _ptr(S_L), B, H, L, dk, dv, chunk, dt, _ptr(workspace), ws_bytes, p,
+                              _stream(dev))
+    _raise(st, "efla_forward_ex")
+    return out, S_L
+
+
+def decode_step(q, k, v, beta, S, out=None):
+    """One decode step, S [N,H,d_k,d_v] fp32 updated in place.  Returns o [N,H,d_v]."""
+    N, H, dk = k.shape
+    dv = v.shape[-1]
+    dt = _dt(q)
+    _check(q, "q", (N, H, dk), q.dtype)
+    _check(k, "k", (N, H, dk), q.dtype)
+    _check(v, "v", (N, H, dv), q.dtype)
+    _check(beta, "beta", (N, H), torch.float32)
+    _check(S, "S", (N, H, dk, dv), torch.float32)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    st = _lib.efla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(out), N, H,
+                               dk, dv, dt, _stream(q.device))
+    _raise(st, "efla_decode_step")
+    return out
+
+
+def coefficients(k, beta, with_lambda: bool = True):
+    """Stage 1: per-token (alpha, lambda) in fp32, shaped like beta."""
+    dk = k.shape[-1]
+    n = beta.numel()
+    _check(k, "k", tuple(beta.shape) + (dk,))
+    _check(beta, "beta", tuple(beta.shape), torch.float32)
+    alpha = torch.empty_like(beta)
+    lam = torch.empty_like(beta) if with_lambda else None
+    st = _lib.efla_coefficients(_ptr(k), _ptr(beta), _ptr(alpha), _ptr(lam), n, dk, _dt(k),
+                                _stream(k.device))
+    _raise(st, "efla_coefficients")
+    return alpha, lam
+
+
+def ut_transform(q, k, v, alpha, chunk: int = 64):
+    """Stage 2: W [B,H,L,d_k], U [B,H,L,d_v], A [B,H,n_chunks,chunk,chunk] in q's dtype."""
+    B, H, L, dk = k.shape
+    dv = v.shape[-1]
+    _check(q, "q", (B, H, L, dk), q.dtype)
+    _check(k, "k", (B, H, L, dk), q.dtype)
+    _check(v, "v", (B, H, L, dv), q.dtype)
+    _check(alpha, "alpha", (B, H, L), torch.float32)
+    nch = (L + chunk - 1) // chunk
+    W = torch.empty_like(k)
+    U = torch.empty_like(v)
+    A = torch.empty((B, H, nch, chunk, chunk), dtype=q.dtype, device=q.device)
+    st = _lib.efla_ut_transform(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(W), _ptr(U), _ptr(A),
+                                B, H, L, dk, dv, chunk, _dt(q), _stream(q.device))
+    _raise(st, "efla_ut_transform")
+    return W, U, A
+
+
+def chunk_scan(q, k, W, U, A, S0=None, chunk: int = 64):
+    """Stage 3: (o [B,H,L,d_v], S_L [B,H,d_k,d_v] fp32) from stage-2 outputs."""
+    B, H, L, dk = k.shape
+    dv = U.shape[-1]
+    _check(W, "W", (B, H, L, dk), q.dtype)
+    _check(U, "U", (B, H, L, dv), q.dtype)
+    nch = (L + chunk - 1) // chunk
+    _check(A, "A", (B, H, nch, chunk, chunk), q.dtype)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), torch.float32)
+    o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    S_L = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    st = _lib.efla_chunk_scan(_ptr(q), _ptr(k), _ptr(W), _ptr(U), _ptr(A), _ptr(S0), _ptr(o),
+                              _ptr(S_L), B, H, L, dk, dv, chunk, _dt(q), _stream(q.device))
+    _raise(st, "efla_chunk_scan")
+    return o, S_L

@@ -1,0 +1,208 @@
+// Host side of the C ABI declared in include/efla.h: argument validation (no
+// HIP call before it passes), workspace sizing, and kernel launches on the
+// caller's stream.
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "efla.h"
+#include "efla_launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t esize(efla_dtype_t dt) { return dt == EFLA_BF16 ? 2 : 4; }
+
+// Shape checks common to the chunked entry points.
+efla_status_t check_shape(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t dt)
+{
+    if (dt != EFLA_F32 && dt != EFLA_BF16) return EFLA_ERR_INVALID_ARG;
+    if (B < 0 || H < 0 || L < 0 || dk <= 0 || dv <= 0 || chunk <= 0) return EFLA_ERR_INVALID_ARG;
+    if (!dim_ok(dk) || !dim_ok(dv) || !chunk_ok(chunk)) return EFLA_ERR_UNSUPPORTED;
+    // grid sizes and element offsets must fit their types
+    const long long bh = (long long)B * H;
+    const long long nchunks = ((long long)L + chunk - 1) / chunk;
+    if (bh * nchunks > INT32_MAX || bh * 8 > INT32_MAX) return EFLA_ERR_UNSUPPORTED;
+    if (bh * (long long)L * (dk > dv ? dk : dv) > (1LL << 46)) return EFLA_ERR_UNSUPPORTED;
+    return EFLA_OK;
+}
+
+struct StagedWs {
+    size_t alpha, w, u, aqk, total;
+};
+
+StagedWs staged_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t dt)
+{
+    const size_t n = (size_t)B * H * L;
+    const size_t nch = (size_t)B * H * ((L + chunk - 1) / chunk);
+    StagedWs s;
+    s.alpha = 0;
+    s.w = s.alpha + align_up(n * sizeof(float));
+    s.u = s.w + align_up(n * dk * esize(dt));
+    s.aqk = s.u + align_up(n * dv * esize(dt));
+    s.total = s.aqk + align_up(nch * chunk * chunk * esize(dt));
+    return s;
+}
+
+efla_path_t resolve_path(efla_path_t p) { return p == EFLA_PATH_AUTO ? EFLA_PATH_STAGED : p; }
+
+int scan_waves_override()
+{
+    const char *e = getenv("EFLA_SCAN_WAVES");
+    return e ? atoi(e) : 0;
+}
+
+efla_status_t hip_status(hipError_t e) { return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *efla_status_string(efla_status_t s)
+{
+    switch (s) {
+    case EFLA_OK: return "EFLA_OK";
+    case EFLA_ERR_INVALID_ARG: return "EFLA_ERR_INVALID_ARG";
+    case EFLA_ERR_UNSUPPORTED: return "EFLA_ERR_UNSUPPORTED";
+    case EFLA_ERR_WORKSPACE: return "EFLA_ERR_WORKSPACE";
+    case EFLA_ERR_HIP: return "EFLA_ERR_HIP";
+    }
+    return "EFLA_ERR_UNKNOWN";
+}
+
+size_t efla_forward_workspace_size_ex(int B, int H, int L, int dk, int dv, int chunk,
+                                      efla_dtype_t dt, efla_path_t path)
+{
+    if (check_shape(B, H, L, dk, dv, chunk, dt) != EFLA_OK) return 0;
+    path = resolve_path(path);
+    if (path == EFLA_PATH_STAGED) return staged_ws(B, H, L, dk, dv, chunk, dt).total;
+    return 0;
+}
+
+size_t efla_forward_workspace_size(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t dt)
+{
+    return efla_forward_workspace_size_ex(B, H, L, dk, dv, chunk, dt, EFLA_PATH_AUTO);
+}
+
+efla_status_t efla_forward_ex(const void *q, const void *k, const void *v, const float *beta,
+                              const float *S0, void *o, float *S_L, int B, int H, int L, int dk,
+                              int dv, int chunk, efla_dtype_t dt, void *workspace,
+                              size_t workspace_bytes, efla_path_t path, void *stream)
+{
+    efla_status_t s = check_shape(B, H, L, dk, dv, chunk, dt);
+    if (s != EFLA_OK) return s;
+    if (path != EFLA_PATH_AUTO && path != EFLA_PATH_STAGED && path != EFLA_PATH_FUSED)
+        return EFLA_ERR_INVALID_ARG;
+    path = resolve_path(path);
+    const long long BH = (long long)B * H;
+    if (BH == 0) return EFLA_OK;
+    if (!S_L || !aligned16(S_L) || (S0 && !aligned16(S0))) return EFLA_ERR_INVALID_ARG;
+    if (L > 0) {
+        if (!q || !k || !v || !beta || !o) return EFLA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(o))
+            return EFLA_ERR_INVALID_ARG;
+    }
+    if (path == EFLA_PATH_FUSED) return EFLA_ERR_UNSUPPORTED;
+    const StagedWs ws = staged_ws(B, H, L, dk, dv, chunk, dt);
+    if (L > 0) {
+        if (!workspace || workspace_bytes < ws.total) return EFLA_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return EFLA_ERR_INVALID_ARG;
+    }
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (L == 0) return hip_status(efla::launch_copy_state(S0, S_L, BH * dk * dv, st));
+
+    const bool bf = dt == EFLA_BF16;
+    char *base = static_cast<char *>(workspace);
+    float *alpha = reinterpret_cast<float *>(base + ws.alpha);
+    void *w = base + ws.w, *u = base + ws.u, *aqk = base + ws.aqk;
+    hipError_t e = efla::dispatch_coef(bf, dk, k, beta, alpha, nullptr, BH * L, st);
+    if (e == hipSuccess)
+        e = efla::dispatch_ut(bf, dk, dv, chunk, q, k, v, alpha, w, u, aqk, (int)BH, L, st);
+    if (e == hipSuccess)
+        e = efla::dispatch_scan(bf, dk, dv, chunk, q, k, w, u, aqk, S0, o, S_L, (int)BH, L,
+                                scan_waves_override(), st);
+    return hip_status(e);
+}
+
+efla_status_t efla_forward(const void *q, const void *k, const void *v, const float *beta,
+                           const float *S0, void *o, float *S_L, int B, int H, int L, int dk,
+                           int dv, int chunk, efla_dtype_t dt, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    return efla_forward_ex(q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt, workspace,
+                           workspace_bytes, EFLA_PATH_AUTO, stream);
+}
+
+efla_status_t efla_decode_step(const void *q, const void *k, const void *v, const float *beta,
+                               float *S, void *o, int N, int H, int dk, int dv, efla_dtype_t dt,
+                               void *stream)
+{
+    if (dt != EFLA_F32 && dt != EFLA_BF16) return EFLA_ERR_INVALID_ARG;
+    if (N < 0 || H < 0 || dk <= 0 || dv <= 0) return EFLA_ERR_INVALID_ARG;
+    if (!dim_ok(dk) || !dim_ok(dv)) return EFLA_ERR_UNSUPPORTED;
+    const long long NH = (long long)N * H;
+    if (NH > INT32_MAX) return EFLA_ERR_UNSUPPORTED;
+    if (NH == 0) return EFLA_OK;
+    if (!q || !k || !v || !beta || !S || !o) return EFLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(S) ||
+        !aligned16(o))
+        return EFLA_ERR_INVALID_ARG;
+    return hip_status(efla::dispatch_decode(dt == EFLA_BF16, dk, dv, q, k, v, beta, S, o, NH,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+efla_status_t efla_coefficients(const void *k, const float *beta, float *alpha, float *lambda,
+                                long n_tokens, int dk, efla_dtype_t dt, void *stream)
+{
+    if (dt != EFLA_F32 && dt != EFLA_BF16) return EFLA_ERR_INVALID_ARG;
+    if (n_tokens < 0 || dk <= 0) return EFLA_ERR_INVALID_ARG;
+    if (!dim_ok(dk)) return EFLA_ERR_UNSUPPORTED;
+    if (n_tokens == 0) return EFLA_OK;
+    if ((n_tokens + 255) / 256 > INT32_MAX) return EFLA_ERR_UNSUPPORTED;
+    if (!k || !beta || !alpha || !aligned16(k)) return EFLA_ERR_INVALID_ARG;
+    return hip_status(efla::dispatch_coef(dt == EFLA_BF16, dk, k, beta, alpha, lambda, n_tokens,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+efla_status_t efla_ut_transform(const void *q, const void *k, const void *v, const float *alpha,
+                                void *w, void *u, void *a_qk, int B, int H, int L, int dk, int dv,
+                                int chunk, efla_dtype_t dt, void *stream)
+{
+    efla_status_t s = check_shape(B, H, L, dk, dv, chunk, dt);
+    if (s != EFLA_OK) return s;
+    const long long BH = (long long)B * H;
+    if (BH == 0 || L == 0) return EFLA_OK;
+    if (!q || !k || !v || !alpha || !w || !u || !a_qk) return EFLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(w) || !aligned16(u) ||
+        !aligned16(a_qk))
+        return EFLA_ERR_INVALID_ARG;
+    return hip_status(efla::dispatch_ut(dt == EFLA_BF16, dk, dv, chunk, q, k, v, alpha, w, u, a_qk,
+                                        (int)BH, L, static_cast<hipStream_t>(stream)));
+}
+
+efla_status_t efla_chunk_scan(const void *q, const void *k, const void *w, const void *u,
+                              const void *a_qk, const float *S0, void *o, float *S_L, int B, int H,
+                              int L, int dk, int dv, int chunk, efla_dtype_t dt, void *stream)
+{
+    efla_status_t s = check_shape(B, H, L, dk, dv, chunk, dt);
+    if (s != EFLA_OK) return s;
+    const long long BH = (long long)B * H;
+    if (BH == 0) return EFLA_OK;
+    if (!S_L || !aligned16(S_L) || (S0 && !aligned16(S0))) return EFLA_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (L == 0) return hip_status(efla::launch_copy_state(S0, S_L, BH * dk * dv, st));
+    if (!q || !k || !w || !u || !a_qk || !o) return EFLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(w) || !aligned16(u) || !aligned16(a_qk) ||
+        !aligned16(o))
+        return EFLA_ERR_INVALID_ARG;
+    return hip_status(efla::dispatch_scan(dt == EFLA_BF16, dk, dv, chunk, q, k, w, u, a_qk, S0, o,
+                                          S_L, (int)BH, L, scan_waves_override(), st));
+}
+
+}  // extern "C"

@@ -1,0 +1,202 @@
+// Device-side building blocks shared by the EFLA kernels (gfx950 / CDNA4).
+//
+// Matrix-core conventions used throughout (wave64):
+//   lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4 (four lane groups).
+//   An "acc tile" is the fp32 result of a 16x16 MFMA: lane holds rows 4g+r
+//   (r = 0..3) of column l16.
+//   v_mfma_f32_16x16x32_bf16: each lane feeds 8 bf16 of A (row l16) and 8 of B
+//   (column l16).  v_mfma_f32_16x16x4_f32: one fp32 of each.
+//
+// The contraction index k may be assigned to (lane group, slot) by any
+// bijection, provided A and B use the same one.  Two maps are used:
+//   NAT  (natural):  bf16 k = 8g + j                  f32 k = g
+//   PERM (acc map):  bf16 k = 16*(j/4) + 4g + (j%4)   f32 k = 4g   (+ r per step)
+// PERM is the row order in which an acc tile already sits in the registers,
+// so a product whose B operand is an acc tile (the state S, or E) consumes it
+// straight from registers without a trip through LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace efla {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct is_bf16_t { static constexpr bool value = false; };
+template <> struct is_bf16_t<__bf16> { static constexpr bool value = true; };
+template <typename T> constexpr bool is_bf16 = is_bf16_t<T>::value;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return static_cast<float>(x); }
+template <typename T> __device__ __forceinline__ T from_f32(float x) { return static_cast<T>(x); }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b)
+{
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v)
+{
+    return bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]),
+                  static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
+}
+
+// Four consecutive-k elements of a bf16 operand held in LDS.  The operand
+// element (idx, k) -- idx is the row of A or the column of B -- lives at
+// M[idx*ld + k] when !STRIDED (k contiguous: one 8-byte read), else at
+// M[k*ld + idx] (four 2-byte reads).
+template <bool STRIDED>
+__device__ __forceinline__ bf16x4 run4(const __bf16 *M, int ld, int idx, int k)
+{
+    if constexpr (!STRIDED) {
+        return *reinterpret_cast<const bf16x4 *>(M + idx * ld + k);
+    } else {
+        return bf16x4{M[(k + 0) * ld + idx], M[(k + 1) * ld + idx], M[(k + 2) * ld + idx],
+                      M[(k + 3) * ld + idx]};
+    }
+}
+
+template <bool STRIDED>
+__device__ __forceinline__ float one(const float *M, int ld, int idx, int k)
+{
+    if constexpr (!STRIDED) return M[idx * ld + k];
+    else return M[k * ld + idx];
+}
+
+// out[mt] (+)= A[16mt.., 0:16KT] * B, where B (16KT x 16) is given as KT acc
+// tiles in registers (PERM map).  A is in LDS, element (i,k) at A[i*lda+k]
+// (!A_STRIDED) or A[k*lda+i] (A_STRIDED).  LOWER: A is block lower
+// triangular (tiles above the diagonal are zero and need not be multiplied).
+template <typename T, int MT, int KT, bool LOWER, bool A_STRIDED>
+__device__ __forceinline__ void mm_acc_b(f32x4 (&out)[MT], const T *A, int lda,
+                                         const f32x4 (&Bacc)[KT])
+{
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+    if constexpr (is_bf16<T>) {
+#pragma unroll
+        for (int s = 0; s < (KT + 1) / 2; ++s) {
+            const bool two = (2 * s + 1 < KT);
+            const bf16x8 b = cat(to_bf16x4(Bacc[2 * s]), two ? to_bf16x4(Bacc[2 * s + 1])
+                                                              : to_bf16x4(zero4()));
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                if (LOWER && 2 * s > mt) continue;
+                const int i = 16 * mt + l16;
+                const bf16x4 a1 = run4<A_STRIDED>(A, lda, i, 32 * s + 4 * g);
+                const bf16x4 a2 = two ? run4<A_STRIDED>(A, lda, i, 32 * s + 16 + 4 * g)
+                                      : to_bf16x4(zero4());
+                out[mt] = mma(cat(a1, a2), b, out[mt]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    if (LOWER && kt > mt) continue;
+                    const float a = one<A_STRIDED>(A, lda, 16 * mt + l16, 16 * kt + 4 * g + r);
+                    out[mt] = mma(a, Bacc[kt][r], out[mt]);
+                }
+            }
+        }
+    }
+}
+
+// acc (+)= A[i0:i0+16, 0:K] * B[0:K, j0:j0+16] with both operands in LDS.
+// A element (i,k): A[i*lda+k] or, A_STRIDED, A[k*lda+i].
+// B element (k,j): B[j*ldb+k] or, B_STRIDED, B[k*ldb+j].
+// K must be a multiple of 16.  KLIM > 0 caps the k range (block-triangular
+// operands): only k < KLIM is multiplied.
+template <typename T, int K, bool A_STRIDED, bool B_STRIDED>
+__device__ __forceinline__ f32x4 mm_lds(f32x4 acc, const T *A, int lda, int i0, const T *B,
+                                        int ldb, int j0, int klim = K)
+{
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+    if constexpr (is_bf16<T>) {
+#pragma unroll
+        for (int s = 0; s < (K + 31) / 32; ++s) {
+            if (32 * s >= klim) break;
+            const int k = 32 * s + 8 * g;       // NAT map
+            bf16x8 a, b;
+            if (k < K) {
+                a = cat(run4<A_STRIDED>(A, lda, i0 + l16, k), run4<A_STRIDED>(A, lda, i0 + l16, k + 4));
+                b = cat(run4<B_STRIDED>(B, ldb, j0 + l16, k), run4<B_STRIDED>(B, ldb, j0 + l16, k + 4));
+            } else {   // K = 16 (or an odd number of 16-blocks): pad the k-block with zeros
+                a = cat(to_bf16x4(zero4()), to_bf16x4(zero4()));
+                b = a;
+            }
+            acc = mma(a, b, acc);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < K / 4; ++s) {
+            if (4 * s >= klim) break;
+            const float a = one<A_STRIDED>(A, lda, i0 + l16, 4 * s + g);
+            const float b = one<B_STRIDED>(B, ldb, j0 + l16, 4 * s + g);
+            acc = mma(a, b, acc);
+        }
+    }
+    return acc;
+}
+
+// Cooperative copy of a rows x COLS tile (COLS elements contiguous per row in
+// global memory, row stride g_ld) into LDS (row stride s_ld), 16 bytes per
+// thread per step.  Rows >= rows_valid are filled with zeros.
+template <typename T, int COLS, int NTHREADS>
+__device__ __forceinline__ void load_tile(T *s, int s_ld, const T *gsrc, long g_ld, int rows_valid,
+                                          int rows)
+{
+    constexpr int V = 16 / sizeof(T);
+    static_assert(COLS % V == 0, "tile width must be a multiple of 16 bytes");
+    constexpr int VPR = COLS / V;
+    for (int idx = threadIdx.x; idx < rows * VPR; idx += NTHREADS) {
+        const int r = idx / VPR, cv = idx - r * VPR;
+        uint4 val = make_uint4(0u, 0u, 0u, 0u);
+        if (r < rows_valid) val = *reinterpret_cast<const uint4 *>(gsrc + r * g_ld + cv * V);
+        *reinterpret_cast<uint4 *>(s + r * s_ld + cv * V) = val;
+    }
+}
+
+// alpha from beta and lambda (Methodology 3 of the EFLA technical summary):
+// (1 - e^{-beta lambda}) / lambda, evaluated as beta * phi(x), x = beta lambda,
+// phi(x) = -expm1(-x)/x, with the lambda -> 0 limit alpha = beta.  For x > 1
+// the equivalent -expm1(-x)/lambda avoids beta*phi under/overflow.
+__device__ __forceinline__ float efla_alpha(float beta, float lambda)
+{
+    const float x = beta * lambda;
+    if (fabsf(x) < 1e-30f) return beta;
+    if (x > 1.0f) return -expm1f(-x) / lambda;
+    return beta * (-expm1f(-x) / x);
+}
+
+// Workgroup -> (sequence, tile) map that keeps the NTILE tiles of one
+// sequence on one XCD.  Consecutive workgroup ids are dispatched round-robin
+// over the 8 XCDs, so ids x, x+8, x+16, ... share an XCD and its L2.
+__device__ __forceinline__ void xcd_map(int bid, int nblocks, int ntile, int &seq, int &tile)
+{
+    int lin = bid;
+    if ((nblocks & 7) == 0) {
+        const int per = nblocks >> 3;
+        lin = (bid & 7) * per + (bid >> 3);
+    }
+    seq = lin / ntile;
+    tile = lin - seq * ntile;
+}
+
+}  // namespace efla

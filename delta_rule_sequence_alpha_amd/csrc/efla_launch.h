@@ -1,0 +1,33 @@
+// Internal host-side launchers of the EFLA kernels (C++ linkage, not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+// Every (d_k, d_v, chunk) the chunked kernels are instantiated for:
+// d_k, d_v in {16, 32, 64, 128} x chunk in {16, 32, 64}.
+#define EFLA_SHAPES_FOR_C(X, CC)                                                                 \
+    X(16, 16, CC) X(16, 32, CC) X(16, 64, CC) X(16, 128, CC)                                     \
+    X(32, 16, CC) X(32, 32, CC) X(32, 64, CC) X(32, 128, CC)                                     \
+    X(64, 16, CC) X(64, 32, CC) X(64, 64, CC) X(64, 128, CC)                                     \
+    X(128, 16, CC) X(128, 32, CC) X(128, 64, CC) X(128, 128, CC)
+#define EFLA_SHAPE_CASES(X) EFLA_SHAPES_FOR_C(X, 16) EFLA_SHAPES_FOR_C(X, 32) EFLA_SHAPES_FOR_C(X, 64)
+
+namespace efla {
+
+hipError_t dispatch_coef(bool bf16, int dk, const void *k, const float *beta, float *alpha,
+                         float *lambda, long n, hipStream_t st);
+
+hipError_t dispatch_decode(bool bf16, int dk, int dv, const void *q, const void *k, const void *v,
+                           const float *beta, float *S, void *o, long NH, hipStream_t st);
+
+hipError_t dispatch_ut(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
+                       const void *v, const float *alpha, void *w, void *u, void *aqk, int BH,
+                       int L, hipStream_t st);
+
+hipError_t dispatch_scan(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
+                         const void *w, const void *u, const void *aqk, const float *S0, void *o,
+                         float *SL, int BH, int L, int nw, hipStream_t st);
+
+hipError_t launch_copy_state(const float *src, float *dst, long n, hipStream_t st);
+
+}  // namespace efla

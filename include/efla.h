@@ -1,0 +1,155 @@
+/*
+ * efla.h - C ABI of the MI355X (gfx950) Exact Flow Linear Attention library.
+ *
+ * The operator ("Exact Flow Linear Attention: Exact Solution from
+ * Continuous-Time Dynamics", gist.science Technical Summary, Methodology 3):
+ * for each (batch b, head h) independently and t = 0 .. L-1,
+ *
+ *     lambda_t = |k_t|^2,   alpha_t = (1 - exp(-beta_t lambda_t)) / lambda_t
+ *                                     (= beta_t in the limit lambda_t -> 0)
+ *     S_t = (I - alpha_t k_t k_t^T) S_{t-1} + alpha_t k_t v_t^T
+ *     o_t = S_t^T q_t                       (the state after the update)
+ *
+ * S_t is d_k x d_v.  The update keeps the delta rule's rank-1 form, which is
+ * what lets the chunkwise (WY/UT) evaluation used here reproduce the token
+ * recurrence (Methodology 3; the pages name the scheme without formulas).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are HIP device pointers owned by the caller.  Tensors are
+ *    row-major and contiguous in the layouts given below; every pointer must be
+ *    16-byte aligned.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Outputs are valid once the caller has synchronised the stream.
+ *  - Arguments are validated before any HIP call.  A call that returns an
+ *    error status has launched nothing.  The library never prints, never
+ *    aborts and never allocates device memory.
+ *  - Distinct calls are thread-safe when they use distinct streams and
+ *    buffers.
+ *  - Supported shapes: d_k, d_v in {16, 32, 64, 128}; chunk in {16, 32, 64}.
+ *    Other values return EFLA_ERR_UNSUPPORTED.
+ *  - Any L >= 0 is accepted.  A last partial chunk is evaluated exactly:
+ *    missing tokens act as alpha = 0, which is the identity update.
+ *  - beta may hold any finite value; no clamp is applied.
+ */
+#ifndef EFLA_H
+#define EFLA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v, o (and of the W, U, A stage outputs).  The state,
+ * beta, alpha and lambda are always fp32.  bf16 inputs are multiplied on bf16
+ * MFMA with fp32 accumulation; fp32 inputs on fp32 MFMA. */
+typedef enum { EFLA_F32 = 0, EFLA_BF16 = 1 } efla_dtype_t;
+
+typedef enum {
+    EFLA_OK = 0,
+    EFLA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, negative size, bad enum */
+    EFLA_ERR_UNSUPPORTED = 2,  /* d_k, d_v or chunk outside the supported set      */
+    EFLA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required       */
+    EFLA_ERR_HIP = 4           /* a HIP launch reported an error                   */
+} efla_status_t;
+
+/* Evaluation strategy of efla_forward_ex. */
+typedef enum {
+    EFLA_PATH_AUTO = 0,    /* the fastest path available for the shape         */
+    EFLA_PATH_STAGED = 1,  /* coefficient -> UT-transform -> state-scan kernels */
+    EFLA_PATH_FUSED = 2    /* one kernel; no intermediate HBM traffic           */
+} efla_path_t;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *efla_status_string(efla_status_t s);
+
+/* Bytes of device workspace efla_forward / efla_forward_ex(path) needs for
+ * this shape (0 when the path needs none).  Returns 0 for invalid shapes. */
+size_t efla_forward_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk,
+                                   efla_dtype_t dt);
+size_t efla_forward_workspace_size_ex(int B, int H, int L, int d_k, int d_v, int chunk,
+                                      efla_dtype_t dt, efla_path_t path);
+
+/*
+ * Chunked forward over whole sequences (Methodology 3).
+ *   q, k  [B,H,L,d_k]  dtype dt           v  [B,H,L,d_v]  dtype dt
+ *   beta  [B,H,L]      fp32               per token and head
+ *   S0    [B,H,d_k,d_v] fp32 or NULL      NULL means the zero initial state
+ *   o     [B,H,L,d_v]  dtype dt           output, o_t = S_t^T q_t
+ *   S_L   [B,H,d_k,d_v] fp32              output, state after token L-1;
+ *                                          may alias S0 (exactly the same
+ *                                          pointer), no other aliasing
+ *   workspace: device buffer of at least efla_forward_workspace_size() bytes,
+ *   256-byte aligned, owned by the caller; it may be NULL when that size is 0.
+ * With L = 0, S_L receives S0 (or zeros) and o is untouched.
+ */
+efla_status_t efla_forward(const void *q, const void *k, const void *v, const float *beta,
+                           const float *S0, void *o, float *S_L,
+                           int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype_t dt,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* efla_forward with an explicit evaluation path; results agree with the
+ * token recurrence to within fp32/bf16 rounding whichever path runs. */
+efla_status_t efla_forward_ex(const void *q, const void *k, const void *v, const float *beta,
+                              const float *S0, void *o, float *S_L,
+                              int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype_t dt,
+                              void *workspace, size_t workspace_bytes, efla_path_t path,
+                              void *stream);
+
+/*
+ * Single-token decode step (the recurrent form of the same update) for N
+ * sequences x H heads, in place:
+ *   q, k [N,H,d_k]  v [N,H,d_v]  dtype dt;  beta [N,H] fp32
+ *   S    [N,H,d_k,d_v] fp32, read and overwritten with S_new
+ *   o    [N,H,d_v]  dtype dt, o = S_new^T q
+ * Each (n,h) state is read completely before any of it is written.
+ */
+efla_status_t efla_decode_step(const void *q, const void *k, const void *v, const float *beta,
+                               float *S, void *o, int N, int H, int d_k, int d_v,
+                               efla_dtype_t dt, void *stream);
+
+/*
+ * Stage 1 of the staged path: per-token coefficients (Methodology 2-3).
+ *   k [n_tokens, d_k] dtype dt; beta [n_tokens] fp32
+ *   alpha [n_tokens] fp32 out; lambda [n_tokens] fp32 out, or NULL to skip.
+ * lambda_t = |k_t|^2 accumulated in fp32 from the stored k;
+ * alpha_t = beta_t * (1 - exp(-x)) / x with x = beta_t lambda_t (expm1 form),
+ * and alpha_t = beta_t when |x| < 1e-30.
+ */
+efla_status_t efla_coefficients(const void *k, const float *beta, float *alpha, float *lambda,
+                                long n_tokens, int d_k, efla_dtype_t dt, void *stream);
+
+/*
+ * Stage 2: per-chunk UT transform.  For every chunk of `chunk` consecutive
+ * tokens of every (b,h) (last chunk possibly partial), with K, V the chunk's
+ * keys and values and a = alpha:
+ *   T = (I + strictly_lower(diag(a) K K^T))^{-1} diag(a)   (fp32, forward
+ *        substitution on 16x16 diagonal blocks, block substitution off them)
+ *   W = T K  -> w [B,H,L,d_k] dtype dt
+ *   U = T V  -> u [B,H,L,d_v] dtype dt
+ *   A = tril(Q K^T), diagonal included -> a_qk [B,H,ceil(L/chunk),chunk,chunk]
+ *       dtype dt (rows/columns past L are zero)
+ *   q, k [B,H,L,d_k], v [B,H,L,d_v] dtype dt; alpha [B,H,L] fp32.
+ */
+efla_status_t efla_ut_transform(const void *q, const void *k, const void *v, const float *alpha,
+                                void *w, void *u, void *a_qk,
+                                int B, int H, int L, int d_k, int d_v, int chunk,
+                                efla_dtype_t dt, void *stream);
+
+/*
+ * Stage 3: inter-chunk state scan.  Per (b,h) the fp32 state S (from S0, or
+ * zero) stays on chip; for each chunk in order
+ *   E = U - W S;   O = Q S + A E;   S <- S + K^T E
+ * with W, U, A from stage 2.  Writes o [B,H,L,d_v] (dtype dt) and S_L.
+ * S_L may alias S0 exactly.
+ */
+efla_status_t efla_chunk_scan(const void *q, const void *k, const void *w, const void *u,
+                              const void *a_qk, const float *S0, void *o, float *S_L,
+                              int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype_t dt,
+                              void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EFLA_H */

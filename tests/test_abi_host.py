@@ -1,0 +1,129 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects bad arguments before any HIP
+call (every call below fails validation, so nothing touches a device)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from delta_rule_sequence_alpha_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "efla.h")
+
+FAKE = 0x10000        # a 16-byte-aligned pointer value that is never dereferenced
+MISALIGNED = 0x10008
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(efla_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail(f"{_lib.LIB_PATH} not built (python -m delta_rule_sequence_alpha_amd.build)")
+    return _lib.lib()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert len(declared) == 9
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (efla_[a-z_]+)\b", out))
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert sorted(n for n, _, _ in _lib.SIGNATURES) == declared
+
+
+def test_status_strings(lib):
+    names = ["EFLA_OK", "EFLA_ERR_INVALID_ARG", "EFLA_ERR_UNSUPPORTED", "EFLA_ERR_WORKSPACE",
+             "EFLA_ERR_HIP"]
+    for i, n in enumerate(names):
+        assert _lib.status_string(i) == n
+    assert _lib.status_string(77) == "EFLA_ERR_UNKNOWN"
+
+
+def test_workspace_size(lib):
+    # staged path: alpha fp32 + W + U (dtype) + A (dtype), each 256-byte aligned
+    B, H, L, d, C = 4, 16, 4096, 128, 64
+    n = B * H * L
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    want = up(n * 4) + up(n * d * 2) + up(n * d * 2) + up(B * H * (L // C) * C * C * 2)
+    assert _lib.efla_forward_workspace_size_ex(B, H, L, d, d, C, _lib.EFLA_BF16,
+                                               _lib.EFLA_PATH_STAGED) == want
+    assert _lib.efla_forward_workspace_size(1, 1, 64, 48, 16, 16, _lib.EFLA_F32) == 0  # unsupported
+    assert _lib.efla_forward_workspace_size(1, 1, -1, 16, 16, 16, _lib.EFLA_F32) == 0  # invalid
+    # ragged L rounds the chunk count up
+    assert _lib.efla_forward_workspace_size_ex(1, 1, 65, 16, 16, 64, _lib.EFLA_F32,
+                                               _lib.EFLA_PATH_STAGED) == \
+        up(65 * 4) + up(65 * 16 * 4) * 2 + up(2 * 64 * 64 * 4)
+
+
+def _fwd(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, S0=None, o=FAKE, S_L=FAKE, B=1, H=1, L=64, dk=16,
+             dv=16, chunk=16, dt=_lib.EFLA_F32, ws=FAKE, ws_bytes=1 << 30, path=0, stream=None)
+    a.update(over)
+    return _lib.efla_forward_ex(a["q"], a["k"], a["v"], a["beta"], a["S0"], a["o"], a["S_L"],
+                                a["B"], a["H"], a["L"], a["dk"], a["dv"], a["chunk"], a["dt"],
+                                a["ws"], a["ws_bytes"], a["path"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dt=7), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(B=-1), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(L=-5), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(dk=0), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(chunk=-16), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(dk=48), _lib.EFLA_ERR_UNSUPPORTED),
+    (dict(dv=256), _lib.EFLA_ERR_UNSUPPORTED),
+    (dict(chunk=128), _lib.EFLA_ERR_UNSUPPORTED),
+    (dict(q=None), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(beta=None), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(S_L=None), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(o=MISALIGNED), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(S0=MISALIGNED), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(ws=None), _lib.EFLA_ERR_WORKSPACE),
+    (dict(ws_bytes=100), _lib.EFLA_ERR_WORKSPACE),
+    (dict(ws=FAKE + 16), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(path=9), _lib.EFLA_ERR_INVALID_ARG),
+])
+def test_forward_validation(lib, over, status):
+    assert _fwd(lib, **over) == status
+
+
+def test_empty_batch_is_a_no_op(lib):
+    # B*H == 0: nothing to do, no pointer is needed and nothing is launched
+    assert _fwd(lib, B=0, q=None, k=None, v=None, beta=None, o=None, S_L=None, ws=None) == _lib.EFLA_OK
+
+
+def test_decode_validation(lib):
+    d = lambda **o: _lib.efla_decode_step(  # noqa: E731
+        o.get("q", FAKE), FAKE, FAKE, FAKE, o.get("S", FAKE), FAKE, o.get("N", 2), 3,
+        o.get("dk", 128), 128, o.get("dt", _lib.EFLA_F32), None)
+    assert d(dt=3) == _lib.EFLA_ERR_INVALID_ARG
+    assert d(N=-1) == _lib.EFLA_ERR_INVALID_ARG
+    assert d(dk=100) == _lib.EFLA_ERR_UNSUPPORTED
+    assert d(q=None) == _lib.EFLA_ERR_INVALID_ARG
+    assert d(S=MISALIGNED) == _lib.EFLA_ERR_INVALID_ARG
+    assert d(N=0) == _lib.EFLA_OK
+
+
+def test_stage_validation(lib):
+    assert _lib.efla_coefficients(FAKE, FAKE, FAKE, None, -1, 128, 0, None) == _lib.EFLA_ERR_INVALID_ARG
+    assert _lib.efla_coefficients(FAKE, FAKE, FAKE, None, 10, 24, 0, None) == _lib.EFLA_ERR_UNSUPPORTED
+    assert _lib.efla_coefficients(None, FAKE, FAKE, None, 10, 128, 0, None) == _lib.EFLA_ERR_INVALID_ARG
+    assert _lib.efla_ut_transform(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 16, 16, 16, 0,
+                                  None) == _lib.EFLA_ERR_INVALID_ARG
+    assert _lib.efla_ut_transform(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 16, 16, 8, 0,
+                                  None) == _lib.EFLA_ERR_UNSUPPORTED
+    assert _lib.efla_chunk_scan(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 1, 1, 64, 16, 16,
+                                16, 0, None) == _lib.EFLA_ERR_INVALID_ARG
+    assert _lib.efla_chunk_scan(FAKE, FAKE, FAKE, FAKE, MISALIGNED, None, FAKE, FAKE, 1, 1, 64, 16,
+                                16, 16, 0, None) == _lib.EFLA_ERR_INVALID_ARG
