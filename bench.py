@@ -122,8 +122,8 @@ def bench_forward(args, w, dev):
     dt = _lib.EFLA_BF16 if w.dtype == "bf16" else _lib.EFLA_F32
     esz = 2 if w.dtype == "bf16" else 4
     path = args.path
-    if path == "auto":
-        path = "staged"
+    if path == "auto":   # the library's own choice: fused kernel for bf16 inputs
+        path = "fused" if w.dtype == "bf16" else "staged"
     pcode = {"staged": _lib.EFLA_PATH_STAGED, "fused": _lib.EFLA_PATH_FUSED}[path]
     B, H, L, dk, dv, C = w.B, w.H, w.L, w.d_k, w.d_v, w.chunk
     o = torch.empty((B, H, L, dv), dtype=qd.dtype, device=dev)

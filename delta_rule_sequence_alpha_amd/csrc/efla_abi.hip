@@ -49,13 +49,21 @@ StagedWs staged_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t 
     return s;
 }
 
-efla_path_t resolve_path(efla_path_t p) { return p == EFLA_PATH_AUTO ? EFLA_PATH_STAGED : p; }
-
-int scan_waves_override()
+// AUTO: the fused kernel where it exists (bf16 inputs), else the staged kernels.
+efla_path_t resolve_path(efla_path_t p, efla_dtype_t dt, int dk, int dv, int chunk)
 {
-    const char *e = getenv("EFLA_SCAN_WAVES");
+    if (p != EFLA_PATH_AUTO) return p;
+    return efla::fused_supported(dt == EFLA_BF16, dk, dv, chunk) ? EFLA_PATH_FUSED
+                                                                  : EFLA_PATH_STAGED;
+}
+
+// Waves per workgroup of the scan / fused kernels (0 = the built-in choice).
+int waves_override(const char *name)
+{
+    const char *e = getenv(name);
     return e ? atoi(e) : 0;
 }
+int scan_waves_override() { return waves_override("EFLA_SCAN_WAVES"); }
 
 efla_status_t hip_status(hipError_t e) { return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP; }
 
@@ -79,7 +87,7 @@ size_t efla_forward_workspace_size_ex(int B, int H, int L, int dk, int dv, int c
                                       efla_dtype_t dt, efla_path_t path)
 {
     if (check_shape(B, H, L, dk, dv, chunk, dt) != EFLA_OK) return 0;
-    path = resolve_path(path);
+    path = resolve_path(path, dt, dk, dv, chunk);
     if (path == EFLA_PATH_STAGED) return staged_ws(B, H, L, dk, dv, chunk, dt).total;
     return 0;
 }
@@ -98,7 +106,7 @@ efla_status_t efla_forward_ex(const void *q, const void *k, const void *v, const
     if (s != EFLA_OK) return s;
     if (path != EFLA_PATH_AUTO && path != EFLA_PATH_STAGED && path != EFLA_PATH_FUSED)
         return EFLA_ERR_INVALID_ARG;
-    path = resolve_path(path);
+    path = resolve_path(path, dt, dk, dv, chunk);
     const long long BH = (long long)B * H;
     if (BH == 0) return EFLA_OK;
     if (!S_L || !aligned16(S_L) || (S0 && !aligned16(S0))) return EFLA_ERR_INVALID_ARG;
@@ -107,14 +115,20 @@ efla_status_t efla_forward_ex(const void *q, const void *k, const void *v, const
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(o))
             return EFLA_ERR_INVALID_ARG;
     }
-    if (path == EFLA_PATH_FUSED) return EFLA_ERR_UNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (path == EFLA_PATH_FUSED) {
+        if (!efla::fused_supported(dt == EFLA_BF16, dk, dv, chunk)) return EFLA_ERR_UNSUPPORTED;
+        if (L == 0) return hip_status(efla::launch_copy_state(S0, S_L, BH * dk * dv, st));
+        return hip_status(efla::dispatch_fused(dt == EFLA_BF16, dk, dv, chunk, q, k, v, beta, S0,
+                                               o, S_L, (int)BH, L,
+                                               waves_override("EFLA_FUSED_WAVES"), st));
+    }
     const StagedWs ws = staged_ws(B, H, L, dk, dv, chunk, dt);
     if (L > 0) {
         if (!workspace || workspace_bytes < ws.total) return EFLA_ERR_WORKSPACE;
         if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return EFLA_ERR_INVALID_ARG;
     }
 
-    hipStream_t st = static_cast<hipStream_t>(stream);
     if (L == 0) return hip_status(efla::launch_copy_state(S0, S_L, BH * dk * dv, st));
 
     const bool bf = dt == EFLA_BF16;

@@ -28,6 +28,12 @@ hipError_t dispatch_scan(bool bf16, int dk, int dv, int chunk, const void *q, co
                          const void *w, const void *u, const void *aqk, const float *S0, void *o,
                          float *SL, int BH, int L, int nw, hipStream_t st);
 
+bool fused_supported(bool bf16, int dk, int dv, int chunk);
+
+hipError_t dispatch_fused(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
+                          const void *v, const float *beta, const float *S0, void *o, float *SL,
+                          int BH, int L, int nw, hipStream_t st);
+
 hipError_t launch_copy_state(const float *src, float *dst, long n, hipStream_t st);
 
 }  // namespace efla
