@@ -282,6 +282,87 @@ def cpu_baseline(w, host):
                       f"OpenMP over heads; inputs converted to fp64 before timing"}
 
 
+# --- HBM traffic from rocprofv3 --pmc ----------------------------------------
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(args, dev):
+    """A plain device copy of COPY_BYTES (read once, written once): the
+    FETCH_SIZE / WRITE_SIZE it reads under rocprofv3 --pmc calibrate those
+    counters to bytes.  Only torch's copy kernel runs (the source is left
+    uninitialised so no fill kernel is launched)."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(max(args.steps, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": max(args.steps, 1)}), flush=True)
+
+
+def _pmc_per_dispatch(csv_path, name_re, counter):
+    """Average over matching dispatches of the counter summed over its
+    dimensions (KiB for FETCH_SIZE / WRITE_SIZE)."""
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter or not re.search(name_re, row["Kernel_Name"]):
+                continue
+            d = int(row["Dispatch_Id"])
+            per[d] = per.get(d, 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for /{name_re}/ in {csv_path}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def pmc_summary(args):
+    """Writes profiles/traffic_<kernel>_<workload>.txt from four rocprofv3
+    --pmc runs under args.pmc_summary: fetch/ and write/ (this bench, one
+    counter each) and cal_fetch/ and cal_write/ (--copy-calibration)."""
+    import glob
+    d = args.pmc_summary
+    w = wl.FORWARD_WORKLOADS[args.workload]
+    kname, kre, src = {"fused": ("fused", r"fused_kernel", "fused_forward.hip"),
+                       "scan": ("scan", r"scan_kernel", "chunk_scan.hip"),
+                       "ut": ("ut", r"ut_kernel", "ut_transform.hip")}[args.pmc_kernel]
+
+    def csv_of(sub):
+        hits = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)
+        if len(hits) != 1:
+            raise SystemExit(f"expected one counter_collection.csv under {d}/{sub}, got {hits}")
+        return hits[0]
+    fk, nf = _pmc_per_dispatch(csv_of("fetch"), kre, "FETCH_SIZE")
+    wk, nw = _pmc_per_dispatch(csv_of("write"), kre, "WRITE_SIZE")
+    cfk, _ = _pmc_per_dispatch(csv_of("cal_fetch"), r"elementwise|copy", "FETCH_SIZE")
+    cwk, _ = _pmc_per_dispatch(csv_of("cal_write"), r"elementwise|copy", "WRITE_SIZE")
+    f_fac = COPY_BYTES / (cfk * 1024.0)
+    w_fac = COPY_BYTES / (cwk * 1024.0)
+    hbm = fk * 1024.0 * f_fac + wk * 1024.0 * w_fac
+    esz = 2 if w.dtype == "bf16" else 4
+    algo = (fused_work(w, esz, True)[1] if kname == "fused"
+            else stage_work(w, esz)[kname][1])
+    out = os.path.join(PROFILES, f"traffic_{kname}_{w.name}.txt")
+    bench_cmd = f"python bench.py --workload {w.name} --steps 5 --warmup 2 --no-decode --no-cpu-baseline"
+    lines = [
+        f"HBM traffic of {kre} on {w.name} from rocprofv3 --pmc (one counter per run)",
+        f"  fetch: rocprofv3 --pmc FETCH_SIZE --kernel-include-regex {kre} --output-format csv -- {bench_cmd}",
+        f"  write: rocprofv3 --pmc WRITE_SIZE --kernel-include-regex {kre} --output-format csv -- {bench_cmd}",
+        "  calibration: the same two counters over python bench.py --copy-calibration --steps 5",
+        f"source_sha256_16: {source_hash(src)}",
+        f"fetch_kib_per_dispatch: {fk:.1f}  (mean of {nf} dispatches)",
+        f"write_kib_per_dispatch: {wk:.1f}  (mean of {nw} dispatches)",
+        f"copy_of_{COPY_BYTES}_bytes: FETCH_SIZE {cfk:.1f} KiB, WRITE_SIZE {cwk:.1f} KiB",
+        f"fetch_factor: {f_fac:.4f}  write_factor: {w_fac:.4f}  (bytes per counted byte)",
+        f"hbm_bytes_per_launch: {hbm:.6e}",
+        f"algorithmic_bytes_per_launch: {algo:.6e}",
+        f"traffic_over_algorithmic: {hbm / algo:.3f}",
+    ]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,7 +372,15 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "staged", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (traffic counter calibration)")
+    ap.add_argument("--pmc-summary", metavar="DIR",
+                    help="write profiles/traffic_<kernel>_<workload>.txt from --pmc runs in DIR")
+    ap.add_argument("--pmc-kernel", default="fused", choices=["fused", "scan", "ut"])
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the operator shards over sequences/heads with no communication; run one "
@@ -302,6 +391,9 @@ def main():
         sys.exit(1)
     _lib.lib()   # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(args, dev)
+        return
     w = wl.FORWARD_WORKLOADS[args.workload]
     print(f"[bench] forward {w.name} path={args.path}", file=sys.stderr, flush=True)
     res, host = bench_forward(args, w, dev)
