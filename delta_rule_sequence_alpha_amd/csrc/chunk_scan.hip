@@ -59,15 +59,53 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) S[mk][r] = S0 ? S0[sbase + (16 * mk + 4 * g + r) * DV + col] : 0.f;
 
+    // The next chunk's tiles are loaded into registers while this chunk is
+    // computed (chunks past the end re-load the last chunk, never stored).
+    // Shapes whose tiles would not fit in registers load each tile at the top
+    // of its chunk instead, one tile at a time.
+    using RW = TileRegs<T, C, DK, NT>;
+    using RU = TileRegs<T, C, TV, NT>;
+    using RA = TileRegs<T, C, C, NT>;
+    constexpr bool PREFETCH = 3 * RW::PER + RU::PER + RA::PER <= 40;
+    RW rW, rQ, rK;
+    RU rU;
+    RA rA;
+    auto load_all = [&](int cn) {
+        cn = min(cn, nchunks - 1);
+        const long t0 = (long)bh * L + (long)cn * C;
+        const int vn = min(C, L - cn * C);
+        rW.load(w + t0 * DK, DK, vn);
+        rQ.load(q + t0 * DK, DK, vn);
+        rK.load(k + t0 * DK, DK, vn);
+        rU.load(u + t0 * DV + tile * TV, DV, vn);
+        rA.load(aqk + ((long)bh * nchunks + cn) * C * C, C, C);
+    };
+    if constexpr (PREFETCH) load_all(0);
+
     for (int c = 0; c < nchunks; ++c) {
         const long tok0 = (long)bh * L + (long)c * C;
         const int valid = min(C, L - c * C);
         __syncthreads();   // the previous chunk is done with LDS
-        load_tile<T, DK, NT>(sW, Lay::LDK, w + tok0 * DK, DK, valid, C);
-        load_tile<T, DK, NT>(sQ, Lay::LDK, q + tok0 * DK, DK, valid, C);
-        load_tile<T, DK, NT>(sK, Lay::LDK, k + tok0 * DK, DK, valid, C);
-        load_tile<T, TV, NT>(sU, Lay::LDU, u + tok0 * DV + tile * TV, DV, valid, C);
-        load_tile<T, C, NT>(sA, Lay::LDC, aqk + ((long)bh * nchunks + c) * C * C, C, C, C);
+        if constexpr (PREFETCH) {
+            rW.store(sW, Lay::LDK, valid);
+            rQ.store(sQ, Lay::LDK, valid);
+            rK.store(sK, Lay::LDK, valid);
+            rU.store(sU, Lay::LDU, valid);
+            rA.store(sA, Lay::LDC, C);
+            load_all(c + 1);
+        } else {
+            RW t;
+            t.load(w + tok0 * DK, DK, valid);
+            t.store(sW, Lay::LDK, valid);
+            t.load(q + tok0 * DK, DK, valid);
+            t.store(sQ, Lay::LDK, valid);
+            t.load(k + tok0 * DK, DK, valid);
+            t.store(sK, Lay::LDK, valid);
+            rU.load(u + tok0 * DV + tile * TV, DV, valid);
+            rU.store(sU, Lay::LDU, valid);
+            rA.load(aqk + ((long)bh * nchunks + c) * C * C, C, C);
+            rA.store(sA, Lay::LDC, C);
+        }
         __syncthreads();
 
         // E = U - W S
@@ -127,18 +165,19 @@ hipError_t launch_scan(const void *q, const void *k, const void *w, const void *
     return hipGetLastError();
 }
 
-// Waves per workgroup: enough workgroups to cover the 256 CUs when the
-// sequences allow it, else wider tiles (fewer redundant LDS loads).
+// Waves per workgroup (1, 2 or 4; an explicit nw > 0 caps it).
 template <typename T, int DK, int DV, int C>
 hipError_t launch_scan_auto(const void *q, const void *k, const void *w, const void *u,
                             const void *aqk, const float *S0, void *o, float *SL, int BH, int L,
                             int nw, hipStream_t st)
 {
-    if (nw <= 0) {
-        nw = 1;
-        if (DV >= 32 && (long)BH * (DV / 32) >= 256) nw = 2;
-    }
-    if (nw == 2 && DV >= 32)
+    // Every wave owns 16 columns whatever NW is (the number of waves, hence of
+    // busy SIMDs, is BH * DV / 16); wider tiles share each chunk's loads
+    // between more waves.
+    if (nw <= 0) nw = DV >= 64 ? 4 : DV >= 32 ? 2 : 1;
+    if (nw >= 4 && DV >= 64)
+        return launch_scan<T, DK, DV, C, 4>(q, k, w, u, aqk, S0, o, SL, BH, L, st);
+    if (nw >= 2 && DV >= 32)
         return launch_scan<T, DK, DV, C, 2>(q, k, w, u, aqk, S0, o, SL, BH, L, st);
     return launch_scan<T, DK, DV, C, 1>(q, k, w, u, aqk, S0, o, SL, BH, L, st);
 }

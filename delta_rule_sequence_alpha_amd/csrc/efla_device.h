@@ -155,23 +155,44 @@ __device__ __forceinline__ f32x4 mm_lds(f32x4 acc, const T *A, int lda, int i0, 
     return acc;
 }
 
-// Cooperative copy of a rows x COLS tile (COLS elements contiguous per row in
-// global memory, row stride g_ld) into LDS (row stride s_ld), 16 bytes per
-// thread per step.  Rows >= rows_valid are filled with zeros.
-template <typename T, int COLS, int NTHREADS>
-__device__ __forceinline__ void load_tile(T *s, int s_ld, const T *gsrc, long g_ld, int rows_valid,
-                                          int rows)
-{
-    constexpr int V = 16 / sizeof(T);
+// A ROWS x COLS tile of a chunk (COLS contiguous elements per row in global
+// memory) held in the registers of the NT threads of a workgroup, 16 bytes per
+// thread per step, so that every load of the tile is in flight at once and can
+// be issued a chunk ahead of its use.  Rows >= valid are read from row
+// valid - 1 (always inside the tensor) and written to LDS as zeros.
+template <typename T, int ROWS, int COLS, int NT>
+struct TileRegs {
+    static constexpr int V = 16 / sizeof(T);
     static_assert(COLS % V == 0, "tile width must be a multiple of 16 bytes");
-    constexpr int VPR = COLS / V;
-    for (int idx = threadIdx.x; idx < rows * VPR; idx += NTHREADS) {
-        const int r = idx / VPR, cv = idx - r * VPR;
-        uint4 val = make_uint4(0u, 0u, 0u, 0u);
-        if (r < rows_valid) val = *reinterpret_cast<const uint4 *>(gsrc + r * g_ld + cv * V);
-        *reinterpret_cast<uint4 *>(s + r * s_ld + cv * V) = val;
+    static constexpr int VPR = COLS / V;
+    static constexpr int N = ROWS * VPR;
+    static constexpr int PER = (N + NT - 1) / NT;
+    static constexpr bool EXACT = N % NT == 0;
+    uint4 r[PER];
+
+    __device__ __forceinline__ void load(const T *g, long g_ld, int valid)
+    {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int idx = (int)threadIdx.x + j * NT;
+            const int row = min(idx / VPR, valid - 1), cv = idx % VPR;
+            if (EXACT || idx < N)
+                r[j] = *reinterpret_cast<const uint4 *>(g + (long)row * g_ld + cv * V);
+        }
     }
-}
+
+    __device__ __forceinline__ void store(T *s, int s_ld, int valid) const
+    {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int idx = (int)threadIdx.x + j * NT;
+            const int row = idx / VPR, cv = idx % VPR;
+            const unsigned m = row < valid ? ~0u : 0u;
+            const uint4 x = make_uint4(r[j].x & m, r[j].y & m, r[j].z & m, r[j].w & m);
+            if (EXACT || idx < N) *reinterpret_cast<uint4 *>(s + row * s_ld + cv * V) = x;
+        }
+    }
+};
 
 // alpha from beta and lambda (Methodology 3 of the EFLA technical summary):
 // (1 - e^{-beta lambda}) / lambda, evaluated as beta * phi(x), x = beta lambda,

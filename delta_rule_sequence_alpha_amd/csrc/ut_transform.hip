@@ -59,9 +59,16 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
     const long tok0 = (long)bh * L + (long)c * C;
     const int valid = min(C, L - c * C);
 
-    load_tile<T, DK, 256>(sK, Lay::LDK, k + tok0 * DK, DK, valid, C);
-    load_tile<T, DK, 256>(sQ, Lay::LDK, q + tok0 * DK, DK, valid, C);
-    load_tile<T, DV, 256>(sV, Lay::LDV, v + tok0 * DV, DV, valid, C);
+    {   // every load of the chunk in flight before the first LDS store
+        TileRegs<T, C, DK, 256> tk, tq;
+        TileRegs<T, C, DV, 256> tv;
+        tk.load(k + tok0 * DK, DK, valid);
+        tq.load(q + tok0 * DK, DK, valid);
+        tv.load(v + tok0 * DV, DV, valid);
+        tk.store(sK, Lay::LDK, valid);
+        tq.store(sQ, Lay::LDK, valid);
+        tv.store(sV, Lay::LDV, valid);
+    }
     for (int i = threadIdx.x; i < C * Lay::LDG; i += 256) sT[i] = 0.f;
     for (int i = threadIdx.x; i < C; i += 256) sAl[i] = (i < valid) ? alpha[tok0 + i] : 0.f;
     __syncthreads();
