@@ -39,6 +39,14 @@ __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// v_mfma_f32_16x16x16_bf16: lane feeds 4 bf16 of A (row l16, k = 4g..4g+3)
+// and of B (column l16, the same k) -- an acc tile's own layout.
+__device__ __forceinline__ f32x4 mma(bf16x4 a, bf16x4 b, f32x4 c)
+{
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);

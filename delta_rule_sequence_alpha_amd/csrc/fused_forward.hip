@@ -27,7 +27,22 @@
 //    signalled that K is in LDS.
 // The scan and prep groups meet at one workgroup barrier per chunk; the only
 // other hand-off is the K wave's one-way signal to the Q wave, a counter in
-// LDS.  The scan reads K^T operands with the transposing LDS read of gfx950.
+// LDS.
+//
+// LDS formats chosen for the readers:
+//  * Q and K rows (d_k = 128): 256-byte rows whose 16-byte chunks are XOR-
+//    swizzled by the row, so the 16-row column reads of the K S / Q S operands
+//    and the 4-row transposing reads of the K^T operand are bank-conflict free.
+//  * The chunk-local matrices the scan multiplies (G below the diagonal,
+//    tril(Q K^T), T_ii) are stored as MFMA A-operand fragments, lane-major: the
+//    prep waves compute each tile transposed (operands swapped, G and Q K^T
+//    being inner products) so that the accumulator already sits in fragment
+//    order, and the scan reads each fragment with one contiguous access.
+//  * G and tril(Q K^T) are stored negated, and the scan keeps -Q S and -O, so
+//    every subtraction of the chunk algebra is an MFMA accumulation.
+// Tails: loads through buffer resources bounded by the valid rows return
+// zeros past the end (beta = 0 makes those tokens the identity) and output
+// stores past the end are dropped.
 #include "efla_device.h"
 #include "efla_launch.h"
 
@@ -36,32 +51,45 @@ namespace efla {
 namespace {
 
 using bf = __bf16;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NP = 2;                 // prep waves per workgroup
 constexpr int kSpinMax = 1 << 22;     // bound on the prep-wave wait (never reached in practice)
+constexpr int kRsrcWord3 = 0x00020000;   // raw (unswizzled, stride 0) buffer resource
+
+// Buffer resource over the first `bytes` bytes at p: loads past the end
+// return zeros, stores past the end are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes < 0 ? 0 : bytes,
+                                             kRsrcWord3);
+}
 
 template <int DK, int DV, int C, int NS>
 struct FusedLayout {
     static constexpr int TV = 16 * NS;
-    static constexpr int MC = C / 16;
+    static constexpr int MC = C / 16, NKC = (MC + 1) / 2;
     static constexpr int NW = NS + NP;
-    static constexpr int LDK = DK + 8, LDV = TV + 8, LDC = C + 8, LDT = 16 + 8, LDD = 20;
+    static constexpr int LDK = DK == 128 ? 128 : DK + 8;   // Q / K row (elements)
+    static constexpr int LDV = TV + 16;                     // V tile row
+    static constexpr int LDO = C + 12;                      // output staging: one column
+    static constexpr int LDD = 20;                          // fp32 G_ii
     // one chunk of inputs
     static constexpr size_t bQ = 0;
     static constexpr size_t bK = bQ + 2 * C * LDK;
     static constexpr size_t bV = bK + 2 * C * LDK;
     static constexpr size_t bBeta = bV + 2 * C * LDV;
     static constexpr size_t inBytes = (bBeta + 4 * C + 15) / 16 * 16;
-    // one chunk of chunk-local quantities
-    static constexpr size_t pGb = 0;                          // bf16 G, blocks below the diagonal
-    static constexpr size_t pA = pGb + 2 * C * LDC;           // bf16 tril(Q K^T)
-    static constexpr size_t pTd = pA + 2 * C * LDC;           // bf16 T_ii: row i -> T_{i/16}[i%16][:]
-    static constexpr size_t pGt = pTd + 2 * C * LDT;          // fp32 G_bb transposed: [b][col][row]
-    static constexpr size_t pLam = pGt + 4 * MC * 16 * LDD;   // fp32 lambda
-    static constexpr size_t pAl = pLam + 4 * C;               // fp32 alpha
+    // one chunk of chunk-local quantities; [i][s][lane] x 16 bytes holds the
+    // A fragments of tiles (i, 2s) and (i, 2s+1)
+    static constexpr size_t pG = 0;                          // -G_{i,m}, m < i
+    static constexpr size_t pA = pG + 1024 * MC * NKC;       // -tril(Q K^T)
+    static constexpr size_t pT = pA + 1024 * MC * NKC;       // T_ii: [i][lane] x 8 bytes
+    static constexpr size_t pGt = pT + 512 * MC;             // fp32 G_ii: [16i + col][row]
+    static constexpr size_t pAl = pGt + 4 * 16 * LDD * MC;   // fp32 alpha
     static constexpr size_t prepBytes = (pAl + 4 * C + 15) / 16 * 16;
-    // output staging tile
-    static constexpr size_t oBytes = (2 * C * LDV + 15) / 16 * 16;
+    // output staging tile, transposed: [column][token]
+    static constexpr size_t oBytes = (2 * TV * LDO + 15) / 16 * 16;
     static constexpr size_t offIn = 0;
     static constexpr size_t offPrep = 2 * inBytes;
     static constexpr size_t offO = offPrep + 2 * prepBytes;
@@ -70,6 +98,18 @@ struct FusedLayout {
 };
 
 __device__ __forceinline__ bf16x4 zb4() { return to_bf16x4(zero4()); }
+__device__ __forceinline__ f32x4 neg(f32x4 x) { return f32x4{-x[0], -x[1], -x[2], -x[3]}; }
+
+// Element offset of the 16-byte chunk c (d_k columns 8c .. 8c+7) of row `row`
+// of a Q or K tile in LDS.  d_k = 128: the chunk index is XORed with a
+// bijection of row mod 16 that spreads both 16 consecutive rows (same chunk)
+// and 4 consecutive rows x 4 consecutive chunks over distinct banks.
+template <int DK>
+__device__ __forceinline__ int kofs(int row, int c)
+{
+    if constexpr (DK == 128) return row * 128 + 8 * (c ^ (((row & 3) << 2) | ((row >> 2) & 3)));
+    else return row * (DK + 8) + 8 * c;
+}
 
 // Which d_k row each accumulator row of the state holds.  S is kept as
 // DK/16 accumulator tiles; tile t = 2s + h (h = 0, 1) and acc row i = 4q + e
@@ -84,103 +124,93 @@ __device__ __forceinline__ int srow(int t, int i)
     return 32 * (t >> 1) + 8 * (i >> 2) + 4 * (t & 1) + (i & 3);
 }
 
-// a if c, else zeros (component-wise, so it stays in registers)
-__device__ __forceinline__ uint4 keep(bool c, uint4 a)
+// transposing LDS read: within each 16-lane group, lane l receives element
+// l%4 of the 4 x 16-bit values addressed by lane 4e + l/4, for e = 0..3
+__device__ __forceinline__ bf16x4 ds_read_tr(const bf *p)
 {
-    return make_uint4(c ? a.x : 0u, c ? a.y : 0u, c ? a.z : 0u, c ? a.w : 0u);
-}
-
-// MFMA operand for row tile `mt` and 32-wide k-block `s` of an LDS matrix
-// (element (i,k) at M[i*ld+k], or M[k*ld+i] when STRIDED), k in the PERM
-// order of an acc tile: {32s+4g..+3, 32s+16+4g..+3}.  KT = 16-wide k tiles.
-template <bool STRIDED, int KT>
-__device__ __forceinline__ bf16x8 a_perm(const bf *M, int ld, int mt, int s)
-{
-    const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
-    const int i = 16 * mt + l16;
-    const bf16x4 a1 = run4<STRIDED>(M, ld, i, 32 * s + 4 * g);
-    const bf16x4 a2 = (2 * s + 1 < KT) ? run4<STRIDED>(M, ld, i, 32 * s + 16 + 4 * g) : zb4();
-    return cat(a1, a2);
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(p));
+    return __builtin_bit_cast(bf16x4, r);
 }
 
 // Row tile `mt`, k-block `s` of Q or K as the A operand against the state
-// (rows in the srow order): one 16-byte read of d_k columns 32s+8g..+7.
+// (rows in the srow order): d_k columns 32s+8g .. +7, one 16-byte read.
 template <int DK>
-__device__ __forceinline__ bf16x8 a_row(const bf *M, int ld, int mt, int s)
+__device__ __forceinline__ bf16x8 a_row(const bf *M, int mt, int s)
 {
-    if constexpr (DK < 32) return a_perm<false, DK / 16>(M, ld, mt, s);
     const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
-    return *reinterpret_cast<const bf16x8 *>(M + (16 * mt + l16) * ld + 32 * s + 8 * g);
+    if constexpr (DK < 32) {   // one 16-wide k tile: PERM order, upper half zero
+        return cat(*reinterpret_cast<const bf16x4 *>(M + (16 * mt + l16) * (DK + 8) + 4 * g), zb4());
+    } else {
+        return *reinterpret_cast<const bf16x8 *>(M + kofs<DK>(16 * mt + l16, 4 * s + g));
+    }
 }
 
-// Same, NAT order {32s+8g..+7}: both operands of a product read from LDS.
-template <int K>
-__device__ __forceinline__ bf16x8 a_nat(const bf *M, int ld, int row, int s)
+// Row `row`, NAT k-block s of Q or K (d_k columns 32s+8g .. +7; zeros past d_k).
+template <int DK>
+__device__ __forceinline__ bf16x8 a_nat(const bf *M, int row, int s)
 {
     const int g = (threadIdx.x & 63) >> 4;
-    const int k = 32 * s + 8 * g;
-    if (k >= K) return cat(zb4(), zb4());
-    return cat(run4<false>(M, ld, row, k), run4<false>(M, ld, row, k + 4));
+    if (32 * s + 8 * g >= DK) return cat(zb4(), zb4());
+    return *reinterpret_cast<const bf16x8 *>(M + kofs<DK>(row, 4 * s + g));
 }
 
-// B operand (PERM order) from KT acc tiles: k-block s = tiles 2s, 2s+1.
-template <int KT>
-__device__ __forceinline__ bf16x8 b_acc(const f32x4 (&T)[KT], int s)
+// K^T operand for state tile mt (d_k rows srow(mt, 0..15)) and token
+// k-block s, PERM order: lane (l16, g) gets K[32s+4g+r][srow(mt,l16)] and
+// K[32s+16+4g+r][srow(mt,l16)].  srow(mt, 4q..4q+3) are 4 consecutive d_k,
+// so lane l16 of the group points the read at K[c0 + l16/4][srow(mt, 4*(l16%4))].
+template <int DK, int MC>
+__device__ __forceinline__ bf16x8 a_kt(const bf *sK, int mt, int s)
 {
-    return cat(to_bf16x4(T[2 * s]), (2 * s + 1 < KT) ? to_bf16x4(T[2 * s + 1]) : zb4());
+    constexpr int LDK = DK == 128 ? 128 : DK + 8;
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+    const int col = srow<DK>(mt, 4 * (l16 & 3));
+    const bf *base = sK + kofs<DK>(32 * s + 4 * g + (l16 >> 2), col >> 3) + (col & 7);
+    const bf16x4 a1 = ds_read_tr(base);
+    const bf16x4 a2 = (2 * s + 1 < MC) ? ds_read_tr(base + 16 * LDK) : zb4();
+    return cat(a1, a2);
+}
+
+// B operand (PERM order) from KT acc tiles, negated: k-block s = tiles 2s, 2s+1.
+template <int KT>
+__device__ __forceinline__ bf16x8 b_acc_neg(const f32x4 (&T)[KT], int s)
+{
+    return cat(to_bf16x4(neg(T[2 * s])), (2 * s + 1 < KT) ? to_bf16x4(neg(T[2 * s + 1])) : zb4());
 }
 
 // One chunk's inputs in the registers of one prep wave: the K wave holds K
 // and beta, the Q wave Q and the V tile.  Row-major 16-byte vectors, lane t
-// taking vectors t, t+64, ...
+// taking vectors t, t+64, ...  Loads go through buffer resources that end at
+// the chunk's last valid row, so rows past it (and a chunk past the end of
+// the sequence, valid <= 0) arrive as zeros with no branch.
 template <int DK, int DV, int C, int NS>
 struct ChunkRegs {
     using Lay = FusedLayout<DK, DV, C, NS>;
     static constexpr int TV = Lay::TV;
     static constexpr int VM = C * DK / 8, VV = C * TV / 8;       // vectors of K (or Q), of V
     static constexpr int PM = (VM + 63) / 64, PV = (VV + 63) / 64;
-    uint4 m[PM], v[PV];
+    u32x4 m[PM], v[PV];
     float beta;
 
-    // Branch-free: rows past `valid` (>= 1) re-read row valid-1 and are
-    // zeroed afterwards, so every lane issues the same loads and the compiler
-    // can count them when it places waits behind later loads and stores.
     __device__ __forceinline__ void load(bool kwave, int lane, const bf *gq, const bf *gk,
                                          const bf *gv, const float *gb, int valid)
     {
-        const bf *gm = kwave ? gk : gq;
-        if (valid >= C) {   // full chunk: plain row-major loads, same count as below
-#pragma unroll
-            for (int i = 0; i < PM; ++i) {
-                const int idx = min(lane + i * 64, VM - 1);
-                m[i] = *reinterpret_cast<const uint4 *>(gm + idx * 8);
-            }
-            if (kwave) {
-                beta = gb[min(lane, C - 1)];
-            } else {
-#pragma unroll
-                for (int i = 0; i < PV; ++i) {
-                    const int idx = min(lane + i * 64, VV - 1), row = idx / (TV / 8), cv = idx % (TV / 8);
-                    v[i] = *reinterpret_cast<const uint4 *>(gv + (long)row * DV + cv * 8);
-                }
-            }
-            return;
-        }
+        const auto rm = rsrc(kwave ? gk : gq, valid * DK * 2);
 #pragma unroll
         for (int i = 0; i < PM; ++i) {
-            const int idx = min(lane + i * 64, VM - 1), row = idx / (DK / 8), cv = idx % (DK / 8);
-            const uint4 a = *reinterpret_cast<const uint4 *>(gm + (long)min(row, valid - 1) * DK + cv * 8);
-            m[i] = keep(row < valid, a);
+            const int idx = min(lane + i * 64, VM - 1);
+            m[i] = __builtin_amdgcn_raw_buffer_load_b128(rm, idx * 16, 0, 0);
         }
         if (kwave) {
-            const float bt = gb[min(lane, valid - 1)];
-            beta = lane < valid ? bt : 0.f;
+            beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 rsrc(gb, valid * 4), min(lane, C - 1) * 4, 0, 0));
         } else {
+            const auto rv = rsrc(gv, ((valid - 1) * DV + TV) * 2);
 #pragma unroll
             for (int i = 0; i < PV; ++i) {
                 const int idx = min(lane + i * 64, VV - 1), row = idx / (TV / 8), cv = idx % (TV / 8);
-                const uint4 a = *reinterpret_cast<const uint4 *>(gv + (long)min(row, valid - 1) * DV + cv * 8);
-                v[i] = keep(row < valid, a);
+                v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (row * DV + cv * 8) * 2, 0, 0);
             }
         }
     }
@@ -191,7 +221,7 @@ struct ChunkRegs {
 #pragma unroll
         for (int i = 0; i < PM; ++i) {
             const int idx = lane + i * 64, row = idx / (DK / 8), cv = idx % (DK / 8);
-            if (VM % 64 == 0 || idx < VM) *reinterpret_cast<uint4 *>(sM + row * Lay::LDK + cv * 8) = m[i];
+            if (VM % 64 == 0 || idx < VM) *reinterpret_cast<u32x4 *>(sM + kofs<DK>(row, cv)) = m[i];
         }
         if (kwave) {
             if (lane < C) reinterpret_cast<float *>(buf + Lay::bBeta)[lane] = beta;
@@ -200,7 +230,7 @@ struct ChunkRegs {
 #pragma unroll
             for (int i = 0; i < PV; ++i) {
                 const int idx = lane + i * 64, row = idx / (TV / 8), cv = idx % (TV / 8);
-                if (VV % 64 == 0 || idx < VV) *reinterpret_cast<uint4 *>(sV + row * Lay::LDV + cv * 8) = v[i];
+                if (VV % 64 == 0 || idx < VV) *reinterpret_cast<u32x4 *>(sV + row * Lay::LDV + cv * 8) = v[i];
             }
         }
     }
@@ -225,10 +255,19 @@ __device__ __forceinline__ void q_wait(unsigned *ctr, unsigned target)
     asm volatile("" ::: "memory");
 }
 
-// K wave, step 1: Gram tiles G = K K^T on and below the diagonal (diagonal
-// blocks transposed in fp32 with lambda from their diagonal, the others in
-// bf16).  All operands are read first, then the MFMAs of every tile run
-// k-block by k-block, so no tile waits on another's accumulation chain.
+// Offset (elements) of the A fragment of tile (i, m) for the calling lane in a
+// [i][m/2][lane] x 16-byte fragment array.
+template <int NKC>
+__device__ __forceinline__ int frag(int i, int m)
+{
+    return ((i * NKC + (m >> 1)) * 64 + (threadIdx.x & 63)) * 8 + (m & 1) * 4;
+}
+
+// K wave, step 1: Gram tiles on and below the diagonal.  Tile (it, jt) is
+// computed as K_jt K_it^T, whose accumulator is G[16it + l16][16jt + 4g + r]:
+// the A fragment of G_{it,jt}.  Diagonal tiles go to LDS in fp32 (lambda is
+// their diagonal), the others negated in bf16.  All operands are read first,
+// then the MFMAs of every tile run k-block by k-block.
 template <int DK, int DV, int C, int NS>
 __device__ __forceinline__ void prep_gram(const char *in, char *prep)
 {
@@ -236,14 +275,13 @@ __device__ __forceinline__ void prep_gram(const char *in, char *prep)
     constexpr int MC = Lay::MC, NKS = (DK + 31) / 32, NT = MC * (MC + 1) / 2;
     const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
     const bf *sK = reinterpret_cast<const bf *>(in + Lay::bK);
-    bf *sGb = reinterpret_cast<bf *>(prep + Lay::pGb);
+    bf *sG = reinterpret_cast<bf *>(prep + Lay::pG);
     float *sGt = reinterpret_cast<float *>(prep + Lay::pGt);
-    float *sLam = reinterpret_cast<float *>(prep + Lay::pLam);
-    bf16x8 kb[MC][NKS];   // K row blocks as operands (NAT order)
+    bf16x8 kb[MC][NKS];
 #pragma unroll
     for (int b = 0; b < MC; ++b)
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) kb[b][s] = a_nat<DK>(sK, Lay::LDK, 16 * b + l16, s);
+        for (int s = 0; s < NKS; ++s) kb[b][s] = a_nat<DK>(sK, 16 * b + l16, s);
     __builtin_amdgcn_sched_barrier(0);
     f32x4 acc[NT];
 #pragma unroll
@@ -254,7 +292,7 @@ __device__ __forceinline__ void prep_gram(const char *in, char *prep)
 #pragma unroll
         for (int it = 0; it < MC; ++it)
 #pragma unroll
-            for (int jt = 0; jt <= it; ++jt, ++t) acc[t] = mma(kb[it][s], kb[jt][s], acc[t]);
+            for (int jt = 0; jt <= it; ++jt, ++t) acc[t] = mma(kb[jt][s], kb[it][s], acc[t]);
     }
     __builtin_amdgcn_sched_barrier(0);
     int t = 0;
@@ -262,22 +300,15 @@ __device__ __forceinline__ void prep_gram(const char *in, char *prep)
     for (int it = 0; it < MC; ++it)
 #pragma unroll
         for (int jt = 0; jt <= it; ++jt, ++t) {
-            if (it == jt) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 4 * g + r;
-                    sGt[(it * 16 + l16) * Lay::LDD + row] = acc[t][r];
-                    if (row == l16) sLam[16 * it + row] = acc[t][r];
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sGb[(16 * it + 4 * g + r) * Lay::LDC + 16 * jt + l16] = static_cast<bf>(acc[t][r]);
-            }
+            if (it == jt)
+                *reinterpret_cast<f32x4 *>(sGt + (16 * it + l16) * Lay::LDD + 4 * g) = acc[t];
+            else
+                *reinterpret_cast<bf16x4 *>(sG + frag<Lay::NKC>(it, jt)) = to_bf16x4(neg(acc[t]));
         }
 }
 
-// Q wave: tril(Q K^T), diagonal tiles masked; operands first, as above.
+// Q wave: tril(Q K^T), negated.  Tile (it, jt) = K_jt Q_it^T, accumulator
+// (Q K^T)[16it + l16][16jt + 4g + r] (A fragment order); diagonal tiles masked.
 template <int DK, int DV, int C, int NS>
 __device__ __forceinline__ void prep_qk(const char *in, char *prep)
 {
@@ -292,8 +323,8 @@ __device__ __forceinline__ void prep_qk(const char *in, char *prep)
     for (int b = 0; b < MC; ++b)
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-            kb[b][s] = a_nat<DK>(sK, Lay::LDK, 16 * b + l16, s);
-            qa[b][s] = a_nat<DK>(sQ, Lay::LDK, 16 * b + l16, s);
+            kb[b][s] = a_nat<DK>(sK, 16 * b + l16, s);
+            qa[b][s] = a_nat<DK>(sQ, 16 * b + l16, s);
         }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 acc[NT];
@@ -305,26 +336,29 @@ __device__ __forceinline__ void prep_qk(const char *in, char *prep)
 #pragma unroll
         for (int it = 0; it < MC; ++it)
 #pragma unroll
-            for (int jt = 0; jt <= it; ++jt, ++t) acc[t] = mma(qa[it][s], kb[jt][s], acc[t]);
+            for (int jt = 0; jt <= it; ++jt, ++t) acc[t] = mma(kb[jt][s], qa[it][s], acc[t]);
     }
     __builtin_amdgcn_sched_barrier(0);
     int t = 0;
 #pragma unroll
     for (int it = 0; it < MC; ++it)
 #pragma unroll
-        for (int jt = 0; jt <= it; ++jt, ++t)
+        for (int jt = 0; jt <= it; ++jt, ++t) {
+            f32x4 a = neg(acc[t]);
+            if (it == jt) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * it + 4 * g + r, col = 16 * jt + l16;
-                sA[row * Lay::LDC + col] = static_cast<bf>(col <= row ? acc[t][r] : 0.f);
+                for (int r = 0; r < 4; ++r)
+                    if (4 * g + r > l16) a[r] = 0.f;
             }
+            *reinterpret_cast<bf16x4 *>(sA + frag<Lay::NKC>(it, jt)) = to_bf16x4(a);
+        }
 }
 
-// K wave, step 2: alpha (lane = token), then every T_ii, lane group b owning
-// block b and lane l16 its column l16.  Right-looking substitution: once
-// T[i][j] is known it is eliminated from every later row, so each of the 16
-// steps carries independent FMAs; the next step's column of G is read while
-// the current one is applied.
+// K wave, step 2: alpha (lane = token; lambda is the Gram diagonal), then
+// every T_ii, lane group b owning block b and lane l16 its column l16.
+// Right-looking substitution: once T[i][j] is known it is eliminated from
+// every later row, so each of the 16 steps carries independent FMAs.  T[i][j]
+// is written to its place in the A fragment of T_bb: lane 16(j/4) + i, slot j%4.
 template <int DK, int DV, int C, int NS>
 __device__ __forceinline__ void prep_diag(const char *in, char *prep)
 {
@@ -333,10 +367,9 @@ __device__ __forceinline__ void prep_diag(const char *in, char *prep)
     const int lane = threadIdx.x & 63;
     const float *sB = reinterpret_cast<const float *>(in + Lay::bBeta);
     const float *sGt = reinterpret_cast<const float *>(prep + Lay::pGt);
-    const float *sLam = reinterpret_cast<const float *>(prep + Lay::pLam);
     float *sAl = reinterpret_cast<float *>(prep + Lay::pAl);
-    bf *sTd = reinterpret_cast<bf *>(prep + Lay::pTd);
-    if (lane < C) sAl[lane] = efla_alpha(sB[lane], sLam[lane]);
+    bf *sT = reinterpret_cast<bf *>(prep + Lay::pT);
+    if (lane < C) sAl[lane] = efla_alpha(sB[lane], sGt[lane * Lay::LDD + (lane & 15)]);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int b = lane >> 4;
     if (b < MC) {
@@ -360,10 +393,11 @@ __device__ __forceinline__ void prep_diag(const char *in, char *prep)
         float acc[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) acc[m] = (m == j) ? 1.f : 0.f;
+        bf *tcol = sT + (b * 64 + 16 * (j >> 2)) * 4 + (j & 3);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const float t = al[i] * acc[i];
-            sTd[(16 * b + i) * Lay::LDT + j] = static_cast<bf>(t);
+            tcol[4 * i] = static_cast<bf>(t);
 #pragma unroll
             for (int m = i + 1; m < 16; ++m) {
                 const float4 gv = gcol[i][m >> 2];
@@ -397,35 +431,40 @@ struct PrepCtx {
     __device__ __forceinline__ int valid_of(int c) const { return min(C, L - c * C); }
 };
 
-// Chunks past the end re-load the last chunk (never stored), keeping the
-// number of loads in flight the same on every path.
+// A chunk past the end (n >= nchunks) has valid <= 0: its loads return zeros
+// and touch no memory.
 template <int DK, int DV, int C, int NS>
 __device__ __attribute__((always_inline)) inline void prep_load(const PrepCtx<DK, DV, C, NS> &x,
                                                                 ChunkRegs<DK, DV, C, NS> &r, int n)
 {
-    n = min(n, x.nchunks - 1);
-    const long off = (long)n * C;
+    const int nc = min(n, x.nchunks - 1);
+    const long off = (long)nc * C;
     r.load(x.kwave, x.lane, x.qb + off * DK, x.kb + off * DK, x.vb + off * DV, x.bb + off,
-           x.valid_of(n));
+           n == nc ? x.valid_of(n) : 0);
 }
 
-// A chunk's output rows, staged in LDS by the scan waves, to HBM (Q wave);
-// rows past `valid` rewrite row valid-1 with its own value.
+// A chunk's output rows, staged transposed in LDS by the scan waves, to HBM
+// (Q wave).  Each 16-lane group turns a 16-row x 8-column block back into
+// rows with two transposing reads and writes 16 bytes per row; rows past the
+// chunk's valid ones fall outside the buffer resource and are dropped.
 template <int DK, int DV, int C, int NS>
 __device__ __attribute__((always_inline)) inline void prep_store_out(const PrepCtx<DK, DV, C, NS> &x,
                                                                      int n)
 {
     using Lay = FusedLayout<DK, DV, C, NS>;
-    constexpr int VPR = Lay::TV / 8, NV = C * VPR;
+    constexpr int TV = Lay::TV, VPR = TV / 8, NITEM = (C / 16) * VPR;
     const bf *os = x.obuf(n & 1);
     const int valid = x.valid_of(n);
-    bf *dst = x.ob + (long)n * C * DV;
+    const auto ro = rsrc(x.ob + (long)n * C * DV, ((valid - 1) * DV + TV) * 2);
+    const int l16 = x.lane & 15, grp = x.lane >> 4;
 #pragma unroll
-    for (int i = 0; i < (NV + 63) / 64; ++i) {
-        const int idx = min(x.lane + i * 64, NV - 1);
-        const int row = min(idx / VPR, valid - 1), cv = idx % VPR;
-        *reinterpret_cast<uint4 *>(dst + (long)row * DV + cv * 8) =
-            *reinterpret_cast<const uint4 *>(os + row * Lay::LDV + cv * 8);
+    for (int it = 0; it < (NITEM + 3) / 4; ++it) {
+        const int item = min(grp + 4 * it, NITEM - 1);   // a repeated item rewrites equal data
+        const int rb = item / VPR, cv = item % VPR;
+        const bf *p = os + (8 * cv + (l16 >> 2)) * Lay::LDO + 16 * rb + 4 * (l16 & 3);
+        const bf16x8 row = cat(ds_read_tr(p), ds_read_tr(p + 4 * Lay::LDO));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, row), ro,
+                                               ((16 * rb + l16) * DV + 8 * cv) * 2, 0, 0);
     }
 }
 
@@ -452,58 +491,40 @@ __device__ __attribute__((always_inline)) inline void prep_interval(const PrepCt
     }
 }
 
-// transposing LDS read: within each 16-lane group, lane l receives element
-// l%4 of the 4 x 16-bit values addressed by lane 4e + l/4, for e = 0..3
-__device__ __forceinline__ bf16x4 ds_read_tr(const bf *p)
-{
-    typedef short v4i16 __attribute__((ext_vector_type(4)));
-    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16 *)(p));
-    return __builtin_bit_cast(bf16x4, r);
-}
-
-// K^T operand for state tile mt (d_k rows srow(mt, 0..15)) and token
-// k-block s, PERM order: lane (l16, g) gets K[32s+4g+r][srow(mt,l16)] and
-// K[32s+16+4g+r][srow(mt,l16)].  srow(mt, 4q..4q+3) are 4 consecutive d_k,
-// so lane l16 of the group points the read at K[c0 + l16/4][srow(mt, 4*(l16%4))].
-template <int DK, int MC>
-__device__ __forceinline__ bf16x8 a_kt(const bf *sK, int ld, int mt, int s)
-{
-    const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
-    const bf *base = sK + (32 * s + 4 * g + (l16 >> 2)) * ld + srow<DK>(mt, 4 * (l16 & 3));
-    const bf16x4 a1 = ds_read_tr(base);
-    const bf16x4 a2 = (2 * s + 1 < MC) ? ds_read_tr(base + 16 * ld) : zb4();
-    return cat(a1, a2);
-}
-
 // One chunk of the scan for the calling wave (16 state columns).
 template <int DK, int DV, int C, int NS>
 __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK / 16], const char *in,
                                                                  const char *pr, bf *os, int wv)
 {
     using Lay = FusedLayout<DK, DV, C, NS>;
-    constexpr int MC = Lay::MC, MK = DK / 16, NKS = (MK + 1) / 2, NKC = (MC + 1) / 2;
+    constexpr int MC = Lay::MC, MK = DK / 16, NKS = (MK + 1) / 2, NKC = Lay::NKC;
     const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
     const bf *sQ = reinterpret_cast<const bf *>(in + Lay::bQ);
     const bf *sK = reinterpret_cast<const bf *>(in + Lay::bK);
     const bf *sV = reinterpret_cast<const bf *>(in + Lay::bV);
-    const bf *sGb = reinterpret_cast<const bf *>(pr + Lay::pGb);
+    const bf *sG = reinterpret_cast<const bf *>(pr + Lay::pG);
     const bf *sA = reinterpret_cast<const bf *>(pr + Lay::pA);
-    const bf *sTd = reinterpret_cast<const bf *>(pr + Lay::pTd);
+    const bf *sT = reinterpret_cast<const bf *>(pr + Lay::pT);
 
-    // X = K S and O = Q S, k-block by k-block with the next block's operands
-    // already in flight
+    // X = V - K S and On = -Q S, k-block by k-block with the next block's
+    // operands already in flight; X starts from V (transposing read: lane
+    // (l16, g) gets V[16mt + 4g + r][16wv + l16]).
     bf16x8 bS[NKS];
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) bS[s] = b_acc(S, s);
-    f32x4 X[MC], O[MC];
+    for (int s = 0; s < NKS; ++s) bS[s] = b_acc_neg(S, s);
+    f32x4 X[MC], On[MC];
 #pragma unroll
-    for (int mt = 0; mt < MC; ++mt) X[mt] = O[mt] = zero4();
+    for (int mt = 0; mt < MC; ++mt) {
+        const bf16x4 vv = ds_read_tr(sV + (16 * mt + 4 * g + (l16 >> 2)) * Lay::LDV + 16 * wv + 4 * (l16 & 3));
+        X[mt] = f32x4{static_cast<float>(vv[0]), static_cast<float>(vv[1]),
+                      static_cast<float>(vv[2]), static_cast<float>(vv[3])};
+        On[mt] = zero4();
+    }
     bf16x8 ak[2][MC], aq[2][MC];
 #pragma unroll
     for (int mt = 0; mt < MC; ++mt) {
-        ak[0][mt] = a_row<DK>(sK, Lay::LDK, mt, 0);
-        aq[0][mt] = a_row<DK>(sQ, Lay::LDK, mt, 0);
+        ak[0][mt] = a_row<DK>(sK, mt, 0);
+        aq[0][mt] = a_row<DK>(sQ, mt, 0);
     }
     // reads of k-block s+1 are issued before the MFMAs of block s and kept
     // there, so each MFMA group covers the next group's LDS latency
@@ -512,72 +533,73 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
         if (s + 1 < NKS) {
 #pragma unroll
             for (int mt = 0; mt < MC; ++mt) {
-                ak[(s + 1) & 1][mt] = a_row<DK>(sK, Lay::LDK, mt, s + 1);
-                aq[(s + 1) & 1][mt] = a_row<DK>(sQ, Lay::LDK, mt, s + 1);
+                ak[(s + 1) & 1][mt] = a_row<DK>(sK, mt, s + 1);
+                aq[(s + 1) & 1][mt] = a_row<DK>(sQ, mt, s + 1);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) {
             X[mt] = mma(ak[s & 1][mt], bS[s], X[mt]);
-            O[mt] = mma(aq[s & 1][mt], bS[s], O[mt]);
+            On[mt] = mma(aq[s & 1][mt], bS[s], On[mt]);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // E by block substitution on X = V - K S
-    bf16x8 ga[MC * NKC];                  // G_{i, 2s..2s+1} for i >= 1
+    // E by block substitution: y = X_i + sum_{m<i} (-G_im) E_m, E_i = T_ii y.
+    // Every MFMA that accumulates onto an earlier MFMA's result has the same
+    // shape (k = 32; a lone block is padded with zeros): the accumulator is
+    // forwarded between dependent MFMAs of one shape only.  T_ii y starts
+    // from zero and uses k = 16.
+    bf16x8 ga[MC * NKC];
 #pragma unroll
     for (int i = 1; i < MC; ++i)
 #pragma unroll
         for (int s = 0; 2 * s < i; ++s) {
-            const bool two = 2 * s + 1 < i;
-            const bf *arow = sGb + (16 * i + l16) * Lay::LDC + 32 * s + 4 * g;
-            ga[i * NKC + s] = cat(*reinterpret_cast<const bf16x4 *>(arow),
-                                  two ? *reinterpret_cast<const bf16x4 *>(arow + 16) : zb4());
+            if (2 * s + 1 < i) ga[i * NKC + s] = *reinterpret_cast<const bf16x8 *>(sG + frag<NKC>(i, 2 * s));
+            else ga[i * NKC + s] = cat(*reinterpret_cast<const bf16x4 *>(sG + frag<NKC>(i, 2 * s)), zb4());
         }
     bf16x4 ta[MC];
 #pragma unroll
-    for (int i = 0; i < MC; ++i) ta[i] = *reinterpret_cast<const bf16x4 *>(sTd + (16 * i + l16) * Lay::LDT + 4 * g);
-#pragma unroll
-    for (int mt = 0; mt < MC; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            X[mt][r] = to_f32(sV[(16 * mt + 4 * g + r) * Lay::LDV + 16 * wv + l16]) - X[mt][r];
+    for (int i = 0; i < MC; ++i) ta[i] = *reinterpret_cast<const bf16x4 *>(sT + (i * 64 + lane) * 4);
     f32x4 E[MC];
+    bf16x4 eb[MC];
 #pragma unroll
     for (int i = 0; i < MC; ++i) {
         f32x4 y = X[i];
 #pragma unroll
         for (int s = 0; 2 * s < i; ++s) {   // only blocks m < i of E exist yet
-            const bf16x8 be = cat(to_bf16x4(E[2 * s]), 2 * s + 1 < i ? to_bf16x4(E[2 * s + 1]) : zb4());
-            y -= mma(ga[i * NKC + s], be, zero4());
+            y = mma(ga[i * NKC + s], cat(eb[2 * s], 2 * s + 1 < i ? eb[2 * s + 1] : zb4()), y);
         }
-        E[i] = mma(cat(ta[i], zb4()), cat(to_bf16x4(y), zb4()), zero4());
+        E[i] = mma(ta[i], to_bf16x4(y), zero4());
+        eb[i] = to_bf16x4(E[i]);
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // O += tril(Q K^T) E;  S += K^T E   (operands read a group ahead)
+    // On += (-tril(Q K^T)) E;  S += K^T E   (operands read a group ahead)
     bf16x8 bE[NKC];
 #pragma unroll
-    for (int s = 0; s < NKC; ++s) bE[s] = b_acc(E, s);
+    for (int s = 0; s < NKC; ++s) bE[s] = cat(eb[2 * s], 2 * s + 1 < MC ? eb[2 * s + 1] : zb4());
     bf16x8 aa[MC * NKC];
 #pragma unroll
     for (int s = 0; s < NKC; ++s)
 #pragma unroll
-        for (int mt = 0; mt < MC; ++mt)
-            if (2 * s <= mt) aa[mt * NKC + s] = a_perm<false, MC>(sA, Lay::LDC, mt, s);
+        for (int mt = 0; mt < MC; ++mt) {
+            if (2 * s + 1 <= mt) aa[mt * NKC + s] = *reinterpret_cast<const bf16x8 *>(sA + frag<NKC>(mt, 2 * s));
+            else if (2 * s == mt) aa[mt * NKC + s] = cat(*reinterpret_cast<const bf16x4 *>(sA + frag<NKC>(mt, 2 * s)), zb4());
+        }
     constexpr int KG = MK / 2 > 0 ? MK / 2 : 1;   // K^T row tiles per read group
     bf16x8 akt[2][KG];
 #pragma unroll
-    for (int j = 0; j < KG; ++j) akt[0][j] = a_kt<DK, MC>(sK, Lay::LDK, j, 0);
+    for (int j = 0; j < KG; ++j) akt[0][j] = a_kt<DK, MC>(sK, j, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < NKC; ++s)
 #pragma unroll
-        for (int mt = 0; mt < MC; ++mt)
-            if (2 * s <= mt) O[mt] = mma(aa[mt * NKC + s], bE[s], O[mt]);
+        for (int mt = 0; mt < MC; ++mt) {
+            if (2 * s <= mt) On[mt] = mma(aa[mt * NKC + s], bE[s], On[mt]);
+        }
     constexpr int NG = (MK + KG - 1) / KG * NKC;   // read groups of K^T
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
@@ -586,7 +608,7 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
             const int s1 = (gi + 1) / ((MK + KG - 1) / KG), mt1 = ((gi + 1) % ((MK + KG - 1) / KG)) * KG;
 #pragma unroll
             for (int j = 0; j < KG; ++j)
-                if (mt1 + j < MK) akt[(gi + 1) & 1][j] = a_kt<DK, MC>(sK, Lay::LDK, mt1 + j, s1);
+                if (mt1 + j < MK) akt[(gi + 1) & 1][j] = a_kt<DK, MC>(sK, mt1 + j, s1);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -595,11 +617,11 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
         __builtin_amdgcn_sched_barrier(0);
     }
 
+    // O = -On to the transposed staging tile: column 16wv + l16, tokens 16mt + 4g ..
 #pragma unroll
     for (int mt = 0; mt < MC; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            os[(16 * mt + 4 * g + r) * Lay::LDV + 16 * wv + l16] = static_cast<bf>(O[mt][r]);
+        *reinterpret_cast<bf16x4 *>(os + (16 * wv + l16) * Lay::LDO + 16 * mt + 4 * g) =
+            to_bf16x4(neg(On[mt]));
 }
 
 template <int DK, int DV, int C, int NS>
@@ -621,14 +643,6 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
     const long tokb = (long)bh * L;
 
     if (threadIdx.x == 0) *reinterpret_cast<unsigned *>(smem + Lay::offCtr) = 0u;
-    // upper tiles of tril(Q K^T) stay zero for the whole kernel
-    for (int b = 0; b < 2; ++b) {
-        bf *sA = reinterpret_cast<bf *>(smem + Lay::offPrep + b * Lay::prepBytes + Lay::pA);
-        for (int i = threadIdx.x; i < C * C; i += 64 * Lay::NW) {
-            const int r = i / C, cc = i - r * C;
-            if ((cc >> 4) > (r >> 4)) sA[r * Lay::LDC + cc] = static_cast<bf>(0.f);
-        }
-    }
     __syncthreads();
 
     if (wv < NS) {
