@@ -54,10 +54,15 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
 
     f32x4 S[MK];
     const long sbase = (long)bh * DK * DV;
+    if (S0) {   // one branch around all the loads, so they are in flight together
 #pragma unroll
-    for (int mk = 0; mk < MK; ++mk)
+        for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[mk][r] = S0 ? S0[sbase + (16 * mk + 4 * g + r) * DV + col] : 0.f;
+            for (int r = 0; r < 4; ++r) S[mk][r] = S0[sbase + (16 * mk + 4 * g + r) * DV + col];
+    } else {
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk) S[mk] = zero4();
+    }
 
     // The next chunk's tiles are loaded into registers while this chunk is
     // computed (chunks past the end re-load the last chunk, never stored).

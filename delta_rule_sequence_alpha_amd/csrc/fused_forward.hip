@@ -17,22 +17,23 @@
 //  * scan waves (0 .. NS-1): wave w keeps 16 columns x all d_k rows of S in
 //    MFMA accumulators and runs only the S-dependent chain of each chunk:
 //    K S, Q S, the block substitution for E, tril(Q K^T) E, K^T E.
-//  * prep wave NS ("K wave"), one chunk ahead of the scan: moves the chunk's
-//    K and beta from registers (prefetched a chunk ahead) into LDS, then forms
-//    the Gram tiles, lambda, alpha and every T_ii (one 16-lane group per
-//    diagonal block).
-//  * prep wave NS+1 ("Q wave"), one chunk ahead: moves Q and the V tile into
-//    LDS, writes the previous chunk's output from an LDS staging tile to HBM
-//    with full-width stores, then forms tril(Q K^T) once the K wave has
-//    signalled that K is in LDS.
-// The scan and prep groups meet at one workgroup barrier per chunk; the only
-// other hand-off is the K wave's one-way signal to the Q wave, a counter in
-// LDS.
+//  * prep wave NS ("K wave"), one chunk ahead of the scan: forms the Gram
+//    tiles, lambda, alpha and every T_ii (one 16-lane group per diagonal
+//    block), and starts the direct-to-LDS loads of K and beta two chunks ahead.
+//  * prep wave NS+1 ("Q wave"), one chunk ahead: writes the previous chunk's
+//    output from an LDS staging tile to HBM with full-width stores, forms
+//    tril(Q K^T), and starts the direct-to-LDS loads of Q and the V tile two
+//    chunks ahead.
+// Inputs rotate through three LDS buffers (chunk c in scan, c+1 in prep, c+2
+// arriving).  All waves meet at one workgroup barrier per chunk, before which
+// each prep wave has waited for its own loads; nothing else synchronises.
 //
 // LDS formats chosen for the readers:
-//  * Q and K rows (d_k = 128): 256-byte rows whose 16-byte chunks are XOR-
-//    swizzled by the row, so the 16-row column reads of the K S / Q S operands
-//    and the 4-row transposing reads of the K^T operand are bank-conflict free.
+//  * Q and K rows: unpadded rows whose 16-byte chunks are XOR-swizzled by the
+//    row (at d_k = 128 the 16-row column reads of the K S / Q S operands and
+//    the 4-row transposing reads of the K^T operand are then bank-conflict
+//    free).  A direct-to-LDS load writes 64 consecutive 16-byte slots, so
+//    each lane fetches the global chunk that belongs in its slot.
 //  * The chunk-local matrices the scan multiplies (G below the diagonal,
 //    tril(Q K^T), T_ii) are stored as MFMA A-operand fragments, lane-major: the
 //    prep waves compute each tile transposed (operands swapped, G and Q K^T
@@ -40,9 +41,9 @@
 //    order, and the scan reads each fragment with one contiguous access.
 //  * G and tril(Q K^T) are stored negated, and the scan keeps -Q S and -O, so
 //    every subtraction of the chunk algebra is an MFMA accumulation.
-// Tails: loads through buffer resources bounded by the valid rows return
-// zeros past the end (beta = 0 makes those tokens the identity) and output
-// stores past the end are dropped.
+// Tails: loads through buffer resources bounded by the valid rows write zeros
+// past the end (beta = 0 makes those tokens the identity) and output stores
+// past the end are dropped.
 #include "efla_device.h"
 #include "efla_launch.h"
 
@@ -65,50 +66,70 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes)
                                              kRsrcWord3);
 }
 
+// Fragment slots (16 bytes per lane, two 16x16 tiles each) of the lower
+// block-triangular chunk matrices: tril(Q K^T) has slots (i, s) for
+// 2s <= i, G below the diagonal for 2s < i; row-major, compact.
+constexpr int a_slot(int i, int s)
+{
+    int o = 0;
+    for (int t = 0; t < i; ++t) o += t / 2 + 1;
+    return o + s;
+}
+constexpr int g_slot(int i, int s)
+{
+    int o = 0;
+    for (int t = 1; t < i; ++t) o += (t - 1) / 2 + 1;
+    return o + s;
+}
+
 template <int DK, int DV, int C, int NS>
 struct FusedLayout {
     static constexpr int TV = 16 * NS;
     static constexpr int MC = C / 16, NKC = (MC + 1) / 2;
     static constexpr int NW = NS + NP;
-    static constexpr int LDK = DK == 128 ? 128 : DK + 8;   // Q / K row (elements)
-    static constexpr int LDV = TV + 16;                     // V tile row
+    static constexpr int NB = 3;                            // input buffers in rotation
     static constexpr int LDO = C + 12;                      // output staging: one column
     static constexpr int LDD = 20;                          // fp32 G_ii
-    // one chunk of inputs
+    // one chunk of inputs: Q, K [C][DK] (swizzled), V tile [C][TV], beta [C]
     static constexpr size_t bQ = 0;
-    static constexpr size_t bK = bQ + 2 * C * LDK;
-    static constexpr size_t bV = bK + 2 * C * LDK;
-    static constexpr size_t bBeta = bV + 2 * C * LDV;
+    static constexpr size_t bK = bQ + 2 * C * DK;
+    static constexpr size_t bV = bK + 2 * C * DK;
+    static constexpr size_t bBeta = bV + 2 * C * TV;
     static constexpr size_t inBytes = (bBeta + 4 * C + 15) / 16 * 16;
-    // one chunk of chunk-local quantities; [i][s][lane] x 16 bytes holds the
-    // A fragments of tiles (i, 2s) and (i, 2s+1)
-    static constexpr size_t pG = 0;                          // -G_{i,m}, m < i
-    static constexpr size_t pA = pG + 1024 * MC * NKC;       // -tril(Q K^T)
-    static constexpr size_t pT = pA + 1024 * MC * NKC;       // T_ii: [i][lane] x 8 bytes
-    static constexpr size_t pGt = pT + 512 * MC;             // fp32 G_ii: [16i + col][row]
-    static constexpr size_t pAl = pGt + 4 * 16 * LDD * MC;   // fp32 alpha
-    static constexpr size_t prepBytes = (pAl + 4 * C + 15) / 16 * 16;
-    // output staging tile, transposed: [column][token]
+    // one chunk of chunk-local quantities (double-buffered), A fragments
+    static constexpr size_t pG = 0;                            // -G_{i,m}, m < i
+    static constexpr size_t pA = pG + 1024 * g_slot(MC, 0);    // -tril(Q K^T)
+    static constexpr size_t pT = pA + 1024 * a_slot(MC, 0);    // T_ii: [i][lane] x 8 bytes
+    static constexpr size_t prepBytes = pT + 512 * MC;
+    // K-wave scratch, used within one interval: fp32 G_ii [16i + col][row], alpha
+    static constexpr size_t kGt = 0;
+    static constexpr size_t kAl = kGt + 4 * 16 * LDD * MC;
+    static constexpr size_t kBytes = kAl + 4 * C;
+    // output staging tile (double-buffered), transposed: [column][token]
     static constexpr size_t oBytes = (2 * TV * LDO + 15) / 16 * 16;
     static constexpr size_t offIn = 0;
-    static constexpr size_t offPrep = 2 * inBytes;
-    static constexpr size_t offO = offPrep + 2 * prepBytes;
-    static constexpr size_t offCtr = offO + 2 * oBytes;
-    static constexpr size_t bytes = offCtr + 16;
+    static constexpr size_t offPrep = NB * inBytes;
+    static constexpr size_t offK = offPrep + 2 * prepBytes;
+    static constexpr size_t offO = (offK + kBytes + 15) / 16 * 16;
+    static constexpr size_t bytes = offO + 2 * oBytes;
 };
 
 __device__ __forceinline__ bf16x4 zb4() { return to_bf16x4(zero4()); }
 __device__ __forceinline__ f32x4 neg(f32x4 x) { return f32x4{-x[0], -x[1], -x[2], -x[3]}; }
 
 // Element offset of the 16-byte chunk c (d_k columns 8c .. 8c+7) of row `row`
-// of a Q or K tile in LDS.  d_k = 128: the chunk index is XORed with a
-// bijection of row mod 16 that spreads both 16 consecutive rows (same chunk)
-// and 4 consecutive rows x 4 consecutive chunks over distinct banks.
+// of a Q or K tile in LDS.  The chunk index is XORed with a bijection of
+// row mod 16 that (with 16 chunks per row) spreads both 16 consecutive rows at
+// one chunk and 4 consecutive rows x 4 consecutive chunks over distinct banks.
+template <int DK>
+__device__ __forceinline__ int kswz(int row)
+{
+    return (((row & 3) << 2) | ((row >> 2) & 3)) & (DK / 8 - 1);
+}
 template <int DK>
 __device__ __forceinline__ int kofs(int row, int c)
 {
-    if constexpr (DK == 128) return row * 128 + 8 * (c ^ (((row & 3) << 2) | ((row >> 2) & 3)));
-    else return row * (DK + 8) + 8 * c;
+    return row * DK + 8 * (c ^ kswz<DK>(row));
 }
 
 // Which d_k row each accumulator row of the state holds.  S is kept as
@@ -141,7 +162,8 @@ __device__ __forceinline__ bf16x8 a_row(const bf *M, int mt, int s)
 {
     const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
     if constexpr (DK < 32) {   // one 16-wide k tile: PERM order, upper half zero
-        return cat(*reinterpret_cast<const bf16x4 *>(M + (16 * mt + l16) * (DK + 8) + 4 * g), zb4());
+        return cat(*reinterpret_cast<const bf16x4 *>(M + kofs<DK>(16 * mt + l16, g >> 1) + 4 * (g & 1)),
+                   zb4());
     } else {
         return *reinterpret_cast<const bf16x8 *>(M + kofs<DK>(16 * mt + l16, 4 * s + g));
     }
@@ -163,12 +185,11 @@ __device__ __forceinline__ bf16x8 a_nat(const bf *M, int row, int s)
 template <int DK, int MC>
 __device__ __forceinline__ bf16x8 a_kt(const bf *sK, int mt, int s)
 {
-    constexpr int LDK = DK == 128 ? 128 : DK + 8;
     const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
     const int col = srow<DK>(mt, 4 * (l16 & 3));
     const bf *base = sK + kofs<DK>(32 * s + 4 * g + (l16 >> 2), col >> 3) + (col & 7);
     const bf16x4 a1 = ds_read_tr(base);
-    const bf16x4 a2 = (2 * s + 1 < MC) ? ds_read_tr(base + 16 * LDK) : zb4();
+    const bf16x4 a2 = (2 * s + 1 < MC) ? ds_read_tr(base + 16 * DK) : zb4();
     return cat(a1, a2);
 }
 
@@ -179,88 +200,61 @@ __device__ __forceinline__ bf16x8 b_acc_neg(const f32x4 (&T)[KT], int s)
     return cat(to_bf16x4(neg(T[2 * s])), (2 * s + 1 < KT) ? to_bf16x4(neg(T[2 * s + 1])) : zb4());
 }
 
-// One chunk's inputs in the registers of one prep wave: the K wave holds K
-// and beta, the Q wave Q and the V tile.  Row-major 16-byte vectors, lane t
-// taking vectors t, t+64, ...  Loads go through buffer resources that end at
-// the chunk's last valid row, so rows past it (and a chunk past the end of
-// the sequence, valid <= 0) arrive as zeros with no branch.
+// Direct-to-LDS load of one tile: instruction j writes bytes [1024 j, 1024 j
+// + 1024) of the LDS tile, lane i the 16 bytes at 1024 j + 16 i, fetched from
+// the global byte offset goff(e) of tile element e = 512 j + 8 i.  Lanes past
+// the tile's end are masked off.
+template <int BYTES, typename F>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, bf *lds, F goff)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < (BYTES + 1023) / 1024; ++j) {
+        const int e = 512 * j + 8 * lane;
+        if (BYTES % 1024 == 0 || 2 * e < BYTES)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void *)(lds + 512 * j), 16, goff(e), 0, 0, 0);
+    }
+}
+
+// The calling prep wave's share of chunk n's inputs, into input buffer `in`:
+// the K wave K and beta, the Q wave Q and the V tile.  The resources end at
+// the chunk's last valid row, so the rows past it arrive as zeros.
 template <int DK, int DV, int C, int NS>
-struct ChunkRegs {
+__device__ __forceinline__ void dma_chunk(bool kwave, char *in, const bf *gq, const bf *gk,
+                                          const bf *gv, const float *gb, int valid)
+{
     using Lay = FusedLayout<DK, DV, C, NS>;
-    static constexpr int TV = Lay::TV;
-    static constexpr int VM = C * DK / 8, VV = C * TV / 8;       // vectors of K (or Q), of V
-    static constexpr int PM = (VM + 63) / 64, PV = (VV + 63) / 64;
-    u32x4 m[PM], v[PV];
-    float beta;
-
-    __device__ __forceinline__ void load(bool kwave, int lane, const bf *gq, const bf *gk,
-                                         const bf *gv, const float *gb, int valid)
-    {
-        const auto rm = rsrc(kwave ? gk : gq, valid * DK * 2);
-#pragma unroll
-        for (int i = 0; i < PM; ++i) {
-            const int idx = min(lane + i * 64, VM - 1);
-            m[i] = __builtin_amdgcn_raw_buffer_load_b128(rm, idx * 16, 0, 0);
-        }
-        if (kwave) {
-            beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                 rsrc(gb, valid * 4), min(lane, C - 1) * 4, 0, 0));
-        } else {
-            const auto rv = rsrc(gv, ((valid - 1) * DV + TV) * 2);
-#pragma unroll
-            for (int i = 0; i < PV; ++i) {
-                const int idx = min(lane + i * 64, VV - 1), row = idx / (TV / 8), cv = idx % (TV / 8);
-                v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (row * DV + cv * 8) * 2, 0, 0);
-            }
-        }
+    constexpr int TV = Lay::TV;
+    // Q / K: the LDS slot of tile element e = (row, slot) holds global chunk
+    // slot ^ kswz(row) of that row
+    auto sw_off = [](int e) {
+        const int row = e / DK, slot = (e % DK) / 8;
+        return 2 * (row * DK + 8 * (slot ^ kswz<DK>(row)));
+    };
+    if (kwave) {
+        dma_tile<2 * C * DK>(rsrc(gk, valid * DK * 2), reinterpret_cast<bf *>(in + Lay::bK), sw_off);
+        const int lane = threadIdx.x & 63;
+        if (lane < C)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc(gb, valid * 4), (__attribute__((address_space(3))) void *)(in + Lay::bBeta), 4,
+                4 * lane, 0, 0, 0);
+    } else {
+        dma_tile<2 * C * DK>(rsrc(gq, valid * DK * 2), reinterpret_cast<bf *>(in + Lay::bQ), sw_off);
+        dma_tile<2 * C * TV>(rsrc(gv, ((valid - 1) * DV + TV) * 2), reinterpret_cast<bf *>(in + Lay::bV),
+                             [](int e) { return 2 * ((e / TV) * DV + e % TV); });
     }
-
-    __device__ __forceinline__ void store(bool kwave, int lane, char *buf) const
-    {
-        bf *sM = reinterpret_cast<bf *>(buf + (kwave ? Lay::bK : Lay::bQ));
-#pragma unroll
-        for (int i = 0; i < PM; ++i) {
-            const int idx = lane + i * 64, row = idx / (DK / 8), cv = idx % (DK / 8);
-            if (VM % 64 == 0 || idx < VM) *reinterpret_cast<u32x4 *>(sM + kofs<DK>(row, cv)) = m[i];
-        }
-        if (kwave) {
-            if (lane < C) reinterpret_cast<float *>(buf + Lay::bBeta)[lane] = beta;
-        } else {
-            bf *sV = reinterpret_cast<bf *>(buf + Lay::bV);
-#pragma unroll
-            for (int i = 0; i < PV; ++i) {
-                const int idx = lane + i * 64, row = idx / (TV / 8), cv = idx % (TV / 8);
-                if (VV % 64 == 0 || idx < VV) *reinterpret_cast<u32x4 *>(sV + row * Lay::LDV + cv * 8) = v[i];
-            }
-        }
-    }
-};
-
-// One-way hand-off from the K wave to the Q wave: the K wave's LDS writes
-// issued before k_signal() are visible to the Q wave after its matching
-// q_wait().  The wait is bounded; the counter only grows.
-__device__ __forceinline__ void k_signal(unsigned *ctr)
-{
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if ((threadIdx.x & 63) == 0)
-        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-__device__ __forceinline__ void q_wait(unsigned *ctr, unsigned target)
+// Offsets (elements) of the calling lane's A fragment of tile (i, m) in the
+// compact fragment arrays of -G (m < i) and -tril(Q K^T) (m <= i).
+__device__ __forceinline__ int gfrag(int i, int m)
 {
-    for (int it = 0; it < kSpinMax; ++it) {
-        if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    asm volatile("" ::: "memory");
+    return (g_slot(i, m >> 1) * 64 + (threadIdx.x & 63)) * 8 + (m & 1) * 4;
 }
-
-// Offset (elements) of the A fragment of tile (i, m) for the calling lane in a
-// [i][m/2][lane] x 16-byte fragment array.
-template <int NKC>
-__device__ __forceinline__ int frag(int i, int m)
+__device__ __forceinline__ int afrag(int i, int m)
 {
-    return ((i * NKC + (m >> 1)) * 64 + (threadIdx.x & 63)) * 8 + (m & 1) * 4;
+    return (a_slot(i, m >> 1) * 64 + (threadIdx.x & 63)) * 8 + (m & 1) * 4;
 }
 
 // K wave, step 1: Gram tiles on and below the diagonal.  Tile (it, jt) is
@@ -269,14 +263,14 @@ __device__ __forceinline__ int frag(int i, int m)
 // their diagonal), the others negated in bf16.  All operands are read first,
 // then the MFMAs of every tile run k-block by k-block.
 template <int DK, int DV, int C, int NS>
-__device__ __forceinline__ void prep_gram(const char *in, char *prep)
+__device__ __forceinline__ void prep_gram(const char *in, char *prep, char *ks)
 {
     using Lay = FusedLayout<DK, DV, C, NS>;
     constexpr int MC = Lay::MC, NKS = (DK + 31) / 32, NT = MC * (MC + 1) / 2;
     const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
     const bf *sK = reinterpret_cast<const bf *>(in + Lay::bK);
     bf *sG = reinterpret_cast<bf *>(prep + Lay::pG);
-    float *sGt = reinterpret_cast<float *>(prep + Lay::pGt);
+    float *sGt = reinterpret_cast<float *>(ks + Lay::kGt);
     bf16x8 kb[MC][NKS];
 #pragma unroll
     for (int b = 0; b < MC; ++b)
@@ -303,7 +297,7 @@ __device__ __forceinline__ void prep_gram(const char *in, char *prep)
             if (it == jt)
                 *reinterpret_cast<f32x4 *>(sGt + (16 * it + l16) * Lay::LDD + 4 * g) = acc[t];
             else
-                *reinterpret_cast<bf16x4 *>(sG + frag<Lay::NKC>(it, jt)) = to_bf16x4(neg(acc[t]));
+                *reinterpret_cast<bf16x4 *>(sG + gfrag(it, jt)) = to_bf16x4(neg(acc[t]));
         }
 }
 
@@ -350,7 +344,7 @@ __device__ __forceinline__ void prep_qk(const char *in, char *prep)
                 for (int r = 0; r < 4; ++r)
                     if (4 * g + r > l16) a[r] = 0.f;
             }
-            *reinterpret_cast<bf16x4 *>(sA + frag<Lay::NKC>(it, jt)) = to_bf16x4(a);
+            *reinterpret_cast<bf16x4 *>(sA + afrag(it, jt)) = to_bf16x4(a);
         }
 }
 
@@ -360,14 +354,14 @@ __device__ __forceinline__ void prep_qk(const char *in, char *prep)
 // every later row, so each of the 16 steps carries independent FMAs.  T[i][j]
 // is written to its place in the A fragment of T_bb: lane 16(j/4) + i, slot j%4.
 template <int DK, int DV, int C, int NS>
-__device__ __forceinline__ void prep_diag(const char *in, char *prep)
+__device__ __forceinline__ void prep_diag(const char *in, char *prep, char *ks)
 {
     using Lay = FusedLayout<DK, DV, C, NS>;
     constexpr int MC = Lay::MC;
     const int lane = threadIdx.x & 63;
     const float *sB = reinterpret_cast<const float *>(in + Lay::bBeta);
-    const float *sGt = reinterpret_cast<const float *>(prep + Lay::pGt);
-    float *sAl = reinterpret_cast<float *>(prep + Lay::pAl);
+    const float *sGt = reinterpret_cast<const float *>(ks + Lay::kGt);
+    float *sAl = reinterpret_cast<float *>(ks + Lay::kAl);
     bf *sT = reinterpret_cast<bf *>(prep + Lay::pT);
     if (lane < C) sAl[lane] = efla_alpha(sB[lane], sGt[lane * Lay::LDD + (lane & 15)]);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -418,30 +412,15 @@ struct PrepCtx {
     bf *ob;
     int L, nchunks, lane;
     bool kwave;
-    __device__ __forceinline__ char *inb(int i) const { return smem + Lay::offIn + i * Lay::inBytes; }
-    __device__ __forceinline__ char *prb(int i) const { return smem + Lay::offPrep + i * Lay::prepBytes; }
+    __device__ __forceinline__ char *inb(int c) const { return smem + Lay::offIn + (c % Lay::NB) * Lay::inBytes; }
+    __device__ __forceinline__ char *prb(int c) const { return smem + Lay::offPrep + (c & 1) * Lay::prepBytes; }
+    __device__ __forceinline__ char *ks() const { return smem + Lay::offK; }
     __device__ __forceinline__ bf *obuf(int i) const
     {
         return reinterpret_cast<bf *>(smem + Lay::offO + i * Lay::oBytes);
     }
-    __device__ __forceinline__ unsigned *ctr() const
-    {
-        return reinterpret_cast<unsigned *>(smem + Lay::offCtr);
-    }
     __device__ __forceinline__ int valid_of(int c) const { return min(C, L - c * C); }
 };
-
-// A chunk past the end (n >= nchunks) has valid <= 0: its loads return zeros
-// and touch no memory.
-template <int DK, int DV, int C, int NS>
-__device__ __attribute__((always_inline)) inline void prep_load(const PrepCtx<DK, DV, C, NS> &x,
-                                                                ChunkRegs<DK, DV, C, NS> &r, int n)
-{
-    const int nc = min(n, x.nchunks - 1);
-    const long off = (long)nc * C;
-    r.load(x.kwave, x.lane, x.qb + off * DK, x.kb + off * DK, x.vb + off * DV, x.bb + off,
-           n == nc ? x.valid_of(n) : 0);
-}
 
 // A chunk's output rows, staged transposed in LDS by the scan waves, to HBM
 // (Q wave).  Each 16-lane group turns a 16-row x 8-column block back into
@@ -449,11 +428,10 @@ __device__ __attribute__((always_inline)) inline void prep_load(const PrepCtx<DK
 // chunk's valid ones fall outside the buffer resource and are dropped.
 template <int DK, int DV, int C, int NS>
 __device__ __attribute__((always_inline)) inline void prep_store_out(const PrepCtx<DK, DV, C, NS> &x,
-                                                                     int n)
+                                                                     int n, const bf *os)
 {
     using Lay = FusedLayout<DK, DV, C, NS>;
     constexpr int TV = Lay::TV, VPR = TV / 8, NITEM = (C / 16) * VPR;
-    const bf *os = x.obuf(n & 1);
     const int valid = x.valid_of(n);
     const auto ro = rsrc(x.ob + (long)n * C * DV, ((valid - 1) * DV + TV) * 2);
     const int l16 = x.lane & 15, grp = x.lane >> 4;
@@ -468,27 +446,44 @@ __device__ __attribute__((always_inline)) inline void prep_store_out(const PrepC
     }
 }
 
-// One prep interval for chunk n (its inputs are in r on entry).  Loads of
-// chunk n+1 are issued as soon as r has been written to LDS.
+// One prep interval: start the loads of chunk n + 1 (into `dma`), write the
+// output of chunk out_chunk (Q wave, if >= 0; staged in `os`) and prepare
+// chunk n (if < nchunks) from its inputs in `in` into `pr`; then wait for
+// this wave's loads, so that they are complete once the interval's closing
+// barrier has been passed.  The buffers are distinct, and saying so
+// (__restrict__) lets the compiler see that the LDS reads here need not wait
+// for the direct-to-LDS loads in flight.
 template <int DK, int DV, int C, int NS>
-__device__ __attribute__((always_inline)) inline void prep_interval(const PrepCtx<DK, DV, C, NS> &x,
-                                                                    ChunkRegs<DK, DV, C, NS> &r,
-                                                                    int n, int out_chunk)
+__device__ __attribute__((always_inline)) inline void prep_interval(
+    const PrepCtx<DK, DV, C, NS> &x, int n, int out_chunk, char *__restrict__ dma,
+    char *__restrict__ in, char *__restrict__ pr, char *__restrict__ ks, bf *__restrict__ os)
 {
-    char *in = x.inb(n & 1);
-    char *pr = x.prb(n & 1);
-    r.store(x.kwave, x.lane, in);
-    prep_load(x, r, n + 1);
-    if (x.kwave) {
-        k_signal(x.ctr());
-        prep_gram<DK, DV, C, NS>(in, pr);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        prep_diag<DK, DV, C, NS>(in, pr);
-    } else {
-        if (out_chunk >= 0) prep_store_out(x, out_chunk);
-        q_wait(x.ctr(), (unsigned)(n + 1));
-        prep_qk<DK, DV, C, NS>(in, pr);
+    if (n + 1 < x.nchunks) {
+        const long off = (long)(n + 1) * C;
+        dma_chunk<DK, DV, C, NS>(x.kwave, dma, x.qb + off * DK, x.kb + off * DK, x.vb + off * DV,
+                                 x.bb + off, x.valid_of(n + 1));
     }
+    if (n < x.nchunks) {
+        if (x.kwave) {
+            prep_gram<DK, DV, C, NS>(in, pr, ks);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            prep_diag<DK, DV, C, NS>(in, pr, ks);
+        } else {
+            if (out_chunk >= 0) prep_store_out(x, out_chunk, os);
+            prep_qk<DK, DV, C, NS>(in, pr);
+        }
+    } else if (!x.kwave && out_chunk >= 0) {
+        prep_store_out(x, out_chunk, os);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int DK, int DV, int C, int NS>
+__device__ __attribute__((always_inline)) inline void prep_step(const PrepCtx<DK, DV, C, NS> &x,
+                                                                int n, int out_chunk)
+{
+    prep_interval(x, n, out_chunk, x.inb(n + 1), x.inb(n), x.prb(n), x.ks(),
+                  x.obuf(out_chunk & 1));
 }
 
 // One chunk of the scan for the calling wave (16 state columns).
@@ -515,7 +510,7 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
     f32x4 X[MC], On[MC];
 #pragma unroll
     for (int mt = 0; mt < MC; ++mt) {
-        const bf16x4 vv = ds_read_tr(sV + (16 * mt + 4 * g + (l16 >> 2)) * Lay::LDV + 16 * wv + 4 * (l16 & 3));
+        const bf16x4 vv = ds_read_tr(sV + (16 * mt + 4 * g + (l16 >> 2)) * Lay::TV + 16 * wv + 4 * (l16 & 3));
         X[mt] = f32x4{static_cast<float>(vv[0]), static_cast<float>(vv[1]),
                       static_cast<float>(vv[2]), static_cast<float>(vv[3])};
         On[mt] = zero4();
@@ -557,8 +552,8 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
     for (int i = 1; i < MC; ++i)
 #pragma unroll
         for (int s = 0; 2 * s < i; ++s) {
-            if (2 * s + 1 < i) ga[i * NKC + s] = *reinterpret_cast<const bf16x8 *>(sG + frag<NKC>(i, 2 * s));
-            else ga[i * NKC + s] = cat(*reinterpret_cast<const bf16x4 *>(sG + frag<NKC>(i, 2 * s)), zb4());
+            if (2 * s + 1 < i) ga[i * NKC + s] = *reinterpret_cast<const bf16x8 *>(sG + gfrag(i, 2 * s));
+            else ga[i * NKC + s] = cat(*reinterpret_cast<const bf16x4 *>(sG + gfrag(i, 2 * s)), zb4());
         }
     bf16x4 ta[MC];
 #pragma unroll
@@ -586,8 +581,8 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
     for (int s = 0; s < NKC; ++s)
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) {
-            if (2 * s + 1 <= mt) aa[mt * NKC + s] = *reinterpret_cast<const bf16x8 *>(sA + frag<NKC>(mt, 2 * s));
-            else if (2 * s == mt) aa[mt * NKC + s] = cat(*reinterpret_cast<const bf16x4 *>(sA + frag<NKC>(mt, 2 * s)), zb4());
+            if (2 * s + 1 <= mt) aa[mt * NKC + s] = *reinterpret_cast<const bf16x8 *>(sA + afrag(mt, 2 * s));
+            else if (2 * s == mt) aa[mt * NKC + s] = cat(*reinterpret_cast<const bf16x4 *>(sA + afrag(mt, 2 * s)), zb4());
         }
     constexpr int KG = MK / 2 > 0 ? MK / 2 : 1;   // K^T row tiles per read group
     bf16x8 akt[2][KG];
@@ -642,22 +637,24 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const long tokb = (long)bh * L;
 
-    if (threadIdx.x == 0) *reinterpret_cast<unsigned *>(smem + Lay::offCtr) = 0u;
-    __syncthreads();
-
     if (wv < NS) {
         // ------------------------------------------------------------ scan waves
         const int col = tile * TV + 16 * wv + l16;
         f32x4 S[MK];
         const long sbase = (long)bh * DK * DV;
+        if (S0) {   // one branch around all the loads, so they are in flight together
 #pragma unroll
-        for (int mk = 0; mk < MK; ++mk)
+            for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S[mk][r] = S0 ? S0[sbase + srow<DK>(mk, 4 * g + r) * DV + col] : 0.f;
+                for (int r = 0; r < 4; ++r) S[mk][r] = S0[sbase + srow<DK>(mk, 4 * g + r) * DV + col];
+        } else {
+#pragma unroll
+            for (int mk = 0; mk < MK; ++mk) S[mk] = zero4();
+        }
+        __syncthreads();   // prologue: chunk 0 loaded
         __syncthreads();   // prologue: chunk 0 prepared
         for (int c = 0; c < nchunks; ++c) {
-            scan_chunk<DK, DV, C, NS>(S, smem + Lay::offIn + (c & 1) * Lay::inBytes,
+            scan_chunk<DK, DV, C, NS>(S, smem + Lay::offIn + (c % Lay::NB) * Lay::inBytes,
                                       smem + Lay::offPrep + (c & 1) * Lay::prepBytes,
                                       reinterpret_cast<bf *>(smem + Lay::offO + (c & 1) * Lay::oBytes),
                                       wv);
@@ -673,19 +670,19 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
         const PrepCtx<DK, DV, C, NS> x{smem, q + tokb * DK, k + tokb * DK, v + tokb * DV + tile * TV,
                                        beta + tokb, o + tokb * DV + tile * TV, L, nchunks, lane,
                                        wv == NS};
-        ChunkRegs<DK, DV, C, NS> r;   // inputs of the next chunk to prepare
-        prep_load(x, r, 0);
-        prep_interval(x, r, 0, -1);   // prologue: chunk 0
+        dma_chunk<DK, DV, C, NS>(x.kwave, x.inb(0), x.qb, x.kb, x.vb, x.bb, x.valid_of(0));
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();                // prologue: chunk 0 loaded
+        prep_step(x, 0, -1);            // prologue: chunk 1 loading, chunk 0 prepared
         __syncthreads();
         for (int c = 0; c < nchunks; ++c) {
-            // interval c: the scan works on chunk c; prepare chunk c+1 and write
-            // the output of chunk c-1
-            if (c + 1 < nchunks) prep_interval(x, r, c + 1, c - 1);
-            else if (!x.kwave && c > 0) prep_store_out(x, c - 1);
+            // interval c: the scan works on chunk c; load chunk c+2, prepare
+            // chunk c+1 and write the output of chunk c-1
+            prep_step(x, c + 1, c - 1);
             __syncthreads();
         }
         __syncthreads();
-        if (!x.kwave) prep_store_out(x, nchunks - 1);
+        if (!x.kwave) prep_store_out(x, nchunks - 1, x.obuf((nchunks - 1) & 1));
     }
 }
 
