@@ -13,17 +13,18 @@
 //   T_ii = (I + D_i strictly_lower(G_ii))^{-1} D_i,
 // with T_ii from forward substitution in fp32 (no division by alpha).
 //
-// Workgroup = (sequence, tile of TV = 16*NS state columns), NS + 2 waves:
+// Workgroup = (sequence, tile of TV = 16*NS state columns), NS + 3 waves:
 //  * scan waves (0 .. NS-1): wave w keeps 16 columns x all d_k rows of S in
 //    MFMA accumulators and runs only the S-dependent chain of each chunk:
 //    K S, Q S, the block substitution for E, tril(Q K^T) E, K^T E.
-//  * prep wave NS ("K wave"), one chunk ahead of the scan: forms the Gram
-//    tiles, lambda, alpha and every T_ii (one 16-lane group per diagonal
-//    block), and starts the direct-to-LDS loads of K and beta two chunks ahead.
-//  * prep wave NS+1 ("Q wave"), one chunk ahead: writes the previous chunk's
-//    output from an LDS staging tile to HBM with full-width stores, forms
-//    tril(Q K^T), and starts the direct-to-LDS loads of Q and the V tile two
-//    chunks ahead.
+//  * prep wave NS ("K wave"): starts the direct-to-LDS loads of K and beta
+//    two chunks ahead, writes the previous chunk's output from an LDS staging
+//    tile to HBM with full-width stores, and forms the Gram tiles below the
+//    diagonal one chunk ahead.
+//  * prep wave NS+1 ("Q wave"): starts the loads of Q and the V tile two
+//    chunks ahead and forms tril(Q K^T) one chunk ahead.
+//  * prep wave NS+2 ("T wave"), one chunk ahead: the diagonal Gram tiles,
+//    lambda, alpha and every T_ii (one 16-lane group per diagonal block).
 // Inputs rotate through three LDS buffers (chunk c in scan, c+1 in prep, c+2
 // arriving).  All waves meet at one workgroup barrier per chunk, before which
 // each prep wave has waited for its own loads; nothing else synchronises.
@@ -54,7 +55,8 @@ namespace {
 using bf = __bf16;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int NP = 2;                 // prep waves per workgroup
+constexpr int NP = 3;                 // prep waves per workgroup
+enum Role { K_WAVE = 0, Q_WAVE = 1, T_WAVE = 2 };   // prep wave NS + role
 constexpr int kSpinMax = 1 << 22;     // bound on the prep-wave wait (never reached in practice)
 constexpr int kRsrcWord3 = 0x00020000;   // raw (unswizzled, stride 0) buffer resource
 
@@ -221,7 +223,7 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, bf *lds, F go
 // the K wave K and beta, the Q wave Q and the V tile.  The resources end at
 // the chunk's last valid row, so the rows past it arrive as zeros.
 template <int DK, int DV, int C, int NS>
-__device__ __forceinline__ void dma_chunk(bool kwave, char *in, const bf *gq, const bf *gk,
+__device__ __forceinline__ void dma_chunk(int role, char *in, const bf *gq, const bf *gk,
                                           const bf *gv, const float *gb, int valid)
 {
     using Lay = FusedLayout<DK, DV, C, NS>;
@@ -232,14 +234,14 @@ __device__ __forceinline__ void dma_chunk(bool kwave, char *in, const bf *gq, co
         const int row = e / DK, slot = (e % DK) / 8;
         return 2 * (row * DK + 8 * (slot ^ kswz<DK>(row)));
     };
-    if (kwave) {
+    if (role == K_WAVE) {
         dma_tile<2 * C * DK>(rsrc(gk, valid * DK * 2), reinterpret_cast<bf *>(in + Lay::bK), sw_off);
         const int lane = threadIdx.x & 63;
         if (lane < C)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc(gb, valid * 4), (__attribute__((address_space(3))) void *)(in + Lay::bBeta), 4,
                 4 * lane, 0, 0, 0);
-    } else {
+    } else if (role == Q_WAVE) {
         dma_tile<2 * C * DK>(rsrc(gq, valid * DK * 2), reinterpret_cast<bf *>(in + Lay::bQ), sw_off);
         dma_tile<2 * C * TV>(rsrc(gv, ((valid - 1) * DV + TV) * 2), reinterpret_cast<bf *>(in + Lay::bV),
                              [](int e) { return 2 * ((e / TV) * DV + e % TV); });
@@ -257,48 +259,58 @@ __device__ __forceinline__ int afrag(int i, int m)
     return (a_slot(i, m >> 1) * 64 + (threadIdx.x & 63)) * 8 + (m & 1) * 4;
 }
 
-// K wave, step 1: Gram tiles on and below the diagonal.  Tile (it, jt) is
-// computed as K_jt K_it^T, whose accumulator is G[16it + l16][16jt + 4g + r]:
-// the A fragment of G_{it,jt}.  Diagonal tiles go to LDS in fp32 (lambda is
-// their diagonal), the others negated in bf16.  All operands are read first,
-// then the MFMAs of every tile run k-block by k-block.
-template <int DK, int DV, int C, int NS>
+// Gram tiles.  Tile (it, jt) is computed as K_jt K_it^T, whose accumulator
+// is G[16it + l16][16jt + 4g + r]: the A fragment of G_{it,jt}.  DIAG: the
+// diagonal tiles, to fp32 scratch (lambda is their diagonal; T wave); else
+// the tiles below the diagonal, negated in bf16 (K wave).  All operands are
+// read first (k-block by k-block), then the MFMAs of every tile run k-block
+// by k-block.
+template <int DK, int DV, int C, int NS, bool DIAG>
 __device__ __forceinline__ void prep_gram(const char *in, char *prep, char *ks)
 {
     using Lay = FusedLayout<DK, DV, C, NS>;
-    constexpr int MC = Lay::MC, NKS = (DK + 31) / 32, NT = MC * (MC + 1) / 2;
+    constexpr int MC = Lay::MC, NKS = (DK + 31) / 32;
+    constexpr int NT = DIAG ? MC : MC * (MC - 1) / 2;
     const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
     const bf *sK = reinterpret_cast<const bf *>(in + Lay::bK);
     bf *sG = reinterpret_cast<bf *>(prep + Lay::pG);
     float *sGt = reinterpret_cast<float *>(ks + Lay::kGt);
-    bf16x8 kb[MC][NKS];
+    if constexpr (NT > 0) {
+        bf16x8 kb[NKS][MC];
 #pragma unroll
-    for (int b = 0; b < MC; ++b)
+        for (int s = 0; s < NKS; ++s)
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) kb[b][s] = a_nat<DK>(sK, 16 * b + l16, s);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 acc[NT];
+            for (int b = 0; b < MC; ++b) kb[s][b] = a_nat<DK>(sK, 16 * b + l16, s);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 acc[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = zero4();
+        for (int t = 0; t < NT; ++t) acc[t] = zero4();
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
+        for (int s = 0; s < NKS; ++s) {
+            int t = 0;
+#pragma unroll
+            for (int it = 0; it < MC; ++it)
+#pragma unroll
+                for (int jt = 0; jt <= it; ++jt) {
+                    if ((it == jt) != DIAG) continue;
+                    acc[t] = mma(kb[s][jt], kb[s][it], acc[t]);
+                    ++t;
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);
         int t = 0;
 #pragma unroll
         for (int it = 0; it < MC; ++it)
 #pragma unroll
-            for (int jt = 0; jt <= it; ++jt, ++t) acc[t] = mma(kb[jt][s], kb[it][s], acc[t]);
+            for (int jt = 0; jt <= it; ++jt) {
+                if ((it == jt) != DIAG) continue;
+                if (DIAG)
+                    *reinterpret_cast<f32x4 *>(sGt + (16 * it + l16) * Lay::LDD + 4 * g) = acc[t];
+                else
+                    *reinterpret_cast<bf16x4 *>(sG + gfrag(it, jt)) = to_bf16x4(neg(acc[t]));
+                ++t;
+            }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    int t = 0;
-#pragma unroll
-    for (int it = 0; it < MC; ++it)
-#pragma unroll
-        for (int jt = 0; jt <= it; ++jt, ++t) {
-            if (it == jt)
-                *reinterpret_cast<f32x4 *>(sGt + (16 * it + l16) * Lay::LDD + 4 * g) = acc[t];
-            else
-                *reinterpret_cast<bf16x4 *>(sG + gfrag(it, jt)) = to_bf16x4(neg(acc[t]));
-        }
 }
 
 // Q wave: tril(Q K^T), negated.  Tile (it, jt) = K_jt Q_it^T, accumulator
@@ -314,9 +326,9 @@ __device__ __forceinline__ void prep_qk(const char *in, char *prep)
     bf *sA = reinterpret_cast<bf *>(prep + Lay::pA);
     bf16x8 kb[MC][NKS], qa[MC][NKS];
 #pragma unroll
-    for (int b = 0; b < MC; ++b)
+    for (int s = 0; s < NKS; ++s)
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) {
+        for (int b = 0; b < MC; ++b) {
             kb[b][s] = a_nat<DK>(sK, 16 * b + l16, s);
             qa[b][s] = a_nat<DK>(sQ, 16 * b + l16, s);
         }
@@ -348,7 +360,7 @@ __device__ __forceinline__ void prep_qk(const char *in, char *prep)
         }
 }
 
-// K wave, step 2: alpha (lane = token; lambda is the Gram diagonal), then
+// T wave, after the diagonal Gram tiles: alpha (lane = token; lambda is the Gram diagonal), then
 // every T_ii, lane group b owning block b and lane l16 its column l16.
 // Right-looking substitution: once T[i][j] is known it is eliminated from
 // every later row, so each of the 16 steps carries independent FMAs.  T[i][j]
@@ -411,7 +423,7 @@ struct PrepCtx {
     const float *bb;
     bf *ob;
     int L, nchunks, lane;
-    bool kwave;
+    int role;
     __device__ __forceinline__ char *inb(int c) const { return smem + Lay::offIn + (c % Lay::NB) * Lay::inBytes; }
     __device__ __forceinline__ char *prb(int c) const { return smem + Lay::offPrep + (c & 1) * Lay::prepBytes; }
     __device__ __forceinline__ char *ks() const { return smem + Lay::offK; }
@@ -423,7 +435,7 @@ struct PrepCtx {
 };
 
 // A chunk's output rows, staged transposed in LDS by the scan waves, to HBM
-// (Q wave).  Each 16-lane group turns a 16-row x 8-column block back into
+// (K wave).  Each 16-lane group turns a 16-row x 8-column block back into
 // rows with two transposing reads and writes 16 bytes per row; rows past the
 // chunk's valid ones fall outside the buffer resource and are dropped.
 template <int DK, int DV, int C, int NS>
@@ -447,7 +459,7 @@ __device__ __attribute__((always_inline)) inline void prep_store_out(const PrepC
 }
 
 // One prep interval: start the loads of chunk n + 1 (into `dma`), write the
-// output of chunk out_chunk (Q wave, if >= 0; staged in `os`) and prepare
+// output of chunk out_chunk (K wave, if >= 0; staged in `os`) and prepare
 // chunk n (if < nchunks) from its inputs in `in` into `pr`; then wait for
 // this wave's loads, so that they are complete once the interval's closing
 // barrier has been passed.  The buffers are distinct, and saying so
@@ -460,20 +472,18 @@ __device__ __attribute__((always_inline)) inline void prep_interval(
 {
     if (n + 1 < x.nchunks) {
         const long off = (long)(n + 1) * C;
-        dma_chunk<DK, DV, C, NS>(x.kwave, dma, x.qb + off * DK, x.kb + off * DK, x.vb + off * DV,
+        dma_chunk<DK, DV, C, NS>(x.role, dma, x.qb + off * DK, x.kb + off * DK, x.vb + off * DV,
                                  x.bb + off, x.valid_of(n + 1));
     }
-    if (n < x.nchunks) {
-        if (x.kwave) {
-            prep_gram<DK, DV, C, NS>(in, pr, ks);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            prep_diag<DK, DV, C, NS>(in, pr, ks);
-        } else {
-            if (out_chunk >= 0) prep_store_out(x, out_chunk, os);
-            prep_qk<DK, DV, C, NS>(in, pr);
-        }
-    } else if (!x.kwave && out_chunk >= 0) {
-        prep_store_out(x, out_chunk, os);
+    if (x.role == K_WAVE) {
+        if (out_chunk >= 0) prep_store_out(x, out_chunk, os);
+        if (n < x.nchunks) prep_gram<DK, DV, C, NS, false>(in, pr, ks);
+    } else if (x.role == Q_WAVE) {
+        if (n < x.nchunks) prep_qk<DK, DV, C, NS>(in, pr);
+    } else if (n < x.nchunks) {
+        prep_gram<DK, DV, C, NS, true>(in, pr, ks);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        prep_diag<DK, DV, C, NS>(in, pr, ks);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -620,9 +630,9 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
 }
 
 template <int DK, int DV, int C, int NS>
-// One workgroup per CU by design (its LDS footprint), one wave per SIMD:
-// let the register allocator use the whole register file for latency hiding.
-__global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(1, 1))) void fused_kernel(
+// One workgroup per CU by design (its LDS footprint); its NS + 3 waves put at
+// most two on a SIMD, so each may use half the register file.
+__global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_kernel(
     const bf *__restrict__ q, const bf *__restrict__ k, const bf *__restrict__ v,
     const float *__restrict__ beta, const float *__restrict__ S0, bf *__restrict__ o,
     float *__restrict__ SL, int L, int nchunks)
@@ -669,8 +679,8 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
         // ------------------------------------------------------------ prep waves
         const PrepCtx<DK, DV, C, NS> x{smem, q + tokb * DK, k + tokb * DK, v + tokb * DV + tile * TV,
                                        beta + tokb, o + tokb * DV + tile * TV, L, nchunks, lane,
-                                       wv == NS};
-        dma_chunk<DK, DV, C, NS>(x.kwave, x.inb(0), x.qb, x.kb, x.vb, x.bb, x.valid_of(0));
+                                       wv - NS};
+        dma_chunk<DK, DV, C, NS>(x.role, x.inb(0), x.qb, x.kb, x.vb, x.bb, x.valid_of(0));
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();                // prologue: chunk 0 loaded
         prep_step(x, 0, -1);            // prologue: chunk 1 loading, chunk 0 prepared
@@ -682,7 +692,7 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
             __syncthreads();
         }
         __syncthreads();
-        if (!x.kwave) prep_store_out(x, nchunks - 1, x.obuf((nchunks - 1) & 1));
+        if (x.role == K_WAVE) prep_store_out(x, nchunks - 1, x.obuf((nchunks - 1) & 1));
     }
 }
 
