@@ -644,7 +644,11 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
     int bh, tile;
     xcd_map(blockIdx.x, gridDim.x, NTILE, bh, tile);
     const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // wave slot -> role: the T wave takes slot 0 and the K wave the last slot,
+    // which share a SIMD (waves are placed on the four SIMDs round-robin), so
+    // the two scan waves keep a SIMD each
+    const int hw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wv = hw == 0 ? Lay::NW - 1 : hw <= NS ? hw - 1 : hw == Lay::NW - 1 ? NS : NS + 1;
     const long tokb = (long)bh * L;
 
     if (wv < NS) {
