@@ -14,6 +14,9 @@ Dynamics", gist.science Technical Summary):
   * Readout o_t = S_t^T q_t (post-update state) and the lambda -> 0 limit
     alpha = beta are the readings stated with the operator's problem statement;
     the pages do not print the readout.
+  * update="euler": the explicit Euler step of the same ODE over the interval
+    beta (alpha := beta), the delta rule the pages compare against (Problem
+    Statement).
 
 Entry points
   alpha(beta, lam)           per-token coefficient (numpy, fp64)
@@ -21,8 +24,10 @@ Entry points
   ut_transform(k, v, alpha, chunk)
                              per-chunk T, W = T K, U = T V by their definition
                              (a library triangular solve; see the function)
-  forward(q, k, v, beta, S0) whole-sequence recurrence (C, fp64, OpenMP)
-  decode(q, k, v, beta, S)   one single-token step (C, fp64, OpenMP)
+  forward(q, k, v, beta, S0, update="exact")
+                             whole-sequence recurrence (C, fp64, OpenMP)
+  decode(q, k, v, beta, S, update="exact")
+                             one single-token step (C, fp64, OpenMP)
 
 Parity of ``forward``/``decode``/``alpha`` is pinned by tests/test_oracle_pins.py
 against matrix exponentials, the exact ODE flow and invariants.  The chunk
@@ -51,9 +56,9 @@ def _lib():
         lib.efla_oracle_alpha.restype = ctypes.c_double
         lib.efla_oracle_alpha.argtypes = [ctypes.c_double, ctypes.c_double]
         lib.efla_oracle_forward.restype = ctypes.c_int
-        lib.efla_oracle_forward.argtypes = [_DP] * 7 + [ctypes.c_long] * 5 + [ctypes.c_int]
+        lib.efla_oracle_forward.argtypes = [_DP] * 7 + [ctypes.c_long] * 5 + [ctypes.c_int] * 2
         lib.efla_oracle_decode.restype = ctypes.c_int
-        lib.efla_oracle_decode.argtypes = [_DP] * 6 + [ctypes.c_long] * 4 + [ctypes.c_int]
+        lib.efla_oracle_decode.argtypes = [_DP] * 6 + [ctypes.c_long] * 4 + [ctypes.c_int] * 2
         lib.efla_oracle_max_threads.restype = ctypes.c_int
         lib.efla_oracle_max_threads.argtypes = []
         _LIB = lib
@@ -141,10 +146,17 @@ def ut_transform(k, v, alph, chunk: int):
     return T, W, U
 
 
-def forward(q, k, v, beta, S0=None, threads: int = 0):
+def _euler(update: str) -> int:
+    if update not in ("exact", "euler"):
+        raise ValueError(f"unknown update {update!r}")
+    return int(update == "euler")
+
+
+def forward(q, k, v, beta, S0=None, threads: int = 0, update: str = "exact"):
     """Token-by-token recurrence in fp64.  Returns (o [B,H,L,dv], S_L [B,H,dk,dv]).
 
     q, k: [B,H,L,dk]; v: [B,H,L,dv]; beta: [B,H,L]; S0: [B,H,dk,dv] or None.
+    update: "exact" (alpha from the exact flow) or "euler" (alpha = beta).
     """
     q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
     B, H, L, dk = k.shape
@@ -160,13 +172,13 @@ def forward(q, k, v, beta, S0=None, threads: int = 0):
     S_L = np.empty((B, H, dk, dv))
     rc = _lib().efla_oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                     None if s0 is None else _ptr(s0), _ptr(o), _ptr(S_L),
-                                    B, H, L, dk, dv, int(threads))
+                                    B, H, L, dk, dv, _euler(update), int(threads))
     if rc != 0:
         raise RuntimeError("oracle forward failed")
     return o, S_L
 
 
-def decode(q, k, v, beta, S, threads: int = 0):
+def decode(q, k, v, beta, S, threads: int = 0, update: str = "exact"):
     """One decode step.  Returns (o [N,H,dv], S_new [N,H,dk,dv]); S is not modified."""
     q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
     S = _f64(S).copy()
@@ -177,7 +189,7 @@ def decode(q, k, v, beta, S, threads: int = 0):
         raise ValueError("shape mismatch")
     o = np.empty((N, H, dv))
     rc = _lib().efla_oracle_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(o),
-                                   N, H, dk, dv, int(threads))
+                                   N, H, dk, dv, _euler(update), int(threads))
     if rc != 0:
         raise RuntimeError("oracle decode failed")
     return o, S

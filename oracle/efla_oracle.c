@@ -18,6 +18,12 @@
  * also what the exponential collapses to when k_t = 0 (then kk^T = 0 and
  * the update is the identity whatever alpha is).
  *
+ * With `euler` set, every function evaluates instead the explicit Euler step
+ * of the same ODE over the interval beta, S + beta (-k k^T S + k v^T), i.e.
+ * the same update with alpha_t = beta_t: the delta rule the pages compare the
+ * exact flow against (Problem Statement; Methodology 3 calls the exact
+ * update its continuous-time counterpart).
+ *
  * The recurrence is evaluated token by token in fp64, one independent
  * (batch, head) sequence per OpenMP iteration.  (I - a k k^T) S is formed as
  * S - a k (k^T S): the same product, without materialising the d_k x d_k
@@ -41,13 +47,14 @@ double efla_oracle_alpha(double beta, double lambda)
     return -expm1(-beta * lambda) / lambda;
 }
 
-/* One token: S <- (I - a k k^T) S + a k v^T, in place.  kS is dv scratch. */
+/* One token: S <- (I - a k k^T) S + a k v^T, in place, a = alpha (or beta
+ * for the Euler step).  kS is dv scratch. */
 static void efla_oracle_token(double *S, const double *k, const double *v, double beta,
-                              long dk, long dv, double *kS)
+                              long dk, long dv, double *kS, int euler)
 {
     double lambda = 0.0;
     for (long i = 0; i < dk; ++i) lambda += k[i] * k[i];
-    const double a = efla_oracle_alpha(beta, lambda);
+    const double a = euler ? beta : efla_oracle_alpha(beta, lambda);
     for (long j = 0; j < dv; ++j) kS[j] = 0.0;
     for (long i = 0; i < dk; ++i)
         for (long j = 0; j < dv; ++j) kS[j] += k[i] * S[i * dv + j];
@@ -79,7 +86,7 @@ static int efla_oracle_threads(int nthreads)
  */
 int efla_oracle_forward(const double *q, const double *k, const double *v, const double *beta,
                         const double *S0, double *o, double *S_L,
-                        long B, long H, long L, long dk, long dv, int nthreads)
+                        long B, long H, long L, long dk, long dv, int euler, int nthreads)
 {
     if (B < 0 || H < 0 || L < 0 || dk <= 0 || dv <= 0) return -1;
     const long BH = B * H;
@@ -97,7 +104,7 @@ int efla_oracle_forward(const double *q, const double *k, const double *v, const
         else memset(S, 0, sizeof(double) * (size_t)(dk * dv));
         for (long t = 0; t < L; ++t) {
             const long tok = bh * L + t;
-            efla_oracle_token(S, k + tok * dk, v + tok * dv, beta[tok], dk, dv, kS);
+            efla_oracle_token(S, k + tok * dk, v + tok * dv, beta[tok], dk, dv, kS, euler);
             efla_oracle_readout(S, q + tok * dk, o + tok * dv, dk, dv);
         }
         free(kS);
@@ -110,7 +117,8 @@ int efla_oracle_forward(const double *q, const double *k, const double *v, const
  * place and o [N,H,dv] = S_new^T q.  q, k [N,H,dk], v [N,H,dv], beta [N,H].
  */
 int efla_oracle_decode(const double *q, const double *k, const double *v, const double *beta,
-                       double *S, double *o, long N, long H, long dk, long dv, int nthreads)
+                       double *S, double *o, long N, long H, long dk, long dv, int euler,
+                       int nthreads)
 {
     if (N < 0 || H < 0 || dk <= 0 || dv <= 0) return -1;
     const long NH = N * H;
@@ -124,7 +132,7 @@ int efla_oracle_decode(const double *q, const double *k, const double *v, const 
             continue;
         }
         double *Sh = S + nh * dk * dv;
-        efla_oracle_token(Sh, k + nh * dk, v + nh * dv, beta[nh], dk, dv, kS);
+        efla_oracle_token(Sh, k + nh * dk, v + nh * dv, beta[nh], dk, dv, kS, euler);
         efla_oracle_readout(Sh, q + nh * dk, o + nh * dv, dk, dv);
         free(kS);
     }

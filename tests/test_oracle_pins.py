@@ -451,6 +451,90 @@ def test_p14_split_and_resume(t0):
     np.testing.assert_allclose(Sb, SL, rtol=0, atol=1e-13)
 
 
+# --- PE: the Euler (delta rule) variant, update="euler" (Problem Statement) -
+
+def _dense_euler(q, k, v, beta, S0):
+    """Explicit Euler step of dS/dt = -k k^T S + k v^T over [0, beta], with
+    dense matrices, token by token; readout after the update."""
+    B, H, L, dk = k.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, H, L, dv))
+    SL = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            S = np.array(S0[b, h], dtype=np.float64)
+            for t in range(L):
+                kt, bt = k[b, h, t], beta[b, h, t]
+                S = S + bt * (-np.outer(kt, kt) @ S + np.outer(kt, v[b, h, t]))
+                o[b, h, t] = S.T @ q[b, h, t]
+            SL[b, h] = S
+    return o, SL
+
+
+@pytest.mark.parametrize("dk,dv", [(4, 4), (8, 3)])
+def test_pe_euler_is_the_explicit_euler_step(dk, dv):
+    rng = np.random.default_rng(100 + dk)
+    B, H, L = 2, 2, 13
+    q = rng.standard_normal((B, H, L, dk))
+    k = rng.standard_normal((B, H, L, dk)) * 0.5
+    v = rng.standard_normal((B, H, L, dv))
+    beta = rng.uniform(0, 1, (B, H, L))
+    S0 = rng.standard_normal((B, H, dk, dv))
+    o, SL = oracle.forward(q, k, v, beta, S0, update="euler")
+    od, SLd = _dense_euler(q, k, v, beta, S0)
+    np.testing.assert_allclose(o, od, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(SL, SLd, rtol=0, atol=1e-12)
+    # one decode step is the same update
+    od1, Sd1 = oracle.decode(q[:, :, 0], k[:, :, 0], v[:, :, 0], beta[:, :, 0], S0, update="euler")
+    o1, S1 = oracle.forward(q[:, :, :1], k[:, :, :1], v[:, :, :1], beta[:, :, :1], S0, update="euler")
+    np.testing.assert_allclose(od1, o1[:, :, 0], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(Sd1, S1, rtol=0, atol=1e-14)
+
+
+def test_pe_euler_and_exact_agree_to_second_order_in_beta():
+    """Over a whole sequence the two updates differ by O(beta^2) per token."""
+    rng = np.random.default_rng(101)
+    B, H, L, dk, dv = 1, 2, 9, 5, 4
+    q = rng.standard_normal((B, H, L, dk))
+    k = rng.standard_normal((B, H, L, dk))
+    v = rng.standard_normal((B, H, L, dv))
+    base = rng.uniform(0.5, 1.0, (B, H, L))
+    gaps = []
+    for scale in (1e-2, 1e-3):
+        oe, _ = oracle.forward(q, k, v, base * scale, None, update="exact")
+        ou, _ = oracle.forward(q, k, v, base * scale, None, update="euler")
+        gaps.append(np.max(np.abs(oe - ou)))
+    assert 70 < gaps[0] / gaps[1] < 130
+
+
+@pytest.mark.parametrize("beta_lam", [0.5, 3.0, 40.0])
+def test_pe_euler_is_unstable_where_the_exact_flow_contracts(beta_lam):
+    """Along k the Euler update multiplies the distance k^T S - v^T to its
+    fixed point by 1 - beta lambda (below -1 once beta lambda > 2: it grows)
+    where the exact flow multiplies it by e^{-beta lambda} (Key
+    Contributions: contraction along the key direction)."""
+    rng = np.random.default_rng(102)
+    dk, dv = 6, 3
+    k = _rand_key(rng, dk, 1.5)
+    lam = float(k @ k)
+    beta = beta_lam / lam
+    v = rng.standard_normal(dv)
+    S = rng.standard_normal((dk, dv))
+    L = 6
+    kk = np.broadcast_to(k, (1, 1, L, dk)).copy()
+    vv = np.broadcast_to(v, (1, 1, L, dv)).copy()
+    bb = np.full((1, 1, L), beta)
+    qq = np.zeros((1, 1, L, dk))
+    for update, factor in (("euler", 1.0 - beta_lam), ("exact", np.exp(-beta_lam))):
+        _, SL = oracle.forward(qq, kk, vv, bb, S[None, None], update=update)
+        # k^T S_t - v^T = factor^L (k^T S_0 - v^T)  (fixed point k^T S = v^T)
+        got = k @ SL[0, 0] - v
+        want = factor ** L * (k @ S - v)
+        np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+    if beta_lam > 2:
+        assert abs(1.0 - beta_lam) ** L > 1.0 > np.exp(-beta_lam)
+
+
 # --- oracle mechanics ---------------------------------------------------------
 
 def test_thread_count_invariance():
