@@ -155,14 +155,15 @@ def bench_forward(args, w, dev):
         srcs = {"coef": "coef_decode.hip", "ut": "ut_transform.hip", "scan": "chunk_scan.hip"}
     else:
         need = _lib.efla_forward_workspace_size_ex(B, H, L, dk, dv, C, dt, pcode)
+        update = [_lib.EFLA_EXACT]
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         names = ["fused"]
 
         def step(ev, timer):
             p = lambda x: None if x is None else x.data_ptr()  # noqa: E731
             timer.record(ev[0])
-            st = _lib.efla_forward_ex(p(qd), p(kd), p(vd), p(bd), p(s0d), p(o), p(S_L), B, H, L,
-                                      dk, dv, C, dt, p(ws), need, pcode, sp)
+            st = _lib.efla_forward_update(p(qd), p(kd), p(vd), p(bd), p(s0d), p(o), p(S_L), B,
+                                          H, L, dk, dv, C, dt, p(ws), need, pcode, update[0], sp)
             timer.record(ev[1])
             if st:
                 raise RuntimeError(f"fused forward failed: {_lib.status_string(st)}")
@@ -182,6 +183,28 @@ def bench_forward(args, w, dev):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     timer.collect(pending)
+
+    # The same kernel with the explicit Euler step (alpha = beta, the delta
+    # rule the exact flow is compared against), timed the same way.
+    compare = None
+    if path == "fused":
+        update[0] = _lib.EFLA_EULER
+        t2 = Timer(stream, names)
+        for _ in range(args.warmup):
+            step(t2.marks(), t2)
+        torch.cuda.synchronize()
+        pend2 = []
+        for _ in range(args.steps):
+            ev = t2.marks()
+            step(ev, t2)
+            pend2.append(ev)
+        torch.cuda.synchronize()
+        t2.collect(pend2)
+        update[0] = _lib.EFLA_EXACT
+        ex_ms, eu_ms = timer.mean("fused"), t2.mean("fused")
+        compare = {"exact_kernel_ms": ex_ms, "euler_kernel_ms": eu_ms,
+                   "exact_over_euler_time": ex_ms / eu_ms,
+                   "note": "same fused kernel, alpha from the exact flow vs alpha = beta"}
 
     ms_step = elapsed * 1e3 / args.steps
     tokens = B * L
@@ -226,6 +249,8 @@ def bench_forward(args, w, dev):
         "kernel_ms": per_kernel,
         "roofline": roof,
     }
+    if compare is not None:
+        res["update_compare"] = compare
     return res, host
 
 

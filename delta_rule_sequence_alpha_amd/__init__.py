@@ -4,9 +4,11 @@ Torch-facing wrappers around the C ABI of libefla.so (include/efla.h).  torch
 supplies device memory and the current stream; every step of the operator
 runs in the library's HIP kernels.
 
-  forward(q, k, v, beta, S0=None, chunk=64, path="auto") -> (o, S_L)
-  decode_step(q, k, v, beta, S) -> o          (S updated in place)
-  coefficients(k, beta) -> (alpha, lambda)    stage 1 of the staged path
+  forward(q, k, v, beta, S0=None, chunk=64, path="auto", update="exact") -> (o, S_L)
+  decode_step(q, k, v, beta, S, update="exact") -> o     (S updated in place)
+  coefficients(k, beta, update="exact") -> (alpha, lambda)   stage 1 of the staged path
+update="euler" evaluates the explicit Euler step of the same ODE instead
+(alpha = beta, the delta rule) on the same kernels.
   ut_transform(q, k, v, alpha, chunk) -> (W, U, A)   stage 2
   chunk_scan(q, k, W, U, A, S0, chunk) -> (o, S_L)   stage 3
 """
@@ -15,13 +17,14 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import (EFLA_BF16, EFLA_F32, EFLA_PATH_AUTO, EFLA_PATH_FUSED, EFLA_PATH_STAGED,
-                   EflaError, LIB_PATH)
+from ._lib import (EFLA_BF16, EFLA_EULER, EFLA_EXACT, EFLA_F32, EFLA_PATH_AUTO, EFLA_PATH_FUSED,
+                   EFLA_PATH_STAGED, EflaError, LIB_PATH)
 
 __all__ = ["forward", "decode_step", "coefficients", "ut_transform", "chunk_scan",
            "workspace_size", "EflaError", "LIB_PATH"]
 
 _PATHS = {"auto": EFLA_PATH_AUTO, "staged": EFLA_PATH_STAGED, "fused": EFLA_PATH_FUSED}
+_UPDATES = {"exact": EFLA_EXACT, "euler": EFLA_EULER}
 
 
 def _dt(x: torch.Tensor) -> int:
@@ -64,7 +67,7 @@ def workspace_size(B, H, L, d_k, d_v, chunk, dtype, path="auto") -> int:
 
 
 def forward(q, k, v, beta, S0=None, chunk: int = 64, path: str = "auto", workspace=None,
-            out=None, S_L=None):
+            out=None, S_L=None, update: str = "exact"):
     """Chunked EFLA forward.  q, k: [B,H,L,d_k]; v: [B,H,L,d_v]; beta: [B,H,L] fp32.
 
     Returns (o [B,H,L,d_v] in q's dtype, S_L [B,H,d_k,d_v] fp32).  ``workspace``
@@ -89,14 +92,14 @@ def forward(q, k, v, beta, S0=None, chunk: int = 64, path: str = "auto", workspa
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _lib.efla_forward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(out),
-                              _ptr(S_L), B, H, L, dk, dv, chunk, dt, _ptr(workspace), ws_bytes, p,
-                              _stream(dev))
-    _raise(st, "efla_forward_ex")
+    st = _lib.efla_forward_update(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(out),
+                                  _ptr(S_L), B, H, L, dk, dv, chunk, dt, _ptr(workspace), ws_bytes,
+                                  p, _UPDATES[update], _stream(dev))
+    _raise(st, "efla_forward_update")
     return out, S_L
 
 
-def decode_step(q, k, v, beta, S, out=None):
+def decode_step(q, k, v, beta, S, out=None, update: str = "exact"):
     """One decode step, S [N,H,d_k,d_v] fp32 updated in place.  Returns o [N,H,d_v]."""
     N, H, dk = k.shape
     dv = v.shape[-1]
@@ -108,13 +111,13 @@ def decode_step(q, k, v, beta, S, out=None):
     _check(S, "S", (N, H, dk, dv), torch.float32)
     if out is None:
         out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
-    st = _lib.efla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(out), N, H,
-                               dk, dv, dt, _stream(q.device))
-    _raise(st, "efla_decode_step")
+    st = _lib.efla_decode_step_update(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(out),
+                                      N, H, dk, dv, dt, _UPDATES[update], _stream(q.device))
+    _raise(st, "efla_decode_step_update")
     return out
 
 
-def coefficients(k, beta, with_lambda: bool = True):
+def coefficients(k, beta, with_lambda: bool = True, update: str = "exact"):
     """Stage 1: per-token (alpha, lambda) in fp32, shaped like beta."""
     dk = k.shape[-1]
     n = beta.numel()
@@ -122,9 +125,9 @@ def coefficients(k, beta, with_lambda: bool = True):
     _check(beta, "beta", tuple(beta.shape), torch.float32)
     alpha = torch.empty_like(beta)
     lam = torch.empty_like(beta) if with_lambda else None
-    st = _lib.efla_coefficients(_ptr(k), _ptr(beta), _ptr(alpha), _ptr(lam), n, dk, _dt(k),
-                                _stream(k.device))
-    _raise(st, "efla_coefficients")
+    st = _lib.efla_coefficients_update(_ptr(k), _ptr(beta), _ptr(alpha), _ptr(lam), n, dk, _dt(k),
+                                       _UPDATES[update], _stream(k.device))
+    _raise(st, "efla_coefficients_update")
     return alpha, lam
 
 

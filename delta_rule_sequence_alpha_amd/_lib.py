@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libefla.so")
 EFLA_F32, EFLA_BF16 = 0, 1
 EFLA_OK, EFLA_ERR_INVALID_ARG, EFLA_ERR_UNSUPPORTED, EFLA_ERR_WORKSPACE, EFLA_ERR_HIP = range(5)
 EFLA_PATH_AUTO, EFLA_PATH_STAGED, EFLA_PATH_FUSED = 0, 1, 2
+EFLA_EXACT, EFLA_EULER = 0, 1
 
 # (name, restype, argtypes) of every exported symbol, in header order.
 _P = ctypes.c_void_p
@@ -27,8 +28,11 @@ SIGNATURES = [
     ("efla_forward_workspace_size_ex", _S, [_I, _I, _I, _I, _I, _I, _I, _I]),
     ("efla_forward", _I, [_P] * 7 + [_I] * 7 + [_P, _S, _P]),
     ("efla_forward_ex", _I, [_P] * 7 + [_I] * 7 + [_P, _S, _I, _P]),
+    ("efla_forward_update", _I, [_P] * 7 + [_I] * 7 + [_P, _S, _I, _I, _P]),
     ("efla_decode_step", _I, [_P] * 6 + [_I] * 5 + [_P]),
+    ("efla_decode_step_update", _I, [_P] * 6 + [_I] * 6 + [_P]),
     ("efla_coefficients", _I, [_P] * 4 + [_L, _I, _I, _P]),
+    ("efla_coefficients_update", _I, [_P] * 4 + [_L, _I, _I, _I, _P]),
     ("efla_ut_transform", _I, [_P] * 7 + [_I] * 7 + [_P]),
     ("efla_chunk_scan", _I, [_P] * 8 + [_I] * 7 + [_P]),
 ]
@@ -90,12 +94,26 @@ def efla_forward_ex(q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt, ws, w
                  ws_bytes, path, stream)
 
 
+def efla_forward_update(q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt, ws, ws_bytes,
+                        path, update, stream) -> int:
+    return _call("efla_forward_update", q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt, ws,
+                 ws_bytes, path, update, stream)
+
+
 def efla_decode_step(q, k, v, beta, S, o, N, H, dk, dv, dt, stream) -> int:
     return _call("efla_decode_step", q, k, v, beta, S, o, N, H, dk, dv, dt, stream)
 
 
+def efla_decode_step_update(q, k, v, beta, S, o, N, H, dk, dv, dt, update, stream) -> int:
+    return _call("efla_decode_step_update", q, k, v, beta, S, o, N, H, dk, dv, dt, update, stream)
+
+
 def efla_coefficients(k, beta, alpha, lam, n_tokens, dk, dt, stream) -> int:
     return _call("efla_coefficients", k, beta, alpha, lam, n_tokens, dk, dt, stream)
+
+
+def efla_coefficients_update(k, beta, alpha, lam, n_tokens, dk, dt, update, stream) -> int:
+    return _call("efla_coefficients_update", k, beta, alpha, lam, n_tokens, dk, dt, update, stream)
 
 
 def efla_ut_transform(q, k, v, alpha, w, u, a_qk, B, H, L, dk, dv, chunk, dt, stream) -> int:

@@ -5,6 +5,8 @@
 //   lambda_t = |k_t|^2,  alpha_t = (1 - e^{-beta_t lambda_t}) / lambda_t.
 // Decode step: the same update applied to one token,
 //   S <- S + alpha k r^T with r = v - S^T k,  o = S_new^T q = S^T q + alpha (k.q) r.
+// Both kernels take `euler`: alpha = beta, the explicit Euler step of the
+// same ODE (the delta rule), for comparison with the exact flow.
 #include "efla_device.h"
 #include "efla_launch.h"
 
@@ -17,7 +19,8 @@ template <typename T, int DK>
 __global__ __launch_bounds__(256) void coef_kernel(const T *__restrict__ k,
                                                    const float *__restrict__ beta,
                                                    float *__restrict__ alpha,
-                                                   float *__restrict__ lambda, long n_tokens)
+                                                   float *__restrict__ lambda, long n_tokens,
+                                                   int euler)
 {
     constexpr int V = 16 / sizeof(T);
     constexpr int LPT = DK / V;                 // lanes per token (<= 64)
@@ -37,21 +40,21 @@ __global__ __launch_bounds__(256) void coef_kernel(const T *__restrict__ k,
 #pragma unroll
     for (int off = LPT / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (tok < n_tokens && sub == 0) {
-        alpha[tok] = efla_alpha(beta[tok], acc);
+        alpha[tok] = update_alpha(euler, beta[tok], acc);
         if (lambda) lambda[tok] = acc;
     }
 }
 
 template <typename T, int DK>
 hipError_t launch_coef(const void *k, const float *beta, float *alpha, float *lambda,
-                       long n_tokens, hipStream_t st)
+                       long n_tokens, bool euler, hipStream_t st)
 {
     constexpr int LPT = DK / (16 / sizeof(T));
     constexpr int TPB = 256 / LPT;
     if (n_tokens == 0) return hipSuccess;
     const long blocks = (n_tokens + TPB - 1) / TPB;
     hipLaunchKernelGGL((coef_kernel<T, DK>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       static_cast<const T *>(k), beta, alpha, lambda, n_tokens);
+                       static_cast<const T *>(k), beta, alpha, lambda, n_tokens, (int)euler);
     return hipGetLastError();
 }
 
@@ -70,7 +73,7 @@ struct DecodeShape {
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const float *__restrict__ beta, float *__restrict__ S, T *__restrict__ o)
+    const float *__restrict__ beta, float *__restrict__ S, T *__restrict__ o, int euler)
 {
     using Sh = DecodeShape<DK, DV>;
     constexpr int NT = Sh::NT, CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT;
@@ -106,7 +109,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
             kq += __shfl_xor(kq, off, 64);
         }
         if (tid == 0) {
-            s_alpha = efla_alpha(beta[nh], lam);
+            s_alpha = update_alpha(euler, beta[nh], lam);
             s_kq = kq;
         }
     }
@@ -155,13 +158,13 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
 
 template <typename T, int DK, int DV>
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *beta, float *S,
-                         void *o, long NH, hipStream_t st)
+                         void *o, long NH, bool euler, hipStream_t st)
 {
     if (NH == 0) return hipSuccess;
     hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3((unsigned)NH),
                        dim3(DecodeShape<DK, DV>::NT), 0, st, static_cast<const T *>(q),
                        static_cast<const T *>(k), static_cast<const T *>(v), beta, S,
-                       static_cast<T *>(o));
+                       static_cast<T *>(o), (int)euler);
     return hipGetLastError();
 }
 
@@ -186,24 +189,25 @@ hipError_t launch_copy_state(const float *src, float *dst, long n, hipStream_t s
 #define EFLA_D_CASES(X) X(16) X(32) X(64) X(128)
 
 hipError_t dispatch_coef(bool bf16, int dk, const void *k, const float *beta, float *alpha,
-                         float *lambda, long n, hipStream_t st)
+                         float *lambda, long n, bool euler, hipStream_t st)
 {
 #define CASE(D)                                                                              \
     if (dk == D)                                                                             \
-        return bf16 ? launch_coef<__bf16, D>(k, beta, alpha, lambda, n, st)                  \
-                    : launch_coef<float, D>(k, beta, alpha, lambda, n, st);
+        return bf16 ? launch_coef<__bf16, D>(k, beta, alpha, lambda, n, euler, st)           \
+                    : launch_coef<float, D>(k, beta, alpha, lambda, n, euler, st);
     EFLA_D_CASES(CASE)
 #undef CASE
     return hipErrorInvalidValue;
 }
 
 hipError_t dispatch_decode(bool bf16, int dk, int dv, const void *q, const void *k, const void *v,
-                           const float *beta, float *S, void *o, long NH, hipStream_t st)
+                           const float *beta, float *S, void *o, long NH, bool euler,
+                           hipStream_t st)
 {
 #define CASE2(DKV, DVV)                                                                      \
     if (dk == DKV && dv == DVV)                                                              \
-        return bf16 ? launch_decode<__bf16, DKV, DVV>(q, k, v, beta, S, o, NH, st)           \
-                    : launch_decode<float, DKV, DVV>(q, k, v, beta, S, o, NH, st);
+        return bf16 ? launch_decode<__bf16, DKV, DVV>(q, k, v, beta, S, o, NH, euler, st)    \
+                    : launch_decode<float, DKV, DVV>(q, k, v, beta, S, o, NH, euler, st);
 #define CASE(D) CASE2(D, 16) CASE2(D, 32) CASE2(D, 64) CASE2(D, 128)
     EFLA_D_CASES(CASE)
 #undef CASE

@@ -97,13 +97,16 @@ size_t efla_forward_workspace_size(int B, int H, int L, int dk, int dv, int chun
     return efla_forward_workspace_size_ex(B, H, L, dk, dv, chunk, dt, EFLA_PATH_AUTO);
 }
 
-efla_status_t efla_forward_ex(const void *q, const void *k, const void *v, const float *beta,
-                              const float *S0, void *o, float *S_L, int B, int H, int L, int dk,
-                              int dv, int chunk, efla_dtype_t dt, void *workspace,
-                              size_t workspace_bytes, efla_path_t path, void *stream)
+efla_status_t efla_forward_update(const void *q, const void *k, const void *v, const float *beta,
+                                  const float *S0, void *o, float *S_L, int B, int H, int L,
+                                  int dk, int dv, int chunk, efla_dtype_t dt, void *workspace,
+                                  size_t workspace_bytes, efla_path_t path, efla_update_t update,
+                                  void *stream)
 {
     efla_status_t s = check_shape(B, H, L, dk, dv, chunk, dt);
     if (s != EFLA_OK) return s;
+    if (update != EFLA_EXACT && update != EFLA_EULER) return EFLA_ERR_INVALID_ARG;
+    const bool euler = update == EFLA_EULER;
     if (path != EFLA_PATH_AUTO && path != EFLA_PATH_STAGED && path != EFLA_PATH_FUSED)
         return EFLA_ERR_INVALID_ARG;
     path = resolve_path(path, dt, dk, dv, chunk);
@@ -121,7 +124,7 @@ efla_status_t efla_forward_ex(const void *q, const void *k, const void *v, const
         if (L == 0) return hip_status(efla::launch_copy_state(S0, S_L, BH * dk * dv, st));
         return hip_status(efla::dispatch_fused(dt == EFLA_BF16, dk, dv, chunk, q, k, v, beta, S0,
                                                o, S_L, (int)BH, L,
-                                               waves_override("EFLA_FUSED_WAVES"), st));
+                                               waves_override("EFLA_FUSED_WAVES"), euler, st));
     }
     const StagedWs ws = staged_ws(B, H, L, dk, dv, chunk, dt);
     if (L > 0) {
@@ -135,13 +138,22 @@ efla_status_t efla_forward_ex(const void *q, const void *k, const void *v, const
     char *base = static_cast<char *>(workspace);
     float *alpha = reinterpret_cast<float *>(base + ws.alpha);
     void *w = base + ws.w, *u = base + ws.u, *aqk = base + ws.aqk;
-    hipError_t e = efla::dispatch_coef(bf, dk, k, beta, alpha, nullptr, BH * L, st);
+    hipError_t e = efla::dispatch_coef(bf, dk, k, beta, alpha, nullptr, BH * L, euler, st);
     if (e == hipSuccess)
         e = efla::dispatch_ut(bf, dk, dv, chunk, q, k, v, alpha, w, u, aqk, (int)BH, L, st);
     if (e == hipSuccess)
         e = efla::dispatch_scan(bf, dk, dv, chunk, q, k, w, u, aqk, S0, o, S_L, (int)BH, L,
                                 scan_waves_override(), st);
     return hip_status(e);
+}
+
+efla_status_t efla_forward_ex(const void *q, const void *k, const void *v, const float *beta,
+                              const float *S0, void *o, float *S_L, int B, int H, int L, int dk,
+                              int dv, int chunk, efla_dtype_t dt, void *workspace,
+                              size_t workspace_bytes, efla_path_t path, void *stream)
+{
+    return efla_forward_update(q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt, workspace,
+                               workspace_bytes, path, EFLA_EXACT, stream);
 }
 
 efla_status_t efla_forward(const void *q, const void *k, const void *v, const float *beta,
@@ -153,11 +165,12 @@ efla_status_t efla_forward(const void *q, const void *k, const void *v, const fl
                            workspace_bytes, EFLA_PATH_AUTO, stream);
 }
 
-efla_status_t efla_decode_step(const void *q, const void *k, const void *v, const float *beta,
-                               float *S, void *o, int N, int H, int dk, int dv, efla_dtype_t dt,
-                               void *stream)
+efla_status_t efla_decode_step_update(const void *q, const void *k, const void *v,
+                                      const float *beta, float *S, void *o, int N, int H, int dk,
+                                      int dv, efla_dtype_t dt, efla_update_t update, void *stream)
 {
     if (dt != EFLA_F32 && dt != EFLA_BF16) return EFLA_ERR_INVALID_ARG;
+    if (update != EFLA_EXACT && update != EFLA_EULER) return EFLA_ERR_INVALID_ARG;
     if (N < 0 || H < 0 || dk <= 0 || dv <= 0) return EFLA_ERR_INVALID_ARG;
     if (!dim_ok(dk) || !dim_ok(dv)) return EFLA_ERR_UNSUPPORTED;
     const long long NH = (long long)N * H;
@@ -168,20 +181,35 @@ efla_status_t efla_decode_step(const void *q, const void *k, const void *v, cons
         !aligned16(o))
         return EFLA_ERR_INVALID_ARG;
     return hip_status(efla::dispatch_decode(dt == EFLA_BF16, dk, dv, q, k, v, beta, S, o, NH,
-                                            static_cast<hipStream_t>(stream)));
+                                            update == EFLA_EULER, static_cast<hipStream_t>(stream)));
 }
 
-efla_status_t efla_coefficients(const void *k, const float *beta, float *alpha, float *lambda,
-                                long n_tokens, int dk, efla_dtype_t dt, void *stream)
+efla_status_t efla_decode_step(const void *q, const void *k, const void *v, const float *beta,
+                               float *S, void *o, int N, int H, int dk, int dv, efla_dtype_t dt,
+                               void *stream)
+{
+    return efla_decode_step_update(q, k, v, beta, S, o, N, H, dk, dv, dt, EFLA_EXACT, stream);
+}
+
+efla_status_t efla_coefficients_update(const void *k, const float *beta, float *alpha,
+                                       float *lambda, long n_tokens, int dk, efla_dtype_t dt,
+                                       efla_update_t update, void *stream)
 {
     if (dt != EFLA_F32 && dt != EFLA_BF16) return EFLA_ERR_INVALID_ARG;
+    if (update != EFLA_EXACT && update != EFLA_EULER) return EFLA_ERR_INVALID_ARG;
     if (n_tokens < 0 || dk <= 0) return EFLA_ERR_INVALID_ARG;
     if (!dim_ok(dk)) return EFLA_ERR_UNSUPPORTED;
     if (n_tokens == 0) return EFLA_OK;
     if ((n_tokens + 255) / 256 > INT32_MAX) return EFLA_ERR_UNSUPPORTED;
     if (!k || !beta || !alpha || !aligned16(k)) return EFLA_ERR_INVALID_ARG;
     return hip_status(efla::dispatch_coef(dt == EFLA_BF16, dk, k, beta, alpha, lambda, n_tokens,
-                                          static_cast<hipStream_t>(stream)));
+                                          update == EFLA_EULER, static_cast<hipStream_t>(stream)));
+}
+
+efla_status_t efla_coefficients(const void *k, const float *beta, float *alpha, float *lambda,
+                                long n_tokens, int dk, efla_dtype_t dt, void *stream)
+{
+    return efla_coefficients_update(k, beta, alpha, lambda, n_tokens, dk, dt, EFLA_EXACT, stream);
 }
 
 efla_status_t efla_ut_transform(const void *q, const void *k, const void *v, const float *alpha,

@@ -214,6 +214,14 @@ __device__ __forceinline__ float efla_alpha(float beta, float lambda)
     return beta * (-expm1f(-x) / x);
 }
 
+// alpha under the chosen update: the exact flow's, or beta itself for the
+// explicit Euler step of the same ODE (the delta rule the pages compare
+// against, Technical Summary, Problem Statement).
+__device__ __forceinline__ float update_alpha(int euler, float beta, float lambda)
+{
+    return euler ? beta : efla_alpha(beta, lambda);
+}
+
 // Workgroup -> (sequence, tile) map that keeps the NTILE tiles of one
 // sequence on one XCD.  Consecutive workgroup ids are dispatched round-robin
 // over the 8 XCDs, so ids x, x+8, x+16, ... share an XCD and its L2.

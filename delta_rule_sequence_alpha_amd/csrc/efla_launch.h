@@ -14,11 +14,13 @@
 
 namespace efla {
 
+// euler: alpha = beta (explicit Euler step) instead of the exact-flow alpha.
 hipError_t dispatch_coef(bool bf16, int dk, const void *k, const float *beta, float *alpha,
-                         float *lambda, long n, hipStream_t st);
+                         float *lambda, long n, bool euler, hipStream_t st);
 
 hipError_t dispatch_decode(bool bf16, int dk, int dv, const void *q, const void *k, const void *v,
-                           const float *beta, float *S, void *o, long NH, hipStream_t st);
+                           const float *beta, float *S, void *o, long NH, bool euler,
+                           hipStream_t st);
 
 hipError_t dispatch_ut(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                        const void *v, const float *alpha, void *w, void *u, void *aqk, int BH,
@@ -32,7 +34,7 @@ bool fused_supported(bool bf16, int dk, int dv, int chunk);
 
 hipError_t dispatch_fused(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                           const void *v, const float *beta, const float *S0, void *o, float *SL,
-                          int BH, int L, int nw, hipStream_t st);
+                          int BH, int L, int nw, bool euler, hipStream_t st);
 
 hipError_t launch_copy_state(const float *src, float *dst, long n, hipStream_t st);
 

@@ -366,7 +366,7 @@ __device__ __forceinline__ void prep_qk(const char *in, char *prep)
 // every later row, so each of the 16 steps carries independent FMAs.  T[i][j]
 // is written to its place in the A fragment of T_bb: lane 16(j/4) + i, slot j%4.
 template <int DK, int DV, int C, int NS>
-__device__ __forceinline__ void prep_diag(const char *in, char *prep, char *ks)
+__device__ __forceinline__ void prep_diag(const char *in, char *prep, char *ks, int euler)
 {
     using Lay = FusedLayout<DK, DV, C, NS>;
     constexpr int MC = Lay::MC;
@@ -375,7 +375,7 @@ __device__ __forceinline__ void prep_diag(const char *in, char *prep, char *ks)
     const float *sGt = reinterpret_cast<const float *>(ks + Lay::kGt);
     float *sAl = reinterpret_cast<float *>(ks + Lay::kAl);
     bf *sT = reinterpret_cast<bf *>(prep + Lay::pT);
-    if (lane < C) sAl[lane] = efla_alpha(sB[lane], sGt[lane * Lay::LDD + (lane & 15)]);
+    if (lane < C) sAl[lane] = update_alpha(euler, sB[lane], sGt[lane * Lay::LDD + (lane & 15)]);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int b = lane >> 4;
     if (b < MC) {
@@ -424,6 +424,7 @@ struct PrepCtx {
     bf *ob;
     int L, nchunks, lane;
     int role;
+    int euler;
     __device__ __forceinline__ char *inb(int c) const { return smem + Lay::offIn + (c % Lay::NB) * Lay::inBytes; }
     __device__ __forceinline__ char *prb(int c) const { return smem + Lay::offPrep + (c & 1) * Lay::prepBytes; }
     __device__ __forceinline__ char *ks() const { return smem + Lay::offK; }
@@ -483,7 +484,7 @@ __device__ __attribute__((always_inline)) inline void prep_interval(
     } else if (n < x.nchunks) {
         prep_gram<DK, DV, C, NS, true>(in, pr, ks);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        prep_diag<DK, DV, C, NS>(in, pr, ks);
+        prep_diag<DK, DV, C, NS>(in, pr, ks, x.euler);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -635,7 +636,7 @@ template <int DK, int DV, int C, int NS>
 __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_kernel(
     const bf *__restrict__ q, const bf *__restrict__ k, const bf *__restrict__ v,
     const float *__restrict__ beta, const float *__restrict__ S0, bf *__restrict__ o,
-    float *__restrict__ SL, int L, int nchunks)
+    float *__restrict__ SL, int L, int nchunks, int euler)
 {
     using Lay = FusedLayout<DK, DV, C, NS>;
     constexpr int TV = Lay::TV, NTILE = DV / TV, MK = DK / 16;
@@ -683,7 +684,7 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
         // ------------------------------------------------------------ prep waves
         const PrepCtx<DK, DV, C, NS> x{smem, q + tokb * DK, k + tokb * DK, v + tokb * DV + tile * TV,
                                        beta + tokb, o + tokb * DV + tile * TV, L, nchunks, lane,
-                                       wv - NS};
+                                       wv - NS, euler};
         dma_chunk<DK, DV, C, NS>(x.role, x.inb(0), x.qb, x.kb, x.vb, x.bb, x.valid_of(0));
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();                // prologue: chunk 0 loaded
@@ -702,7 +703,8 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
 
 template <int DK, int DV, int C, int NS>
 hipError_t launch_fused(const void *q, const void *k, const void *v, const float *beta,
-                        const float *S0, void *o, float *SL, int BH, int L, hipStream_t st)
+                        const float *S0, void *o, float *SL, int BH, int L, bool euler,
+                        hipStream_t st)
 {
     using Lay = FusedLayout<DK, DV, C, NS>;
     static_assert(Lay::bytes <= 160 * 1024, "fused kernel LDS budget");
@@ -716,18 +718,19 @@ hipError_t launch_fused(const void *q, const void *k, const void *v, const float
     hipLaunchKernelGGL((fused_kernel<DK, DV, C, NS>), dim3((unsigned)(BH * NTILE)),
                        dim3(64 * Lay::NW), Lay::bytes, st, static_cast<const bf *>(q),
                        static_cast<const bf *>(k), static_cast<const bf *>(v), beta, S0,
-                       static_cast<bf *>(o), SL, L, nchunks);
+                       static_cast<bf *>(o), SL, L, nchunks, (int)euler);
     return hipGetLastError();
 }
 
 template <int DK, int DV, int C>
 hipError_t launch_fused_ns(const void *q, const void *k, const void *v, const float *beta,
                            const float *S0, void *o, float *SL, int BH, int L, int ns,
-                           hipStream_t st)
+                           bool euler, hipStream_t st)
 {
     if (ns <= 0) ns = DV >= 32 ? 2 : 1;
-    if (ns >= 2 && DV >= 32) return launch_fused<DK, DV, C, 2>(q, k, v, beta, S0, o, SL, BH, L, st);
-    return launch_fused<DK, DV, C, 1>(q, k, v, beta, S0, o, SL, BH, L, st);
+    if (ns >= 2 && DV >= 32)
+        return launch_fused<DK, DV, C, 2>(q, k, v, beta, S0, o, SL, BH, L, euler, st);
+    return launch_fused<DK, DV, C, 1>(q, k, v, beta, S0, o, SL, BH, L, euler, st);
 }
 
 }  // namespace
@@ -742,12 +745,12 @@ bool fused_supported(bool bf16, int dk, int dv, int chunk)
 
 hipError_t dispatch_fused(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                           const void *v, const float *beta, const float *S0, void *o, float *SL,
-                          int BH, int L, int ns, hipStream_t st)
+                          int BH, int L, int ns, bool euler, hipStream_t st)
 {
     if (!bf16) return hipErrorInvalidValue;
 #define CASE(DKV, DVV, CC)                                                                      \
     if (dk == DKV && dv == DVV && chunk == CC)                                                  \
-        return launch_fused_ns<DKV, DVV, CC>(q, k, v, beta, S0, o, SL, BH, L, ns, st);
+        return launch_fused_ns<DKV, DVV, CC>(q, k, v, beta, S0, o, SL, BH, L, ns, euler, st);
     EFLA_SHAPE_CASES(CASE)
 #undef CASE
     return hipErrorInvalidValue;

@@ -60,6 +60,17 @@ typedef enum {
     EFLA_PATH_FUSED = 2    /* one kernel; no intermediate HBM traffic           */
 } efla_path_t;
 
+/* Coefficient of the update.
+ *  EFLA_EXACT: alpha = (1 - exp(-beta lambda)) / lambda, the exact flow
+ *              (Methodology 2-3); what efla_forward, efla_forward_ex,
+ *              efla_decode_step and efla_coefficients compute.
+ *  EFLA_EULER: alpha = beta, the explicit Euler step of the same ODE -- the
+ *              delta rule the pages compare the exact flow against (Problem
+ *              Statement).  Same kernels, layouts and rules; only alpha
+ *              differs.
+ * Any other value returns EFLA_ERR_INVALID_ARG. */
+typedef enum { EFLA_EXACT = 0, EFLA_EULER = 1 } efla_update_t;
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *efla_status_string(efla_status_t s);
 
@@ -96,6 +107,13 @@ efla_status_t efla_forward_ex(const void *q, const void *k, const void *v, const
                               void *workspace, size_t workspace_bytes, efla_path_t path,
                               void *stream);
 
+/* efla_forward_ex with an explicit update (EFLA_EXACT or EFLA_EULER). */
+efla_status_t efla_forward_update(const void *q, const void *k, const void *v, const float *beta,
+                                  const float *S0, void *o, float *S_L,
+                                  int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype_t dt,
+                                  void *workspace, size_t workspace_bytes, efla_path_t path,
+                                  efla_update_t update, void *stream);
+
 /*
  * Single-token decode step (the recurrent form of the same update) for N
  * sequences x H heads, in place:
@@ -108,6 +126,12 @@ efla_status_t efla_decode_step(const void *q, const void *k, const void *v, cons
                                float *S, void *o, int N, int H, int d_k, int d_v,
                                efla_dtype_t dt, void *stream);
 
+/* efla_decode_step with an explicit update (EFLA_EXACT or EFLA_EULER). */
+efla_status_t efla_decode_step_update(const void *q, const void *k, const void *v,
+                                      const float *beta, float *S, void *o, int N, int H,
+                                      int d_k, int d_v, efla_dtype_t dt, efla_update_t update,
+                                      void *stream);
+
 /*
  * Stage 1 of the staged path: per-token coefficients (Methodology 2-3).
  *   k [n_tokens, d_k] dtype dt; beta [n_tokens] fp32
@@ -118,6 +142,12 @@ efla_status_t efla_decode_step(const void *q, const void *k, const void *v, cons
  */
 efla_status_t efla_coefficients(const void *k, const float *beta, float *alpha, float *lambda,
                                 long n_tokens, int d_k, efla_dtype_t dt, void *stream);
+
+/* efla_coefficients with an explicit update: EFLA_EULER writes alpha = beta
+ * (lambda is still |k|^2). */
+efla_status_t efla_coefficients_update(const void *k, const float *beta, float *alpha,
+                                       float *lambda, long n_tokens, int d_k, efla_dtype_t dt,
+                                       efla_update_t update, void *stream);
 
 /*
  * Stage 2: per-chunk UT transform.  For every chunk of `chunk` consecutive

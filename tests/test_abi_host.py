@@ -32,7 +32,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 9
+    assert len(declared) == 12
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], check=True,
                          capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (efla_[a-z_]+)\b", out))
@@ -127,3 +127,22 @@ def test_stage_validation(lib):
                                 16, 0, None) == _lib.EFLA_ERR_INVALID_ARG
     assert _lib.efla_chunk_scan(FAKE, FAKE, FAKE, FAKE, MISALIGNED, None, FAKE, FAKE, 1, 1, 64, 16,
                                 16, 16, 0, None) == _lib.EFLA_ERR_INVALID_ARG
+
+
+def test_update_variant_validation(lib):
+    """The *_update entry points reject an unknown update before any HIP call,
+    and otherwise validate exactly like the exact-update entry points."""
+    def f(update, S_L=FAKE, dk=16):
+        return _lib.efla_forward_update(FAKE, FAKE, FAKE, FAKE, None, FAKE, S_L, 1, 2, 64, dk, 16,
+                                        16, _lib.EFLA_F32, FAKE, 1 << 30, 0, update, None)
+    assert f(2) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(_lib.EFLA_EULER, S_L=None) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(_lib.EFLA_EULER, dk=24) == _lib.EFLA_ERR_UNSUPPORTED
+    assert _lib.efla_decode_step_update(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 128, 0, -1,
+                                        None) == _lib.EFLA_ERR_INVALID_ARG
+    assert _lib.efla_decode_step_update(FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 2, 128, 128, 0,
+                                        _lib.EFLA_EULER, None) == _lib.EFLA_ERR_INVALID_ARG
+    assert _lib.efla_coefficients_update(FAKE, FAKE, FAKE, None, 10, 128, 0, 7,
+                                         None) == _lib.EFLA_ERR_INVALID_ARG
+    assert _lib.efla_coefficients_update(FAKE, FAKE, FAKE, None, 10, 24, 0, _lib.EFLA_EULER,
+                                         None) == _lib.EFLA_ERR_UNSUPPORTED
