@@ -9,7 +9,10 @@ JSON line.  The decode step (256 sequences x 16 heads, d=128, fp32 state) is
 timed in the same run and reported under "decode".
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload lm1.3b-bf16]
-                  [--path auto|staged|fused] [--no-cpu-baseline] [--no-decode]
+                  [--path auto|staged|fused] [--no-cpu-baseline] [--no-decode] [--no-compare]
+
+The fused path is also timed with the Euler update (alpha = beta) and both
+kernel times are reported under "update_compare".
 """
 from __future__ import annotations
 
@@ -159,49 +162,51 @@ def bench_forward(args, w, dev):
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         names = ["fused"]
 
-        def step(ev, timer):
+        def step(ev, timer):   # one kernel: timed over the whole region (ev, timer unused)
             p = lambda x: None if x is None else x.data_ptr()  # noqa: E731
-            timer.record(ev[0])
             st = _lib.efla_forward_update(p(qd), p(kd), p(vd), p(bd), p(s0d), p(o), p(S_L), B,
                                           H, L, dk, dv, C, dt, p(ws), need, pcode, update[0], sp)
-            timer.record(ev[1])
             if st:
                 raise RuntimeError(f"fused forward failed: {_lib.status_string(st)}")
         work = {"fused": fused_work(w, esz, S0 is not None)}
         srcs = {"fused": "fused_forward.hip"}
 
-    timer = Timer(stream, names)
-    for _ in range(args.warmup):
-        step(timer.marks(), timer)
-    torch.cuda.synchronize()
-    pending = []
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        ev = timer.marks()
-        step(ev, timer)
-        pending.append(ev)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    timer.collect(pending)
+    def timed(k_steps):
+        """Warmup, then k_steps steps between HIP events on the launch stream.
+        Returns (wall seconds, per-kernel mean ms).  The single fused kernel is
+        timed over the whole region (its mean launch duration); the staged
+        kernels each get an event pair per launch."""
+        timer = Timer(stream, names)
+        for _ in range(args.warmup):
+            step(timer.marks(), timer)
+        torch.cuda.synchronize()
+        pending = []
+        r0 = torch.cuda.Event(enable_timing=True)
+        r1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        r0.record(stream)
+        for _ in range(k_steps):
+            ev = timer.marks() if path == "staged" else None
+            step(ev, timer)
+            pending.append(ev)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        if path == "staged":
+            timer.collect(pending)
+            return wall, {n: timer.mean(n) for n in names}
+        return wall, {"fused": r0.elapsed_time(r1) / k_steps}
+
+    elapsed, per_kernel = timed(args.steps)
 
     # The same kernel with the explicit Euler step (alpha = beta, the delta
     # rule the exact flow is compared against), timed the same way.
     compare = None
-    if path == "fused":
+    if path == "fused" and not args.no_compare:
         update[0] = _lib.EFLA_EULER
-        t2 = Timer(stream, names)
-        for _ in range(args.warmup):
-            step(t2.marks(), t2)
-        torch.cuda.synchronize()
-        pend2 = []
-        for _ in range(args.steps):
-            ev = t2.marks()
-            step(ev, t2)
-            pend2.append(ev)
-        torch.cuda.synchronize()
-        t2.collect(pend2)
+        _, eu = timed(args.steps)
         update[0] = _lib.EFLA_EXACT
-        ex_ms, eu_ms = timer.mean("fused"), t2.mean("fused")
+        ex_ms, eu_ms = per_kernel["fused"], eu["fused"]
         compare = {"exact_kernel_ms": ex_ms, "euler_kernel_ms": eu_ms,
                    "exact_over_euler_time": ex_ms / eu_ms,
                    "note": "same fused kernel, alpha from the exact flow vs alpha = beta"}
@@ -210,7 +215,6 @@ def bench_forward(args, w, dev):
     tokens = B * L
     F = flops_per_token(dk, dv, C) * B * H * L
     peak = MFMA_PEAK[w.dtype]
-    per_kernel = {n: timer.mean(n) for n in names}
     dom = max(per_kernel, key=per_kernel.get)
     fl, by = work[dom]
     t_dom = per_kernel[dom] * 1e-3
@@ -397,6 +401,8 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "staged", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip timing the Euler variant of the fused kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (traffic counter calibration)")
     ap.add_argument("--pmc-summary", metavar="DIR",
