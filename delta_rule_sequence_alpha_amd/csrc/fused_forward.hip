@@ -45,6 +45,8 @@
 // Tails: loads through buffer resources bounded by the valid rows write zeros
 // past the end (beta = 0 makes those tokens the identity) and output stores
 // past the end are dropped.
+#include <utility>
+
 #include "efla_device.h"
 #include "efla_launch.h"
 
@@ -103,10 +105,9 @@ struct FusedLayout {
     static constexpr size_t pA = pG + 1024 * g_slot(MC, 0);    // -tril(Q K^T)
     static constexpr size_t pT = pA + 1024 * a_slot(MC, 0);    // T_ii: [i][lane] x 8 bytes
     static constexpr size_t prepBytes = pT + 512 * MC;
-    // K-wave scratch, used within one interval: fp32 G_ii [16i + col][row], alpha
+    // T-wave scratch, used within one interval: fp32 G_ii [16i + col][row]
     static constexpr size_t kGt = 0;
-    static constexpr size_t kAl = kGt + 4 * 16 * LDD * MC;
-    static constexpr size_t kBytes = kAl + 4 * C;
+    static constexpr size_t kBytes = kGt + 4 * 16 * LDD * MC;
     // output staging tile (double-buffered), transposed: [column][token]
     static constexpr size_t oBytes = (2 * TV * LDO + 15) / 16 * 16;
     static constexpr size_t offIn = 0;
@@ -360,10 +361,51 @@ __device__ __forceinline__ void prep_qk(const char *in, char *prep)
         }
 }
 
-// T wave, after the diagonal Gram tiles: alpha (lane = token; lambda is the Gram diagonal), then
-// every T_ii, lane group b owning block b and lane l16 its column l16.
-// Right-looking substitution: once T[i][j] is known it is eliminated from
-// every later row, so each of the 16 steps carries independent FMAs.  T[i][j]
+// Row-broadcast helpers for the T_ii substitution: within each 16-lane row
+// of the wave, every lane reads lane I's value (DPP row_newbcast).
+template <int I>
+__device__ __forceinline__ float row_bcast(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                              0x150 + I, 0xf, 0xf, false));
+}
+// acc -= (lane I's g) * t, the broadcast and the negation folded into the
+// FMA.  A DPP source needs two wait states after a VALU write; g comes
+// straight from an LDS load and no VALU instruction writes it.
+template <int I>
+__device__ __forceinline__ void fnmac_row_bcast(float &acc, float g, float t)
+{
+    asm volatile("v_fmac_f32_dpp %0, -%1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                 : "+v"(acc)
+                 : "v"(g), "v"(t), "n"(I));
+}
+
+// Step i of the right-looking substitution for column j = l16 of T_bb: T[i][j]
+// = alpha_i acc[i] (lane i holds alpha_i), then acc[m] -= G[m][i] T[i][j] for
+// m > i, G[m][i] being lane i's own gc[m].
+template <int I>
+__device__ __forceinline__ void subst_step(float (&acc)[16], const float (&gc)[16], float al,
+                                           bf *tcol)
+{
+    const float t = row_bcast<I>(al) * acc[I];
+    tcol[4 * I] = static_cast<bf>(t);
+#pragma unroll
+    for (int m = I + 1; m < 16; ++m) fnmac_row_bcast<I>(acc[m], gc[m], t);
+}
+template <int... I>
+__device__ __forceinline__ void subst(float (&acc)[16], const float (&gc)[16], float al, bf *tcol,
+                                      std::integer_sequence<int, I...>)
+{
+    (subst_step<I>(acc, gc, al, tcol), ...);
+}
+
+// T wave, after the diagonal Gram tiles: every T_ii, lane group b (a 16-lane
+// row) owning block b and lane j its column j.  Lane j loads row j of G_bb,
+// which is column j (G is symmetric): lambda of token 16b + j is its
+// diagonal entry, so the lane forms that token's alpha itself.  Then the 16
+// steps of the right-looking substitution (once T[i][j] is known it is
+// eliminated from every later row, so each step carries independent FMAs),
+// reading column i of G and alpha_i from lane i by row broadcast.  T[i][j]
 // is written to its place in the A fragment of T_bb: lane 16(j/4) + i, slot j%4.
 template <int DK, int DV, int C, int NS>
 __device__ __forceinline__ void prep_diag(const char *in, char *prep, char *ks, int euler)
@@ -373,44 +415,24 @@ __device__ __forceinline__ void prep_diag(const char *in, char *prep, char *ks, 
     const int lane = threadIdx.x & 63;
     const float *sB = reinterpret_cast<const float *>(in + Lay::bBeta);
     const float *sGt = reinterpret_cast<const float *>(ks + Lay::kGt);
-    float *sAl = reinterpret_cast<float *>(ks + Lay::kAl);
     bf *sT = reinterpret_cast<bf *>(prep + Lay::pT);
-    if (lane < C) sAl[lane] = update_alpha(euler, sB[lane], sGt[lane * Lay::LDD + (lane & 15)]);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int b = lane >> 4;
     if (b < MC) {
         const int j = lane & 15;
-        const float *Gt = sGt + b * 16 * Lay::LDD;
-        float al[16];
+        const float *grow = sGt + (16 * b + j) * Lay::LDD;
+        float gc[16];
 #pragma unroll
         for (int i = 0; i < 16; i += 4) {
-            const float4 x = *reinterpret_cast<const float4 *>(sAl + 16 * b + i);
-            al[i] = x.x; al[i + 1] = x.y; al[i + 2] = x.z; al[i + 3] = x.w;
+            const float4 x = *reinterpret_cast<const float4 *>(grow + i);
+            gc[i] = x.x; gc[i + 1] = x.y; gc[i + 2] = x.z; gc[i + 3] = x.w;
         }
-        // every value the substitution reads, G[m][i] for m > i, loaded up
-        // front as float4 groups of column i (rows 4*qq .. 4*qq+3)
-        float4 gcol[16][4];
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-#pragma unroll
-            for (int qq = (i + 1) / 4; qq < 4; ++qq)
-                gcol[i][qq] = *reinterpret_cast<const float4 *>(Gt + i * Lay::LDD + 4 * qq);
-        __builtin_amdgcn_sched_barrier(0);
+        const float lam = grow[j];
+        const float al = update_alpha(euler, sB[lane], lam);
         float acc[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) acc[m] = (m == j) ? 1.f : 0.f;
-        bf *tcol = sT + (b * 64 + 16 * (j >> 2)) * 4 + (j & 3);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float t = al[i] * acc[i];
-            tcol[4 * i] = static_cast<bf>(t);
-#pragma unroll
-            for (int m = i + 1; m < 16; ++m) {
-                const float4 gv = gcol[i][m >> 2];
-                const float gm = (m & 3) == 0 ? gv.x : (m & 3) == 1 ? gv.y : (m & 3) == 2 ? gv.z : gv.w;
-                acc[m] = fmaf(-gm, t, acc[m]);
-            }
-        }
+        subst(acc, gc, al, sT + (b * 64 + 16 * (j >> 2)) * 4 + (j & 3),
+              std::make_integer_sequence<int, 16>{});
     }
 }
 
