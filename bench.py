@@ -12,7 +12,8 @@ timed in the same run and reported under "decode".
                   [--path auto|staged|fused] [--no-cpu-baseline] [--no-decode] [--no-compare]
 
 The fused path is also timed with the Euler update (alpha = beta) and both
-kernel times are reported under "update_compare".
+kernel times are reported under "update_compare"; a packed (varlen) batch of
+the same token count is timed under "varlen".
 """
 from __future__ import annotations
 
@@ -296,6 +297,42 @@ def bench_decode(args, dev, n_distinct=8):
                     f"({nh * w.d_k * w.d_v * 4} B) equals the 256 MiB Infinity Cache size"}
 
 
+def bench_varlen(args, dev, n_seq=16):
+    """Packed sequences: the lm1.3b-bf16 token count per head (4 x 4096)
+    split at random into n_seq sequences, 16 heads, fused kernel."""
+    w = wl.FORWARD_WORKLOADS["lm1.3b-bf16"]
+    lengths = wl.varlen_lengths(n_seq, w.B * w.L, seed=0)
+    q, k, v, beta, cu, S0 = wl.varlen_inputs(w, lengths, seed=0)
+    qd, kd, vd, bd, cud, s0d = (x.to(dev) for x in (q, k, v, beta, cu, S0))
+    H, T = w.H, q.shape[1]
+    o = torch.empty((H, T, w.d_v), dtype=torch.bfloat16, device=dev)
+    S_L = torch.empty((n_seq, H, w.d_k, w.d_v), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    p = lambda x: x.data_ptr()  # noqa: E731
+
+    def step():
+        st = _lib.efla_forward_varlen(p(qd), p(kd), p(vd), p(bd), p(cud), p(s0d), p(o), p(S_L),
+                                      n_seq, H, T, w.d_k, w.d_v, w.chunk, _lib.EFLA_BF16,
+                                      _lib.EFLA_EXACT, sp)
+        if st:
+            raise RuntimeError(f"varlen forward failed: {_lib.status_string(st)}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    return {"sequences": n_seq, "heads": H, "tokens_per_head": T, "longest": max(lengths),
+            "shortest": min(lengths), "kernel_ms": ms, "tokens_per_s": T / (ms * 1e-3),
+            "note": "lm1.3b-bf16 recipe; random lengths; the longest sequence sets the time"}
+
+
 def cpu_baseline(w, host):
     """The fp64 oracle on the host cores, timed on the whole workload."""
     import oracle
@@ -431,6 +468,9 @@ def main():
     if not args.no_decode:
         print("[bench] decode-f32", file=sys.stderr, flush=True)
         res["decode"] = bench_decode(args, dev)
+    if not args.no_compare and w.dtype == "bf16":
+        print("[bench] varlen", file=sys.stderr, flush=True)
+        res["varlen"] = bench_varlen(args, dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, host)

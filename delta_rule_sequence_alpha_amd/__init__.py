@@ -6,6 +6,8 @@ runs in the library's HIP kernels.
 
   forward(q, k, v, beta, S0=None, chunk=64, path="auto", update="exact") -> (o, S_L)
   decode_step(q, k, v, beta, S, update="exact") -> o     (S updated in place)
+  forward_varlen(q, k, v, beta, cu_seqlens, S0=None, chunk=64) -> (o, S_L)
+                                              packed sequences, [H, T, d] tensors
   coefficients(k, beta, update="exact") -> (alpha, lambda)   stage 1 of the staged path
 update="euler" evaluates the explicit Euler step of the same ODE instead
 (alpha = beta, the delta rule) on the same kernels.
@@ -20,7 +22,7 @@ from . import _lib
 from ._lib import (EFLA_BF16, EFLA_EULER, EFLA_EXACT, EFLA_F32, EFLA_PATH_AUTO, EFLA_PATH_FUSED,
                    EFLA_PATH_STAGED, EflaError, LIB_PATH)
 
-__all__ = ["forward", "decode_step", "coefficients", "ut_transform", "chunk_scan",
+__all__ = ["forward", "forward_varlen", "decode_step", "coefficients", "ut_transform", "chunk_scan",
            "workspace_size", "EflaError", "LIB_PATH"]
 
 _PATHS = {"auto": EFLA_PATH_AUTO, "staged": EFLA_PATH_STAGED, "fused": EFLA_PATH_FUSED}
@@ -96,6 +98,32 @@ def forward(q, k, v, beta, S0=None, chunk: int = 64, path: str = "auto", workspa
                                   _ptr(S_L), B, H, L, dk, dv, chunk, dt, _ptr(workspace), ws_bytes,
                                   p, _UPDATES[update], _stream(dev))
     _raise(st, "efla_forward_update")
+    return out, S_L
+
+
+def forward_varlen(q, k, v, beta, cu_seqlens, S0=None, chunk: int = 64, out=None, S_L=None,
+                   update: str = "exact"):
+    """Packed sequences: q, k [H,T,d_k], v [H,T,d_v], beta [H,T]; cu_seqlens int32
+    [N+1] on the device.  Returns (o [H,T,d_v], S_L [N,H,d_k,d_v] fp32)."""
+    H, T, dk = k.shape
+    dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    dt = _dt(q)
+    _check(q, "q", (H, T, dk), q.dtype)
+    _check(k, "k", (H, T, dk), q.dtype)
+    _check(v, "v", (H, T, dv), q.dtype)
+    _check(beta, "beta", (H, T), torch.float32)
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)
+    if S0 is not None:
+        _check(S0, "S0", (N, H, dk, dv), torch.float32)
+    if out is None:
+        out = torch.empty((H, T, dv), dtype=q.dtype, device=q.device)
+    if S_L is None:
+        S_L = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    st = _lib.efla_forward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(cu_seqlens), _ptr(S0),
+                                  _ptr(out), _ptr(S_L), N, H, T, dk, dv, chunk, dt,
+                                  _UPDATES[update], _stream(q.device))
+    _raise(st, "efla_forward_varlen")
     return out, S_L
 
 

@@ -28,6 +28,7 @@ SIGNATURES = [
     ("efla_forward_workspace_size_ex", _S, [_I, _I, _I, _I, _I, _I, _I, _I]),
     ("efla_forward", _I, [_P] * 7 + [_I] * 7 + [_P, _S, _P]),
     ("efla_forward_ex", _I, [_P] * 7 + [_I] * 7 + [_P, _S, _I, _P]),
+    ("efla_forward_varlen", _I, [_P] * 8 + [_I] * 8 + [_P]),
     ("efla_forward_update", _I, [_P] * 7 + [_I] * 7 + [_P, _S, _I, _I, _P]),
     ("efla_decode_step", _I, [_P] * 6 + [_I] * 5 + [_P]),
     ("efla_decode_step_update", _I, [_P] * 6 + [_I] * 6 + [_P]),
@@ -98,6 +99,12 @@ def efla_forward_update(q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt, w
                         path, update, stream) -> int:
     return _call("efla_forward_update", q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt, ws,
                  ws_bytes, path, update, stream)
+
+
+def efla_forward_varlen(q, k, v, beta, cu_seqlens, S0, o, S_L, N, H, T, dk, dv, chunk, dt, update,
+                        stream) -> int:
+    return _call("efla_forward_varlen", q, k, v, beta, cu_seqlens, S0, o, S_L, N, H, T, dk, dv,
+                 chunk, dt, update, stream)
 
 
 def efla_decode_step(q, k, v, beta, S, o, N, H, dk, dv, dt, stream) -> int:

@@ -147,6 +147,32 @@ efla_status_t efla_forward_update(const void *q, const void *k, const void *v, c
     return hip_status(e);
 }
 
+efla_status_t efla_forward_varlen(const void *q, const void *k, const void *v, const float *beta,
+                                  const int *cu_seqlens, const float *S0, void *o, float *S_L,
+                                  int N, int H, int T, int dk, int dv, int chunk, efla_dtype_t dt,
+                                  efla_update_t update, void *stream)
+{
+    // the tensors are [H, T, d]: one "batch" of H rows of T tokens
+    efla_status_t s = check_shape(1, H, T, dk, dv, chunk, dt);
+    if (s != EFLA_OK) return s;
+    if (N < 0) return EFLA_ERR_INVALID_ARG;
+    if (update != EFLA_EXACT && update != EFLA_EULER) return EFLA_ERR_INVALID_ARG;
+    if (!efla::fused_supported(dt == EFLA_BF16, dk, dv, chunk)) return EFLA_ERR_UNSUPPORTED;
+    const long long NH = (long long)N * H;
+    if (NH * 8 > INT32_MAX) return EFLA_ERR_UNSUPPORTED;
+    if (NH == 0) return EFLA_OK;
+    if (!cu_seqlens || !S_L || !aligned16(S_L) || (S0 && !aligned16(S0)))
+        return EFLA_ERR_INVALID_ARG;
+    if (T > 0) {
+        if (!q || !k || !v || !beta || !o) return EFLA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(o))
+            return EFLA_ERR_INVALID_ARG;
+    }
+    return hip_status(efla::dispatch_fused_varlen(
+        dt == EFLA_BF16, dk, dv, chunk, q, k, v, beta, S0, o, S_L, (int)NH, T, cu_seqlens, H,
+        waves_override("EFLA_FUSED_WAVES"), update == EFLA_EULER, static_cast<hipStream_t>(stream)));
+}
+
 efla_status_t efla_forward_ex(const void *q, const void *k, const void *v, const float *beta,
                               const float *S0, void *o, float *S_L, int B, int H, int L, int dk,
                               int dv, int chunk, efla_dtype_t dt, void *workspace,

@@ -36,6 +36,14 @@ hipError_t dispatch_fused(bool bf16, int dk, int dv, int chunk, const void *q, c
                           const void *v, const float *beta, const float *S0, void *o, float *SL,
                           int BH, int L, int nw, bool euler, hipStream_t st);
 
+// Packed sequences: BH = N * H workgroup sequences, bh = seq * H + h; head h's
+// tokens are an L-token axis holding the N sequences back to back, sequence
+// seq at [cu[seq], cu[seq+1]) (cu: device int32 [N+1]).
+hipError_t dispatch_fused_varlen(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
+                                 const void *v, const float *beta, const float *S0, void *o,
+                                 float *SL, int BH, int L, const int *cu, int H, int nw, bool euler,
+                                 hipStream_t st);
+
 hipError_t launch_copy_state(const float *src, float *dst, long n, hipStream_t st);
 
 }  // namespace efla

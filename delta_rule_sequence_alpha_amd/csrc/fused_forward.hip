@@ -658,7 +658,7 @@ template <int DK, int DV, int C, int NS>
 __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_kernel(
     const bf *__restrict__ q, const bf *__restrict__ k, const bf *__restrict__ v,
     const float *__restrict__ beta, const float *__restrict__ S0, bf *__restrict__ o,
-    float *__restrict__ SL, int L, int nchunks, int euler)
+    float *__restrict__ SL, int L, int nchunks, const int *__restrict__ cu_seqlens, int H, int euler)
 {
     using Lay = FusedLayout<DK, DV, C, NS>;
     constexpr int TV = Lay::TV, NTILE = DV / TV, MK = DK / 16;
@@ -672,7 +672,20 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
     // the two scan waves keep a SIMD each
     const int hw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wv = hw == 0 ? Lay::NW - 1 : hw <= NS ? hw - 1 : hw == Lay::NW - 1 ? NS : NS + 1;
-    const long tokb = (long)bh * L;
+    // (sequence, head) -> its tokens.  Fixed length: sequence bh holds L
+    // tokens at bh * L.  Packed (cu_seqlens): bh = seq * H + h, and the
+    // sequences of head h are concatenated along its L-token axis; a bad
+    // offset is clamped into [0, L] (an empty or shortened sequence), never
+    // read past the tensor.
+    long tokb = (long)bh * L;
+    if (cu_seqlens) {
+        const int seq = bh / H, h = bh - seq * H;
+        const int t0 = min(max(cu_seqlens[seq], 0), L);
+        const int t1 = min(max(cu_seqlens[seq + 1], t0), L);
+        tokb = (long)h * L + t0;
+        L = t1 - t0;
+        nchunks = (L + C - 1) / C;
+    }
 
     if (wv < NS) {
         // ------------------------------------------------------------ scan waves
@@ -719,20 +732,20 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
             __syncthreads();
         }
         __syncthreads();
-        if (x.role == K_WAVE) prep_store_out(x, nchunks - 1, x.obuf((nchunks - 1) & 1));
+        if (x.role == K_WAVE && nchunks > 0) prep_store_out(x, nchunks - 1, x.obuf((nchunks - 1) & 1));
     }
 }
 
 template <int DK, int DV, int C, int NS>
 hipError_t launch_fused(const void *q, const void *k, const void *v, const float *beta,
-                        const float *S0, void *o, float *SL, int BH, int L, bool euler,
-                        hipStream_t st)
+                        const float *S0, void *o, float *SL, int BH, int L, const int *cu, int H,
+                        bool euler, hipStream_t st)
 {
     using Lay = FusedLayout<DK, DV, C, NS>;
     static_assert(Lay::bytes <= 160 * 1024, "fused kernel LDS budget");
     constexpr int NTILE = DV / Lay::TV;
     const int nchunks = (L + C - 1) / C;
-    if (BH == 0 || nchunks == 0) return hipSuccess;
+    if (BH == 0 || (nchunks == 0 && !cu)) return hipSuccess;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&fused_kernel<DK, DV, C, NS>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
@@ -740,19 +753,19 @@ hipError_t launch_fused(const void *q, const void *k, const void *v, const float
     hipLaunchKernelGGL((fused_kernel<DK, DV, C, NS>), dim3((unsigned)(BH * NTILE)),
                        dim3(64 * Lay::NW), Lay::bytes, st, static_cast<const bf *>(q),
                        static_cast<const bf *>(k), static_cast<const bf *>(v), beta, S0,
-                       static_cast<bf *>(o), SL, L, nchunks, (int)euler);
+                       static_cast<bf *>(o), SL, L, nchunks, cu, H, (int)euler);
     return hipGetLastError();
 }
 
 template <int DK, int DV, int C>
 hipError_t launch_fused_ns(const void *q, const void *k, const void *v, const float *beta,
-                           const float *S0, void *o, float *SL, int BH, int L, int ns,
-                           bool euler, hipStream_t st)
+                           const float *S0, void *o, float *SL, int BH, int L, const int *cu,
+                           int H, int ns, bool euler, hipStream_t st)
 {
     if (ns <= 0) ns = DV >= 32 ? 2 : 1;
     if (ns >= 2 && DV >= 32)
-        return launch_fused<DK, DV, C, 2>(q, k, v, beta, S0, o, SL, BH, L, euler, st);
-    return launch_fused<DK, DV, C, 1>(q, k, v, beta, S0, o, SL, BH, L, euler, st);
+        return launch_fused<DK, DV, C, 2>(q, k, v, beta, S0, o, SL, BH, L, cu, H, euler, st);
+    return launch_fused<DK, DV, C, 1>(q, k, v, beta, S0, o, SL, BH, L, cu, H, euler, st);
 }
 
 }  // namespace
@@ -769,10 +782,19 @@ hipError_t dispatch_fused(bool bf16, int dk, int dv, int chunk, const void *q, c
                           const void *v, const float *beta, const float *S0, void *o, float *SL,
                           int BH, int L, int ns, bool euler, hipStream_t st)
 {
+    return dispatch_fused_varlen(bf16, dk, dv, chunk, q, k, v, beta, S0, o, SL, BH, L, nullptr, 0,
+                                 ns, euler, st);
+}
+
+hipError_t dispatch_fused_varlen(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
+                                 const void *v, const float *beta, const float *S0, void *o,
+                                 float *SL, int BH, int L, const int *cu, int H, int ns, bool euler,
+                                 hipStream_t st)
+{
     if (!bf16) return hipErrorInvalidValue;
 #define CASE(DKV, DVV, CC)                                                                      \
     if (dk == DKV && dv == DVV && chunk == CC)                                                  \
-        return launch_fused_ns<DKV, DVV, CC>(q, k, v, beta, S0, o, SL, BH, L, ns, euler, st);
+        return launch_fused_ns<DKV, DVV, CC>(q, k, v, beta, S0, o, SL, BH, L, cu, H, ns, euler, st);
     EFLA_SHAPE_CASES(CASE)
 #undef CASE
     return hipErrorInvalidValue;

@@ -22,6 +22,10 @@ a direction uniform on the sphere is ``g / |g|`` with ``g ~ N(0, I)``.  The
 spike mask is one Bernoulli(0.05) draw per (batch, position), shared by all
 heads.  bf16 tensors are the round-to-nearest-even cast of the fp32 draw.
 
+Packed (varlen) batches: ``varlen_lengths`` splits a token total at sorted
+uniform cut points; ``varlen_inputs`` draws one [1, H, T, d] batch with a
+recipe and returns it as [H, T, d] with the cumulative offsets, and per-
+sequence initial states from ``default_rng([seed, 1])``.
 Decode: the state is drawn from ``default_rng([seed, 0])``; the tokens of step
 ``s`` (s = 0, 1, ...) come from ``default_rng([seed, s + 1])`` in the order q, k,
 v, beta.
@@ -42,6 +46,8 @@ __all__ = [
     "forward_inputs",
     "decode_state",
     "decode_tokens",
+    "varlen_lengths",
+    "varlen_inputs",
 ]
 
 
@@ -188,3 +194,32 @@ def decode_tokens(w: DecodeWorkload, step: int, seed: int = 0, n_seq: int | None
         q, k, v, beta = q[:n_seq], k[:n_seq], v[:n_seq], beta[:n_seq]
     return (_store(q, w.dtype), _store(k, w.dtype), _store(v, w.dtype),
             torch.from_numpy(np.ascontiguousarray(beta)))
+
+
+def varlen_lengths(n: int, total: int, seed: int = 0, min_len: int = 0) -> list:
+    """n sequence lengths (>= min_len) summing to ``total``: a uniform random
+    split of the remaining tokens (sorted cut points), so short, long and
+    empty sequences all occur."""
+    rng = np.random.default_rng([seed, 7])
+    rest = total - n * min_len
+    if rest < 0:
+        raise ValueError("total too small for n * min_len")
+    cuts = np.sort(rng.integers(0, rest + 1, size=n - 1))
+    parts = np.diff(np.concatenate([[0], cuts, [rest]]))
+    return [int(p) + min_len for p in parts]
+
+
+def varlen_inputs(w: ForwardWorkload, lengths, seed: int = 0):
+    """Packed sequences for the varlen forward, values drawn with recipe
+    ``w.recipe`` (the workload's B and L are ignored; its H, d_k, d_v, dtype
+    are used).  Returns (q, k [H,T,d_k], v [H,T,d_v], beta [H,T], cu_seqlens
+    int32 [N+1], S0 [N,H,d_k,d_v] fp32 or None) as CPU tensors; T = sum of
+    lengths, sequence n at tokens [cu_seqlens[n], cu_seqlens[n+1])."""
+    T = int(sum(lengths))
+    q, k, v, beta, S0 = forward_inputs(w.with_(B=1, L=T), seed=seed)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
+    S0n = None
+    if S0 is not None:
+        rng = np.random.default_rng([seed, 1])
+        S0n = torch.from_numpy(_normal(rng, (len(lengths), w.H, w.d_k, w.d_v), 0.02))
+    return q[0], k[0], v[0], beta[0], cu, S0n

@@ -107,6 +107,27 @@ efla_status_t efla_forward_ex(const void *q, const void *k, const void *v, const
                               void *workspace, size_t workspace_bytes, efla_path_t path,
                               void *stream);
 
+/*
+ * Chunked forward over N packed sequences of varying length (Methodology 3;
+ * each sequence is an independent recurrence, so its chunks restart at its
+ * first token).
+ *   q, k [H,T,d_k], v [H,T,d_v] dtype dt; beta [H,T] fp32: for each head the N
+ *        sequences back to back along the T-token axis, sequence n at tokens
+ *        [cu_seqlens[n], cu_seqlens[n+1])
+ *   cu_seqlens  device int32 [N+1], non-decreasing, cu_seqlens[0] = 0,
+ *        cu_seqlens[N] <= T.  Offsets outside [0, T] are clamped into it (the
+ *        sequence shrinks; no access leaves the tensors).
+ *   S0   [N,H,d_k,d_v] fp32 or NULL (zero state); S_L [N,H,d_k,d_v] fp32 out,
+ *        may alias S0 exactly
+ *   o    [H,T,d_v] dtype dt; tokens outside every sequence are left untouched
+ * Needs no workspace.  Only the fused path exists for it: dt must be
+ * EFLA_BF16, else EFLA_ERR_UNSUPPORTED.
+ */
+efla_status_t efla_forward_varlen(const void *q, const void *k, const void *v, const float *beta,
+                                  const int *cu_seqlens, const float *S0, void *o, float *S_L,
+                                  int N, int H, int T, int d_k, int d_v, int chunk,
+                                  efla_dtype_t dt, efla_update_t update, void *stream);
+
 /* efla_forward_ex with an explicit update (EFLA_EXACT or EFLA_EULER). */
 efla_status_t efla_forward_update(const void *q, const void *k, const void *v, const float *beta,
                                   const float *S0, void *o, float *S_L,

@@ -32,7 +32,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 12
+    assert len(declared) == 13
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], check=True,
                          capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (efla_[a-z_]+)\b", out))
@@ -146,3 +146,22 @@ def test_update_variant_validation(lib):
                                          None) == _lib.EFLA_ERR_INVALID_ARG
     assert _lib.efla_coefficients_update(FAKE, FAKE, FAKE, None, 10, 24, 0, _lib.EFLA_EULER,
                                          None) == _lib.EFLA_ERR_UNSUPPORTED
+
+
+def test_varlen_validation(lib):
+    def f(**o):
+        a = dict(q=FAKE, cu=FAKE, S_L=FAKE, N=3, H=2, T=100, dk=64, dv=64, chunk=64,
+                 dt=_lib.EFLA_BF16, update=0)
+        a.update(o)
+        return _lib.efla_forward_varlen(a["q"], FAKE, FAKE, FAKE, a["cu"], None, FAKE, a["S_L"],
+                                        a["N"], a["H"], a["T"], a["dk"], a["dv"], a["chunk"],
+                                        a["dt"], a["update"], None)
+    assert f(dt=_lib.EFLA_F32) == _lib.EFLA_ERR_UNSUPPORTED   # fused path only
+    assert f(N=-1) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(T=-1) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(dk=24) == _lib.EFLA_ERR_UNSUPPORTED
+    assert f(update=5) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(cu=None) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(S_L=MISALIGNED) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(q=None) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(N=0, cu=None) == _lib.EFLA_OK     # nothing to do
