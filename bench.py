@@ -126,9 +126,12 @@ def bench_forward(args, w, dev):
     dt = _lib.EFLA_BF16 if w.dtype == "bf16" else _lib.EFLA_F32
     esz = 2 if w.dtype == "bf16" else 4
     path = args.path
-    if path == "auto":   # the library's own choice: fused kernel for bf16 inputs
-        path = "fused" if w.dtype == "bf16" else "staged"
-    pcode = {"staged": _lib.EFLA_PATH_STAGED, "fused": _lib.EFLA_PATH_FUSED}[path]
+    if path == "auto":   # the library's own choice for this shape
+        path = {_lib.EFLA_PATH_FUSED: "fused", _lib.EFLA_PATH_STAGED: "staged",
+                _lib.EFLA_PATH_SEGMENTED: "segmented"}[
+            _lib.efla_forward_path(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, dt)]
+    pcode = {"staged": _lib.EFLA_PATH_STAGED, "fused": _lib.EFLA_PATH_FUSED,
+             "segmented": _lib.EFLA_PATH_SEGMENTED}[path]
     B, H, L, dk, dv, C = w.B, w.H, w.L, w.d_k, w.d_v, w.chunk
     o = torch.empty((B, H, L, dv), dtype=qd.dtype, device=dev)
     S_L = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
@@ -161,7 +164,7 @@ def bench_forward(args, w, dev):
         need = _lib.efla_forward_workspace_size_ex(B, H, L, dk, dv, C, dt, pcode)
         update = [_lib.EFLA_EXACT]
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-        names = ["fused"]
+        names = [path]
 
         def step(ev, timer):   # one kernel: timed over the whole region (ev, timer unused)
             p = lambda x: None if x is None else x.data_ptr()  # noqa: E731
@@ -169,8 +172,8 @@ def bench_forward(args, w, dev):
                                           H, L, dk, dv, C, dt, p(ws), need, pcode, update[0], sp)
             if st:
                 raise RuntimeError(f"fused forward failed: {_lib.status_string(st)}")
-        work = {"fused": fused_work(w, esz, S0 is not None)}
-        srcs = {"fused": "fused_forward.hip"}
+        work = {path: fused_work(w, esz, S0 is not None)}
+        srcs = {path: "fused_forward.hip" if path == "fused" else "chunk_scan.hip"}
 
     def timed(k_steps):
         """Warmup, then k_steps steps between HIP events on the launch stream.
@@ -196,7 +199,7 @@ def bench_forward(args, w, dev):
         if path == "staged":
             timer.collect(pending)
             return wall, {n: timer.mean(n) for n in names}
-        return wall, {"fused": r0.elapsed_time(r1) / k_steps}
+        return wall, {path: r0.elapsed_time(r1) / k_steps}
 
     elapsed, per_kernel = timed(args.steps)
 
@@ -435,7 +438,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="lm1.3b-bf16", choices=sorted(wl.FORWARD_WORKLOADS))
-    ap.add_argument("--path", default="auto", choices=["auto", "staged", "fused"])
+    ap.add_argument("--path", default="auto", choices=["auto", "staged", "fused", "segmented"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-compare", action="store_true",

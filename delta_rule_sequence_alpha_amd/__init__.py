@@ -20,12 +20,13 @@ import torch
 
 from . import _lib
 from ._lib import (EFLA_BF16, EFLA_EULER, EFLA_EXACT, EFLA_F32, EFLA_PATH_AUTO, EFLA_PATH_FUSED,
-                   EFLA_PATH_STAGED, EflaError, LIB_PATH)
+                   EFLA_PATH_SEGMENTED, EFLA_PATH_STAGED, EflaError, LIB_PATH)
 
 __all__ = ["forward", "forward_varlen", "decode_step", "coefficients", "ut_transform", "chunk_scan",
            "workspace_size", "EflaError", "LIB_PATH"]
 
-_PATHS = {"auto": EFLA_PATH_AUTO, "staged": EFLA_PATH_STAGED, "fused": EFLA_PATH_FUSED}
+_PATHS = {"auto": EFLA_PATH_AUTO, "staged": EFLA_PATH_STAGED, "fused": EFLA_PATH_FUSED,
+          "segmented": EFLA_PATH_SEGMENTED}
 _UPDATES = {"exact": EFLA_EXACT, "euler": EFLA_EULER}
 
 

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(_PKG, "libefla.so")
 
 EFLA_F32, EFLA_BF16 = 0, 1
 EFLA_OK, EFLA_ERR_INVALID_ARG, EFLA_ERR_UNSUPPORTED, EFLA_ERR_WORKSPACE, EFLA_ERR_HIP = range(5)
-EFLA_PATH_AUTO, EFLA_PATH_STAGED, EFLA_PATH_FUSED = 0, 1, 2
+EFLA_PATH_AUTO, EFLA_PATH_STAGED, EFLA_PATH_FUSED, EFLA_PATH_SEGMENTED = 0, 1, 2, 3
 EFLA_EXACT, EFLA_EULER = 0, 1
 
 # (name, restype, argtypes) of every exported symbol, in header order.
@@ -23,6 +23,7 @@ _I = ctypes.c_int
 _L = ctypes.c_long
 _S = ctypes.c_size_t
 SIGNATURES = [
+    ("efla_forward_path", _I, [_I] * 7),
     ("efla_status_string", ctypes.c_char_p, [_I]),
     ("efla_forward_workspace_size", _S, [_I, _I, _I, _I, _I, _I, _I]),
     ("efla_forward_workspace_size_ex", _S, [_I, _I, _I, _I, _I, _I, _I, _I]),
@@ -70,6 +71,10 @@ def status_string(s: int) -> str:
 
 def _call(name: str, *args) -> int:
     return int(getattr(lib(), name)(*args))
+
+
+def efla_forward_path(B, H, L, dk, dv, chunk, dt) -> int:
+    return int(lib().efla_forward_path(B, H, L, dk, dv, chunk, dt))
 
 
 def efla_status_string(s: int) -> str:

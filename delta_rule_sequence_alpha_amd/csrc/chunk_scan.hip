@@ -13,10 +13,31 @@
 // owns 16 columns: all d_k rows of them stay in MFMA accumulators for the
 // whole sequence, and every product above is wave-local.  The state feeds the
 // next MFMA as its B operand straight from the accumulators (PERM map).
+//
+// Segment scan over L.  A chunk maps its entry state affinely, S -> P S + R
+// with P = I - K^T W and R = K^T U, and these maps compose, so a sequence
+// split into G chunk-aligned segments is scanned in three launches:
+//   SUMMARY: every (sequence, segment) in parallel forms its segment's map --
+//            R, the state reached from S = 0 (the usual columns), and P, the
+//            state reached from S = I with U = 0 (d_k extra columns);
+//   combine: S_in(0) = S0, S_in(g) = P_{g-1} S_in(g-1) + R_{g-1};
+//   REPLAY:  every (sequence, segment) in parallel from S_in(g), writing o,
+//            and the last segment S_L.
 #include "efla_device.h"
 #include "efla_launch.h"
 
 namespace efla {
+
+enum ScanMode { SCAN_WHOLE = 0, SCAN_SUMMARY = 1, SCAN_REPLAY = 2 };
+
+struct SegArgs {
+    int mode;          // ScanMode
+    int G;             // segments per sequence (1 for SCAN_WHOLE)
+    int seg_chunks;    // chunks per segment (the last one may be shorter)
+    float *R;          // SUMMARY: [BH, G, DK, DV]
+    float *P;          // SUMMARY: [BH, G, DK, DK]
+    const float *Sin;  // REPLAY: [BH, G, DK, DV]
+};
 
 template <typename T, int DK, int DV, int C, int NW>
 struct ScanLayout {
@@ -35,7 +56,7 @@ template <typename T, int DK, int DV, int C, int NW>
 __global__ __launch_bounds__(64 * NW) void scan_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ w,
     const T *__restrict__ u, const T *__restrict__ aqk, const float *__restrict__ S0,
-    T *__restrict__ o, float *__restrict__ SL, int L, int nchunks)
+    T *__restrict__ o, float *__restrict__ SL, int L, int nchunks, SegArgs sg)
 {
     using Lay = ScanLayout<T, DK, DV, C, NW>;
     constexpr int TV = Lay::TV, NTILE = DV / TV, MC = C / 16, MK = DK / 16;
@@ -47,14 +68,32 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
     T *sA = reinterpret_cast<T *>(smem + Lay::offA);
     T *sU = reinterpret_cast<T *>(smem + Lay::offU);
 
-    int bh, tile;
-    xcd_map(blockIdx.x, gridDim.x, NTILE, bh, tile);
+    // workgroup -> (sequence bh, segment gs, column tile); SUMMARY adds the
+    // DK / TV tiles of P after the NTILE tiles of R
+    const int ntiles = NTILE + (sg.mode == SCAN_SUMMARY ? DK / TV : 0);
+    int bhs, tile;
+    xcd_map(blockIdx.x, gridDim.x, ntiles, bhs, tile);
+    const int bh = bhs / sg.G, gs = bhs - bh * sg.G;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
-    const int col = tile * TV + 16 * wv + l16;   // this lane's state column
+    const bool ptile = tile >= NTILE;                 // a column of P (U = 0, from S = I)
+    const int utile = ptile ? 0 : tile;               // U columns read (ignored for P)
+    const int col = (ptile ? tile - NTILE : tile) * TV + 16 * wv + l16;   // this lane's column
+    const int c_begin = gs * sg.seg_chunks, c_end = min(nchunks, c_begin + sg.seg_chunks);
 
     f32x4 S[MK];
     const long sbase = (long)bh * DK * DV;
-    if (S0) {   // one branch around all the loads, so they are in flight together
+    const long segbase = ((long)bh * sg.G + gs) * DK * DV;
+    if (sg.mode == SCAN_REPLAY) {
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[mk][r] = sg.Sin[segbase + (16 * mk + 4 * g + r) * DV + col];
+    } else if (sg.mode == SCAN_SUMMARY) {
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[mk][r] = (ptile && 16 * mk + 4 * g + r == col) ? 1.f : 0.f;
+    } else if (S0) {   // one branch around all the loads, so they are in flight together
 #pragma unroll
         for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
@@ -76,18 +115,18 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
     RU rU;
     RA rA;
     auto load_all = [&](int cn) {
-        cn = min(cn, nchunks - 1);
+        cn = min(cn, c_end - 1);
         const long t0 = (long)bh * L + (long)cn * C;
         const int vn = min(C, L - cn * C);
         rW.load(w + t0 * DK, DK, vn);
         rQ.load(q + t0 * DK, DK, vn);
         rK.load(k + t0 * DK, DK, vn);
-        rU.load(u + t0 * DV + tile * TV, DV, vn);
+        rU.load(u + t0 * DV + utile * TV, DV, vn);
         rA.load(aqk + ((long)bh * nchunks + cn) * C * C, C, C);
     };
-    if constexpr (PREFETCH) load_all(0);
+    if constexpr (PREFETCH) load_all(c_begin);
 
-    for (int c = 0; c < nchunks; ++c) {
+    for (int c = c_begin; c < c_end; ++c) {
         const long tok0 = (long)bh * L + (long)c * C;
         const int valid = min(C, L - c * C);
         __syncthreads();   // the previous chunk is done with LDS
@@ -106,7 +145,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
             t.store(sQ, Lay::LDK, valid);
             t.load(k + tok0 * DK, DK, valid);
             t.store(sK, Lay::LDK, valid);
-            rU.load(u + tok0 * DV + tile * TV, DV, valid);
+            rU.load(u + tok0 * DV + utile * TV, DV, valid);
             rU.store(sU, Lay::LDU, valid);
             rA.load(aqk + ((long)bh * nchunks + c) * C * C, C, C);
             rA.store(sA, Lay::LDC, C);
@@ -122,81 +161,173 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
         for (int mt = 0; mt < MC; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                E[mt][r] = to_f32(sU[(16 * mt + 4 * g + r) * Lay::LDU + 16 * wv + l16]) - E[mt][r];
+                E[mt][r] = (ptile ? 0.f : to_f32(sU[(16 * mt + 4 * g + r) * Lay::LDU + 16 * wv + l16])) -
+                           E[mt][r];
 
-        // O = Q S + A E
-        f32x4 O[MC];
+        if (sg.mode != SCAN_SUMMARY) {   // a segment's map needs no output
+            // O = Q S + A E
+            f32x4 O[MC];
 #pragma unroll
-        for (int mt = 0; mt < MC; ++mt) O[mt] = zero4();
-        mm_acc_b<T, MC, MK, false, false>(O, sQ, Lay::LDK, S);
-        mm_acc_b<T, MC, MC, true, false>(O, sA, Lay::LDC, E);
+            for (int mt = 0; mt < MC; ++mt) O[mt] = zero4();
+            mm_acc_b<T, MC, MK, false, false>(O, sQ, Lay::LDK, S);
+            mm_acc_b<T, MC, MC, true, false>(O, sA, Lay::LDC, E);
+            T *op = o + tok0 * DV;
+#pragma unroll
+            for (int mt = 0; mt < MC; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * mt + 4 * g + r;
+                    if (row < valid) op[(long)row * DV + col] = from_f32<T>(O[mt][r]);
+                }
+        }
 
         // S += K^T E   (A = K^T: element (i = d_k row, k = token) at sK[k*LDK + i])
         mm_acc_b<T, MK, MC, false, true>(S, sK, Lay::LDK, E);
-
-        T *op = o + tok0 * DV;
-#pragma unroll
-        for (int mt = 0; mt < MC; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * mt + 4 * g + r;
-                if (row < valid) op[(long)row * DV + col] = from_f32<T>(O[mt][r]);
-            }
     }
 
+    float *dst = SL + sbase;
+    int ld = DV;
+    if (sg.mode == SCAN_SUMMARY) {
+        dst = ptile ? sg.P + ((long)bh * sg.G + gs) * DK * DK : sg.R + segbase;
+        ld = ptile ? DK : DV;
+    } else if (sg.mode == SCAN_REPLAY && gs != sg.G - 1) {
+        return;   // only the last segment's final state is the sequence's
+    }
 #pragma unroll
     for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) SL[sbase + (16 * mk + 4 * g + r) * DV + col] = S[mk][r];
+        for (int r = 0; r < 4; ++r) dst[(16 * mk + 4 * g + r) * ld + col] = S[mk][r];
+}
+
+// S_in(0) = S0 (or 0); S_in(g) = P_{g-1} S_in(g-1) + R_{g-1} for g = 1 .. G-1.
+// One workgroup per (sequence, 16 columns); S_in(g-1)'s columns stay in LDS,
+// P rows are read from L2; fp32 FMAs (G - 1 small products per sequence).
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void seg_combine_kernel(const float *__restrict__ S0,
+                                                          const float *__restrict__ P,
+                                                          const float *__restrict__ R,
+                                                          float *__restrict__ Sin, int G)
+{
+    constexpr int NCB = DV / 16, PER = DK * 16 / 256;   // outputs per thread
+    __shared__ float cur[DK][17];
+    const int bh = blockIdx.x / NCB, cb = blockIdx.x - bh * NCB;
+    const int t = threadIdx.x, j = t & 15, i0 = t >> 4;   // rows i0, i0 + 16, ...
+    for (int e = t; e < DK * 16; e += 256) {
+        const int i = e >> 4, jj = e & 15;
+        const float x = S0 ? S0[((long)bh * DK + i) * DV + cb * 16 + jj] : 0.f;
+        cur[i][jj] = x;
+        Sin[(((long)bh * G) * DK + i) * DV + cb * 16 + jj] = x;
+    }
+    __syncthreads();
+    for (int gs = 1; gs < G; ++gs) {
+        const float *Pg = P + ((long)bh * G + gs - 1) * DK * DK;
+        const float *Rg = R + ((long)bh * G + gs - 1) * DK * DV;
+        float acc[PER];
+#pragma unroll
+        for (int p = 0; p < PER; ++p) acc[p] = Rg[(long)(i0 + 16 * p) * DV + cb * 16 + j];
+        for (int m = 0; m < DK; ++m) {
+            const float s = cur[m][j];
+#pragma unroll
+            for (int p = 0; p < PER; ++p) acc[p] = fmaf(Pg[(long)(i0 + 16 * p) * DK + m], s, acc[p]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            cur[i0 + 16 * p][j] = acc[p];
+            Sin[(((long)bh * G + gs) * DK + i0 + 16 * p) * DV + cb * 16 + j] = acc[p];
+        }
+        __syncthreads();
+    }
 }
 
 template <typename T, int DK, int DV, int C, int NW>
 hipError_t launch_scan(const void *q, const void *k, const void *w, const void *u, const void *aqk,
-                       const float *S0, void *o, float *SL, int BH, int L, hipStream_t st)
+                       const float *S0, void *o, float *SL, int BH, int L, SegArgs sg,
+                       hipStream_t st)
 {
     using Lay = ScanLayout<T, DK, DV, C, NW>;
-    constexpr int NTILE = DV / Lay::TV;
+    const int ntiles = DV / Lay::TV + (sg.mode == SCAN_SUMMARY ? DK / Lay::TV : 0);
     const int nchunks = (L + C - 1) / C;
     if (BH == 0) return hipSuccess;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&scan_kernel<T, DK, DV, C, NW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((scan_kernel<T, DK, DV, C, NW>), dim3((unsigned)(BH * NTILE)),
+    hipLaunchKernelGGL((scan_kernel<T, DK, DV, C, NW>), dim3((unsigned)(BH * sg.G * ntiles)),
                        dim3(64 * NW), Lay::bytes, st, static_cast<const T *>(q),
                        static_cast<const T *>(k), static_cast<const T *>(w),
                        static_cast<const T *>(u), static_cast<const T *>(aqk), S0,
-                       static_cast<T *>(o), SL, L, nchunks);
+                       static_cast<T *>(o), SL, L, nchunks, sg);
     return hipGetLastError();
 }
 
-// Waves per workgroup (1, 2 or 4; an explicit nw > 0 caps it).
+// Waves per workgroup (1, 2 or 4; an explicit nw > 0 caps it).  The
+// segment summary also tiles the d_k columns of P, so there the tile must
+// divide d_k too.
 template <typename T, int DK, int DV, int C>
 hipError_t launch_scan_auto(const void *q, const void *k, const void *w, const void *u,
                             const void *aqk, const float *S0, void *o, float *SL, int BH, int L,
-                            int nw, hipStream_t st)
+                            int nw, SegArgs sg, hipStream_t st)
 {
     // Every wave owns 16 columns whatever NW is (the number of waves, hence of
     // busy SIMDs, is BH * DV / 16); wider tiles share each chunk's loads
     // between more waves.
-    if (nw <= 0) nw = DV >= 64 ? 4 : DV >= 32 ? 2 : 1;
-    if (nw >= 4 && DV >= 64)
-        return launch_scan<T, DK, DV, C, 4>(q, k, w, u, aqk, S0, o, SL, BH, L, st);
-    if (nw >= 2 && DV >= 32)
-        return launch_scan<T, DK, DV, C, 2>(q, k, w, u, aqk, S0, o, SL, BH, L, st);
-    return launch_scan<T, DK, DV, C, 1>(q, k, w, u, aqk, S0, o, SL, BH, L, st);
+    constexpr int DMIN = DK < DV ? DK : DV;
+    const int wmax = sg.mode == SCAN_SUMMARY ? DMIN : DV;
+    if (nw <= 0) nw = 4;
+    if (nw >= 4 && wmax >= 64)
+        return launch_scan<T, DK, DV, C, 4>(q, k, w, u, aqk, S0, o, SL, BH, L, sg, st);
+    if (nw >= 2 && wmax >= 32)
+        return launch_scan<T, DK, DV, C, 2>(q, k, w, u, aqk, S0, o, SL, BH, L, sg, st);
+    return launch_scan<T, DK, DV, C, 1>(q, k, w, u, aqk, S0, o, SL, BH, L, sg, st);
+}
+
+template <typename T, int DK, int DV, int C>
+hipError_t launch_scan_segmented(const void *q, const void *k, const void *w, const void *u,
+                                 const void *aqk, const float *S0, void *o, float *SL, int BH,
+                                 int L, int G, int seg_chunks, float *R, float *P, float *Sin,
+                                 int nw, hipStream_t st)
+{
+    if (BH == 0) return hipSuccess;
+    SegArgs sum{SCAN_SUMMARY, G, seg_chunks, R, P, nullptr};
+    hipError_t e = launch_scan_auto<T, DK, DV, C>(q, k, w, u, aqk, nullptr, o, SL, BH, L, nw, sum, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((seg_combine_kernel<DK, DV>), dim3((unsigned)(BH * (DV / 16))), dim3(256), 0,
+                       st, S0, P, R, Sin, G);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    SegArgs rep{SCAN_REPLAY, G, seg_chunks, nullptr, nullptr, Sin};
+    return launch_scan_auto<T, DK, DV, C>(q, k, w, u, aqk, nullptr, o, SL, BH, L, nw, rep, st);
 }
 
 hipError_t dispatch_scan(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                          const void *w, const void *u, const void *aqk, const float *S0, void *o,
                          float *SL, int BH, int L, int nw, hipStream_t st)
 {
+    const SegArgs whole{SCAN_WHOLE, 1, 1 << 30, nullptr, nullptr, nullptr};
 #define CASE(DKV, DVV, CC)                                                                      \
     if (dk == DKV && dv == DVV && chunk == CC)                                                  \
         return bf16 ? launch_scan_auto<__bf16, DKV, DVV, CC>(q, k, w, u, aqk, S0, o, SL, BH, L, \
-                                                             nw, st)                            \
+                                                             nw, whole, st)                     \
                     : launch_scan_auto<float, DKV, DVV, CC>(q, k, w, u, aqk, S0, o, SL, BH, L,  \
-                                                            nw, st);
+                                                            nw, whole, st);
+    EFLA_SHAPE_CASES(CASE)
+#undef CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t dispatch_scan_segmented(bool bf16, int dk, int dv, int chunk, const void *q,
+                                   const void *k, const void *w, const void *u, const void *aqk,
+                                   const float *S0, void *o, float *SL, int BH, int L, int G,
+                                   int seg_chunks, float *R, float *P, float *Sin, int nw,
+                                   hipStream_t st)
+{
+#define CASE(DKV, DVV, CC)                                                                      \
+    if (dk == DKV && dv == DVV && chunk == CC)                                                  \
+        return bf16 ? launch_scan_segmented<__bf16, DKV, DVV, CC>(                              \
+                          q, k, w, u, aqk, S0, o, SL, BH, L, G, seg_chunks, R, P, Sin, nw, st)  \
+                    : launch_scan_segmented<float, DKV, DVV, CC>(                               \
+                          q, k, w, u, aqk, S0, o, SL, BH, L, G, seg_chunks, R, P, Sin, nw, st);
     EFLA_SHAPE_CASES(CASE)
 #undef CASE
     return hipErrorInvalidValue;

@@ -32,29 +32,69 @@ efla_status_t check_shape(int B, int H, int L, int dk, int dv, int chunk, efla_d
     return EFLA_OK;
 }
 
-struct StagedWs {
-    size_t alpha, w, u, aqk, total;
+// Segments of the segmented scan: enough (sequence, segment, column tile)
+// workgroups in its summary pass for ~2 per CU of the 256, with at least 4
+// chunks per segment.  G = 1 means splitting does not pay.
+struct SegPlan {
+    int G, seg_chunks;
 };
 
-StagedWs staged_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t dt)
+SegPlan seg_plan(long long BH, int L, int dk, int dv, int chunk)
+{
+    const int nchunks = (L + chunk - 1) / chunk;
+    const int dmin = dk < dv ? dk : dv;
+    const int tv = dmin >= 64 ? 64 : dmin;               // columns per summary workgroup
+    const long long tiles = BH * ((dk + dv) / tv);
+    long long G = (512 + tiles - 1) / (tiles > 0 ? tiles : 1);
+    if (G > nchunks / 4) G = nchunks / 4;
+    // it costs about three scans' work: only worth it with many segments on
+    // a GPU the plain scan leaves mostly idle
+    if (G < 4 || BH * ((dv + 63) / 64) >= 128) G = 1;
+    SegPlan p;
+    p.seg_chunks = (int)((nchunks + G - 1) / G);
+    p.G = p.seg_chunks > 0 ? (nchunks + p.seg_chunks - 1) / p.seg_chunks : 1;
+    return p;
+}
+
+struct StagedWs {
+    size_t alpha, w, u, aqk, R, P, Sin, total;
+};
+
+StagedWs staged_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t dt, int G)
 {
     const size_t n = (size_t)B * H * L;
     const size_t nch = (size_t)B * H * ((L + chunk - 1) / chunk);
+    const size_t segs = (size_t)B * H * G;
     StagedWs s;
     s.alpha = 0;
     s.w = s.alpha + align_up(n * sizeof(float));
     s.u = s.w + align_up(n * dk * esize(dt));
     s.aqk = s.u + align_up(n * dv * esize(dt));
-    s.total = s.aqk + align_up(nch * chunk * chunk * esize(dt));
+    s.R = s.aqk + align_up(nch * chunk * chunk * esize(dt));
+    s.total = s.R;
+    s.P = s.Sin = s.R;
+    if (G > 1) {   // the segmented scan's maps and entry states (fp32)
+        s.P = s.R + align_up(segs * dk * dv * sizeof(float));
+        s.Sin = s.P + align_up(segs * dk * dk * sizeof(float));
+        s.total = s.Sin + align_up(segs * dk * dv * sizeof(float));
+    }
     return s;
 }
 
-// AUTO: the fused kernel where it exists (bf16 inputs), else the staged kernels.
-efla_path_t resolve_path(efla_path_t p, efla_dtype_t dt, int dk, int dv, int chunk)
+// AUTO: the fused kernel where it exists (bf16 inputs); else the segmented
+// scan when it has more than one segment per sequence, else the staged one.
+efla_path_t resolve_path(efla_path_t p, efla_dtype_t dt, int B, int H, int L, int dk, int dv,
+                         int chunk)
 {
     if (p != EFLA_PATH_AUTO) return p;
-    return efla::fused_supported(dt == EFLA_BF16, dk, dv, chunk) ? EFLA_PATH_FUSED
-                                                                  : EFLA_PATH_STAGED;
+    if (efla::fused_supported(dt == EFLA_BF16, dk, dv, chunk)) return EFLA_PATH_FUSED;
+    return seg_plan((long long)B * H, L, dk, dv, chunk).G > 1 ? EFLA_PATH_SEGMENTED
+                                                               : EFLA_PATH_STAGED;
+}
+
+int plan_G(efla_path_t p, int B, int H, int L, int dk, int dv, int chunk)
+{
+    return p == EFLA_PATH_SEGMENTED ? seg_plan((long long)B * H, L, dk, dv, chunk).G : 1;
 }
 
 // Waves per workgroup of the scan / fused kernels (0 = the built-in choice).
@@ -83,12 +123,19 @@ const char *efla_status_string(efla_status_t s)
     return "EFLA_ERR_UNKNOWN";
 }
 
+efla_path_t efla_forward_path(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t dt)
+{
+    if (check_shape(B, H, L, dk, dv, chunk, dt) != EFLA_OK) return EFLA_PATH_AUTO;
+    return resolve_path(EFLA_PATH_AUTO, dt, B, H, L, dk, dv, chunk);
+}
+
 size_t efla_forward_workspace_size_ex(int B, int H, int L, int dk, int dv, int chunk,
                                       efla_dtype_t dt, efla_path_t path)
 {
     if (check_shape(B, H, L, dk, dv, chunk, dt) != EFLA_OK) return 0;
-    path = resolve_path(path, dt, dk, dv, chunk);
-    if (path == EFLA_PATH_STAGED) return staged_ws(B, H, L, dk, dv, chunk, dt).total;
+    path = resolve_path(path, dt, B, H, L, dk, dv, chunk);
+    if (path == EFLA_PATH_STAGED || path == EFLA_PATH_SEGMENTED)
+        return staged_ws(B, H, L, dk, dv, chunk, dt, plan_G(path, B, H, L, dk, dv, chunk)).total;
     return 0;
 }
 
@@ -107,9 +154,10 @@ efla_status_t efla_forward_update(const void *q, const void *k, const void *v, c
     if (s != EFLA_OK) return s;
     if (update != EFLA_EXACT && update != EFLA_EULER) return EFLA_ERR_INVALID_ARG;
     const bool euler = update == EFLA_EULER;
-    if (path != EFLA_PATH_AUTO && path != EFLA_PATH_STAGED && path != EFLA_PATH_FUSED)
+    if (path != EFLA_PATH_AUTO && path != EFLA_PATH_STAGED && path != EFLA_PATH_FUSED &&
+        path != EFLA_PATH_SEGMENTED)
         return EFLA_ERR_INVALID_ARG;
-    path = resolve_path(path, dt, dk, dv, chunk);
+    path = resolve_path(path, dt, B, H, L, dk, dv, chunk);
     const long long BH = (long long)B * H;
     if (BH == 0) return EFLA_OK;
     if (!S_L || !aligned16(S_L) || (S0 && !aligned16(S0))) return EFLA_ERR_INVALID_ARG;
@@ -126,7 +174,8 @@ efla_status_t efla_forward_update(const void *q, const void *k, const void *v, c
                                                o, S_L, (int)BH, L,
                                                waves_override("EFLA_FUSED_WAVES"), euler, st));
     }
-    const StagedWs ws = staged_ws(B, H, L, dk, dv, chunk, dt);
+    const SegPlan plan = path == EFLA_PATH_SEGMENTED ? seg_plan(BH, L, dk, dv, chunk) : SegPlan{1, 0};
+    const StagedWs ws = staged_ws(B, H, L, dk, dv, chunk, dt, plan.G);
     if (L > 0) {
         if (!workspace || workspace_bytes < ws.total) return EFLA_ERR_WORKSPACE;
         if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return EFLA_ERR_INVALID_ARG;
@@ -141,7 +190,14 @@ efla_status_t efla_forward_update(const void *q, const void *k, const void *v, c
     hipError_t e = efla::dispatch_coef(bf, dk, k, beta, alpha, nullptr, BH * L, euler, st);
     if (e == hipSuccess)
         e = efla::dispatch_ut(bf, dk, dv, chunk, q, k, v, alpha, w, u, aqk, (int)BH, L, st);
-    if (e == hipSuccess)
+    if (e == hipSuccess && plan.G > 1)
+        e = efla::dispatch_scan_segmented(bf, dk, dv, chunk, q, k, w, u, aqk, S0, o, S_L, (int)BH, L,
+                                          plan.G, plan.seg_chunks,
+                                          reinterpret_cast<float *>(base + ws.R),
+                                          reinterpret_cast<float *>(base + ws.P),
+                                          reinterpret_cast<float *>(base + ws.Sin),
+                                          scan_waves_override(), st);
+    else if (e == hipSuccess)
         e = efla::dispatch_scan(bf, dk, dv, chunk, q, k, w, u, aqk, S0, o, S_L, (int)BH, L,
                                 scan_waves_override(), st);
     return hip_status(e);

@@ -30,6 +30,16 @@ hipError_t dispatch_scan(bool bf16, int dk, int dv, int chunk, const void *q, co
                          const void *w, const void *u, const void *aqk, const float *S0, void *o,
                          float *SL, int BH, int L, int nw, hipStream_t st);
 
+// The same scan split over L into G segments of seg_chunks chunks (the last
+// may be shorter): segment maps (R [BH,G,dk,dv], P [BH,G,dk,dk]), their
+// composition into entry states (Sin [BH,G,dk,dv]) and the segments replayed
+// from them; o and S_L as from dispatch_scan.
+hipError_t dispatch_scan_segmented(bool bf16, int dk, int dv, int chunk, const void *q,
+                                   const void *k, const void *w, const void *u, const void *aqk,
+                                   const float *S0, void *o, float *SL, int BH, int L, int G,
+                                   int seg_chunks, float *R, float *P, float *Sin, int nw,
+                                   hipStream_t st);
+
 bool fused_supported(bool bf16, int dk, int dv, int chunk);
 
 hipError_t dispatch_fused(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,

@@ -53,11 +53,18 @@ typedef enum {
     EFLA_ERR_HIP = 4           /* a HIP launch reported an error                   */
 } efla_status_t;
 
-/* Evaluation strategy of efla_forward_ex. */
+/* Evaluation strategy of efla_forward_ex.  AUTO takes FUSED for bf16 inputs;
+ * for fp32, SEGMENTED when the sequences are too few to fill the GPU and long
+ * enough to split, else STAGED. */
 typedef enum {
     EFLA_PATH_AUTO = 0,    /* the fastest path available for the shape         */
     EFLA_PATH_STAGED = 1,  /* coefficient -> UT-transform -> state-scan kernels */
-    EFLA_PATH_FUSED = 2    /* one kernel; no intermediate HBM traffic           */
+    EFLA_PATH_FUSED = 2,   /* one kernel; no intermediate HBM traffic           */
+    EFLA_PATH_SEGMENTED = 3 /* staged, with the state scan split over L into
+                               segments: each segment's affine map S -> P S + R
+                               is formed in parallel, the maps are composed into
+                               every segment's entry state, and the segments are
+                               replayed in parallel (for few, long sequences) */
 } efla_path_t;
 
 /* Coefficient of the update.
@@ -70,6 +77,10 @@ typedef enum {
  *              differs.
  * Any other value returns EFLA_ERR_INVALID_ARG. */
 typedef enum { EFLA_EXACT = 0, EFLA_EULER = 1 } efla_update_t;
+
+/* The path EFLA_PATH_AUTO takes for this shape (EFLA_PATH_AUTO itself for an
+ * invalid shape). */
+efla_path_t efla_forward_path(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype_t dt);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *efla_status_string(efla_status_t s);
@@ -157,9 +168,10 @@ efla_status_t efla_decode_step_update(const void *q, const void *k, const void *
  * Stage 1 of the staged path: per-token coefficients (Methodology 2-3).
  *   k [n_tokens, d_k] dtype dt; beta [n_tokens] fp32
  *   alpha [n_tokens] fp32 out; lambda [n_tokens] fp32 out, or NULL to skip.
- * lambda_t = |k_t|^2 accumulated in fp32 from the stored k;
- * alpha_t = beta_t * (1 - exp(-x)) / x with x = beta_t lambda_t (expm1 form),
- * and alpha_t = beta_t when |x| < 1e-30.
+ * lambda_t = |k_t|^2 accumulated in fp32 from the stored k; with
+ * x = beta_t lambda_t, alpha_t = beta_t phi(x), phi(x) = (1 - e^{-x}) / x from
+ * its Taylor series for |x| < 1/2 (so alpha_t = beta_t at lambda_t = 0), and
+ * (1 - e^{-x}) / lambda_t otherwise.
  */
 efla_status_t efla_coefficients(const void *k, const float *beta, float *alpha, float *lambda,
                                 long n_tokens, int d_k, efla_dtype_t dt, void *stream);

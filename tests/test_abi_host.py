@@ -32,7 +32,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 13
+    assert len(declared) == 14
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], check=True,
                          capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (efla_[a-z_]+)\b", out))
@@ -165,3 +165,17 @@ def test_varlen_validation(lib):
     assert f(S_L=MISALIGNED) == _lib.EFLA_ERR_INVALID_ARG
     assert f(q=None) == _lib.EFLA_ERR_INVALID_ARG
     assert f(N=0, cu=None) == _lib.EFLA_OK     # nothing to do
+
+
+def test_auto_path_choice(lib):
+    # bf16: the fused kernel; fp32: segmented scan for few long sequences, else staged
+    assert _lib.efla_forward_path(4, 16, 4096, 128, 128, 64, _lib.EFLA_BF16) == _lib.EFLA_PATH_FUSED
+    assert _lib.efla_forward_path(1, 16, 65536, 128, 128, 64, _lib.EFLA_F32) == _lib.EFLA_PATH_SEGMENTED
+    assert _lib.efla_forward_path(1, 1, 64, 16, 16, 16, _lib.EFLA_F32) == _lib.EFLA_PATH_STAGED
+    assert _lib.efla_forward_path(8, 16, 4096, 128, 128, 64, _lib.EFLA_F32) == _lib.EFLA_PATH_STAGED
+    assert _lib.efla_forward_path(1, 1, 64, 24, 16, 16, _lib.EFLA_F32) == _lib.EFLA_PATH_AUTO
+    seg = _lib.efla_forward_workspace_size_ex(1, 16, 65536, 128, 128, 64, _lib.EFLA_F32,
+                                              _lib.EFLA_PATH_SEGMENTED)
+    stg = _lib.efla_forward_workspace_size_ex(1, 16, 65536, 128, 128, 64, _lib.EFLA_F32,
+                                              _lib.EFLA_PATH_STAGED)
+    assert seg > stg > 0
