@@ -28,6 +28,16 @@ Entry points
                              whole-sequence recurrence (C, fp64, OpenMP)
   decode(q, k, v, beta, S, update="exact")
                              one single-token step (C, fp64, OpenMP)
+  alpha_grad(beta, lam, update="exact")
+                             (d alpha/d beta, d alpha/d lambda) per token (C, fp64)
+  backward(q, k, v, beta, S0, dO, dS_L=None, update="exact")
+                             gradients (dq, dk, dv, dbeta, dS0) of a loss with
+                             dLoss/do = dO and dLoss/dS_L = dS_L: the adjoint of
+                             the token recurrence, backwards in time (C, fp64)
+
+``backward`` and ``alpha_grad`` are pinned by tests/test_oracle_backward_pins.py
+against central finite differences of ``forward`` and against torch's automatic
+differentiation of an independently written fp64 recurrence.
 
 Parity of ``forward``/``decode``/``alpha`` is pinned by tests/test_oracle_pins.py
 against matrix exponentials, the exact ODE flow and invariants.  The chunk
@@ -59,6 +69,11 @@ def _lib():
         lib.efla_oracle_forward.argtypes = [_DP] * 7 + [ctypes.c_long] * 5 + [ctypes.c_int] * 2
         lib.efla_oracle_decode.restype = ctypes.c_int
         lib.efla_oracle_decode.argtypes = [_DP] * 6 + [ctypes.c_long] * 4 + [ctypes.c_int] * 2
+        lib.efla_oracle_alpha_grad.restype = None
+        lib.efla_oracle_alpha_grad.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int,
+                                               _DP, _DP]
+        lib.efla_oracle_backward.restype = ctypes.c_int
+        lib.efla_oracle_backward.argtypes = [_DP] * 12 + [ctypes.c_long] * 5 + [ctypes.c_int] * 2
         lib.efla_oracle_max_threads.restype = ctypes.c_int
         lib.efla_oracle_max_threads.argtypes = []
         _LIB = lib
@@ -193,3 +208,52 @@ def decode(q, k, v, beta, S, threads: int = 0, update: str = "exact"):
     if rc != 0:
         raise RuntimeError("oracle decode failed")
     return o, S
+
+
+def alpha_grad(beta, lam, update: str = "exact"):
+    """(d alpha / d beta, d alpha / d lambda) from the C oracle, elementwise (fp64)."""
+    beta = _f64(beta)
+    lam = _f64(lam)
+    beta, lam = np.broadcast_arrays(beta, lam)
+    db = np.empty(beta.shape)
+    dl = np.empty(beta.shape)
+    a = ctypes.c_double()
+    b = ctypes.c_double()
+    eu = _euler(update)
+    for idx in np.ndindex(*beta.shape):
+        _lib().efla_oracle_alpha_grad(float(beta[idx]), float(lam[idx]), eu, ctypes.byref(a),
+                                      ctypes.byref(b))
+        db[idx] = a.value
+        dl[idx] = b.value
+    return db, dl
+
+
+def backward(q, k, v, beta, S0, dO, dS_L=None, threads: int = 0, update: str = "exact"):
+    """Gradients through ``forward`` of a loss with dLoss/do = dO and
+    dLoss/dS_L = dS_L (None: zero).  Returns (dq, dk, dv, dbeta, dS0) in fp64,
+    shaped like q, k, v, beta and [B,H,dk,dv]; dS0 is returned even when S0 is
+    None (the gradient with respect to the zero initial state)."""
+    q, k, v, beta, dO = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(dO)
+    B, H, L, dk = k.shape
+    dv = v.shape[-1]
+    if q.shape != (B, H, L, dk) or v.shape != (B, H, L, dv) or beta.shape != (B, H, L) \
+            or dO.shape != (B, H, L, dv):
+        raise ValueError("shape mismatch")
+    s0 = None if S0 is None else _f64(S0)
+    dsl = None if dS_L is None else _f64(dS_L)
+    for x in (s0, dsl):
+        if x is not None and x.shape != (B, H, dk, dv):
+            raise ValueError("state shape mismatch")
+    dq = np.empty((B, H, L, dk))
+    dk_ = np.empty((B, H, L, dk))
+    dv_ = np.empty((B, H, L, dv))
+    dbeta = np.empty((B, H, L))
+    dS0 = np.empty((B, H, dk, dv))
+    rc = _lib().efla_oracle_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                     None if s0 is None else _ptr(s0), _ptr(dO),
+                                     None if dsl is None else _ptr(dsl), _ptr(dq), _ptr(dk_),
+                                     _ptr(dv_), _ptr(dbeta), _ptr(dS0), B, H, L, dk, dv,
+                                     _euler(update), int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle backward failed")
+    return dq, dk_, dv_, dbeta, dS0
