@@ -13,6 +13,10 @@ update="euler" evaluates the explicit Euler step of the same ODE instead
 (alpha = beta, the delta rule) on the same kernels.
   ut_transform(q, k, v, alpha, chunk) -> (W, U, A)   stage 2
   chunk_scan(q, k, W, U, A, S0, chunk) -> (o, S_L)   stage 3
+  backward(q, k, v, beta, S0, d_o, dS_L=None, chunk=64, update="exact")
+      -> (dq, dk, dv, dbeta, dS0)   gradients of a loss through forward
+  efla(q, k, v, beta, S0=None, chunk=64, update="exact") -> (o, S_L)
+      forward + backward as a torch.autograd.Function
 """
 from __future__ import annotations
 
@@ -23,7 +27,7 @@ from ._lib import (EFLA_BF16, EFLA_EULER, EFLA_EXACT, EFLA_F32, EFLA_PATH_AUTO, 
                    EFLA_PATH_SEGMENTED, EFLA_PATH_STAGED, EflaError, LIB_PATH)
 
 __all__ = ["forward", "forward_varlen", "decode_step", "coefficients", "ut_transform", "chunk_scan",
-           "workspace_size", "EflaError", "LIB_PATH"]
+           "backward", "efla", "workspace_size", "backward_workspace_size", "EflaError", "LIB_PATH"]
 
 _PATHS = {"auto": EFLA_PATH_AUTO, "staged": EFLA_PATH_STAGED, "fused": EFLA_PATH_FUSED,
           "segmented": EFLA_PATH_SEGMENTED}
@@ -194,3 +198,68 @@ def chunk_scan(q, k, W, U, A, S0=None, chunk: int = 64):
                               _ptr(S_L), B, H, L, dk, dv, chunk, _dt(q), _stream(q.device))
     _raise(st, "efla_chunk_scan")
     return o, S_L
+
+
+def backward_workspace_size(B, H, L, d_k, d_v, chunk, dtype) -> int:
+    dt = EFLA_BF16 if dtype == torch.bfloat16 else EFLA_F32
+    return _lib.efla_backward_workspace_size(B, H, L, d_k, d_v, chunk, dt)
+
+
+def backward(q, k, v, beta, S0, d_o, dS_L=None, chunk: int = 64, update: str = "exact",
+             workspace=None, want_dS0: bool = True):
+    """Gradients of a loss through ``forward``: given d_o = dLoss/do and
+    dS_L = dLoss/dS_L (None: zero), returns (dq, dk, dv, dbeta, dS0) with dq,
+    dk, dv in q's dtype, dbeta and dS0 fp32 (dS0 None if not ``want_dS0``)."""
+    B, H, L, dk = k.shape
+    dv = v.shape[-1]
+    dt = _dt(q)
+    _check(q, "q", (B, H, L, dk), q.dtype)
+    _check(k, "k", (B, H, L, dk), q.dtype)
+    _check(v, "v", (B, H, L, dv), q.dtype)
+    _check(beta, "beta", (B, H, L), torch.float32)
+    _check(d_o, "d_o", (B, H, L, dv), q.dtype)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), torch.float32)
+    if dS_L is not None:
+        _check(dS_L, "dS_L", (B, H, dk, dv), torch.float32)
+    dev = q.device
+    dq = torch.empty_like(q)
+    dkk = torch.empty_like(k)
+    dvv = torch.empty_like(v)
+    dbeta = torch.empty_like(beta)
+    dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None
+    need = _lib.efla_backward_workspace_size(B, H, L, dk, dv, chunk, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.efla_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(d_o), _ptr(dS_L),
+                            _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dbeta), _ptr(dS0), B, H, L, dk,
+                            dv, chunk, dt, _UPDATES[update], _ptr(workspace), ws_bytes,
+                            _stream(dev))
+    _raise(st, "efla_backward")
+    return dq, dkk, dvv, dbeta, dS0
+
+
+class _EflaFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, beta, S0, chunk, update):
+        o, S_L = forward(q, k, v, beta, S0, chunk=chunk, update=update)
+        ctx.save_for_backward(q, k, v, beta, S0)
+        ctx.chunk, ctx.update = chunk, update
+        return o, S_L
+
+    @staticmethod
+    def backward(ctx, d_o, dS_L):
+        q, k, v, beta, S0 = ctx.saved_tensors
+        if d_o is None:
+            d_o = torch.zeros_like(q[..., :1].expand(*q.shape[:-1], v.shape[-1]))
+        d_o = d_o.contiguous()
+        dS_L = None if dS_L is None else dS_L.contiguous()
+        dq, dk, dv, dbeta, dS0 = backward(q, k, v, beta, S0, d_o, dS_L, chunk=ctx.chunk,
+                                          update=ctx.update, want_dS0=S0 is not None)
+        return dq, dk, dv, dbeta, dS0, None, None
+
+
+def efla(q, k, v, beta, S0=None, chunk: int = 64, update: str = "exact"):
+    """(o, S_L) = forward(...), differentiable in q, k, v, beta and S0."""
+    return _EflaFunction.apply(q, k, v, beta, S0, chunk, update)

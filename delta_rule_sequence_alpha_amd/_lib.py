@@ -37,6 +37,8 @@ SIGNATURES = [
     ("efla_coefficients_update", _I, [_P] * 4 + [_L, _I, _I, _I, _P]),
     ("efla_ut_transform", _I, [_P] * 7 + [_I] * 7 + [_P]),
     ("efla_chunk_scan", _I, [_P] * 8 + [_I] * 7 + [_P]),
+    ("efla_backward_workspace_size", _S, [_I] * 7),
+    ("efla_backward", _I, [_P] * 12 + [_I] * 8 + [_P, _S, _P]),
 ]
 
 _lib = None
@@ -136,3 +138,13 @@ def efla_ut_transform(q, k, v, alpha, w, u, a_qk, B, H, L, dk, dv, chunk, dt, st
 def efla_chunk_scan(q, k, w, u, a_qk, S0, o, S_L, B, H, L, dk, dv, chunk, dt, stream) -> int:
     return _call("efla_chunk_scan", q, k, w, u, a_qk, S0, o, S_L, B, H, L, dk, dv, chunk, dt,
                  stream)
+
+
+def efla_backward_workspace_size(B, H, L, dk, dv, chunk, dt) -> int:
+    return int(lib().efla_backward_workspace_size(B, H, L, dk, dv, chunk, dt))
+
+
+def efla_backward(q, k, v, beta, S0, d_o, dS_L, dq, dk_, dv_, dbeta, dS0, B, H, L, dk, dv, chunk,
+                  dt, update, ws, ws_bytes, stream) -> int:
+    return _call("efla_backward", q, k, v, beta, S0, d_o, dS_L, dq, dk_, dv_, dbeta, dS0, B, H, L,
+                 dk, dv, chunk, dt, update, ws, ws_bytes, stream)

@@ -1,0 +1,434 @@
+// Per-chunk gradients of the chunkwise EFLA forward ("Exact Flow Linear
+// Attention: Exact Solution from Continuous-Time Dynamics", Technical Summary,
+// Methodology 3: the exact-flow update keeps the delta rule's chunkwise form;
+// the pages train with it but print no backward).
+//
+// One chunk of C tokens, entry state S (d_k x d_v), D = diag(alpha):
+//   Gamma = K K^T,  N = (I + D strictly_lower(Gamma))^{-1},  T = N D
+//   X = V - K S         (the residuals v_t - S_{t-1}^T k_t, stacked)
+//   E = T X,  O = Q S + (tril(Q K^T)) E,  S_out = S + K^T E.
+// Given the chunk's dE = dLoss/dE and dS_out (both from the reverse scan):
+//   dX = T^T dE = D (N^T dE)                         dv = dX
+//   dq = dO S^T + dA K,   dA = tril(dO E^T)
+//   dk = -dX S^T + E dS_out^T + dA^T Q + dGam K + dGam^T K + 2 dlambda k
+// and alpha enters through T = N D and through G = D strictly_lower(Gamma):
+//   dalpha_j  = x_j . (N^T dE)_j                 (the D factor of T; x_j = row j of X)
+//   dN  = dE (D X)^T,   dG = -strictly_lower(N^T dN N^T)
+//   dalpha_i += sum_{j<i} dG_ij Gamma_ij,   dGam = D dG
+//   dbeta = dalpha d alpha / d beta,   dlambda = dalpha d alpha / d lambda.
+// All of it in fp32 on fp32 MFMA (16x16x4), one workgroup of 8 waves per
+// chunk.  LDS holds K, two C x max(d_k, d_v) fp32 operand buffers and three
+// C x C matrices; the entry state and dS_out are read from the workspace
+// straight into MFMA registers.
+#include "efla_device.h"
+#include "efla_launch.h"
+
+namespace efla {
+
+// d alpha / d beta and d alpha / d lambda.  With x = beta lambda:
+// d alpha / d beta = e^{-x}; d alpha / d lambda = -beta^2 g(x) with
+// g(x) = (1 - (1 + x) e^{-x}) / x^2 = sum_{n>=0} (-1)^n (n+1) x^n / (n+2)!,
+// summed to n = 9 for |x| < 1/2 (the closed form cancels there), else the
+// closed form.  Euler (alpha = beta): 1 and 0.
+__device__ __forceinline__ void alpha_partials(int euler, float beta, float lambda, float &da_db,
+                                               float &da_dl)
+{
+    if (euler) {
+        da_db = 1.f;
+        da_dl = 0.f;
+        return;
+    }
+    const float x = beta * lambda;
+    const float e = __builtin_amdgcn_exp2f(-x * 1.44269504088896341f);
+    constexpr float c[10] = {1.f / 2,          -2.f / 6,         3.f / 24,         -4.f / 120,
+                             5.f / 720,        -6.f / 5040,      7.f / 40320,      -8.f / 362880,
+                             9.f / 3628800,    -10.f / 39916800};
+    float p = c[9];
+#pragma unroll
+    for (int n = 8; n >= 0; --n) p = fmaf(p, x, c[n]);
+    const float direct = (1.f - e - x * e) / (x * x);
+    const float gx = fabsf(x) < 0.5f ? p : direct;
+    da_db = e;
+    da_dl = -beta * beta * gx;
+}
+
+template <int DK, int DV, int C>
+struct GradLayout {
+    static constexpr int NW = 8;
+    static constexpr int DM = DK > DV ? DK : DV;
+    static constexpr int LDK = DK + 4, LDV = DV + 4, LDC = C + 4;
+    static constexpr int B1 = (C * LDV > 2 * C * LDC) ? C * LDV : 2 * C * LDC;   // floats
+    static constexpr int B2 = (C * LDV > C * LDK) ? C * LDV : C * LDK;
+    static constexpr size_t offK = 0;
+    static constexpr size_t offB1 = offK + sizeof(float) * C * LDK;
+    static constexpr size_t offB2 = offB1 + sizeof(float) * B1;
+    static constexpr size_t offGam = offB2 + sizeof(float) * B2;
+    static constexpr size_t offN = offGam + sizeof(float) * C * LDC;
+    static constexpr size_t offD = offN + sizeof(float) * C * LDC;
+    // alpha, lambda, beta, dlambda [C] and two [NW][C] tables of per-wave
+    // partial sums of dalpha (summed in a fixed order: deterministic)
+    static constexpr size_t offVec = offD + sizeof(float) * C * LDC;
+    static constexpr size_t bytes = offVec + sizeof(float) * (4 + 2 * NW) * C;
+};
+
+// Sum over the 16 lanes of a lane group (one acc-tile row).
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
+    x += __shfl_xor(x, 4, 64);
+    x += __shfl_xor(x, 8, 64);
+    return x;
+}
+
+template <typename T, int DK, int DV, int C>
+__global__ __launch_bounds__(512) void grad_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const T *__restrict__ dout, const float *__restrict__ beta, const float *__restrict__ alpha,
+    const float *__restrict__ lambda, const float *__restrict__ states,
+    const float *__restrict__ dSout, const float *__restrict__ dE, T *__restrict__ dq,
+    T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ dbeta, int L, int nchunks,
+    int euler)
+{
+    using Lay = GradLayout<DK, DV, C>;
+    constexpr int NW = Lay::NW, NT = 64 * NW, MC = C / 16, MK = DK / 16, MV = DV / 16;
+    constexpr int LDK = Lay::LDK, LDV = Lay::LDV, LDC = Lay::LDC;
+    constexpr int TPW = (MC * MC + NW - 1) / NW;   // C x C tiles per wave
+    static_assert(MC <= 4 && NW == 8, "a wave's C x C tiles t, t + NW lie in distinct block rows");
+    extern __shared__ __align__(16) char smem[];
+    float *sK = reinterpret_cast<float *>(smem + Lay::offK);
+    float *sB1 = reinterpret_cast<float *>(smem + Lay::offB1);
+    float *sB2 = reinterpret_cast<float *>(smem + Lay::offB2);
+    float *sGam = reinterpret_cast<float *>(smem + Lay::offGam);
+    float *sN = reinterpret_cast<float *>(smem + Lay::offN);
+    float *sD = reinterpret_cast<float *>(smem + Lay::offD);
+    float *sAl = reinterpret_cast<float *>(smem + Lay::offVec);
+    float *sLam = sAl + C, *sBeta = sAl + 2 * C, *sDl = sAl + 3 * C;
+    float *sPT = sAl + 4 * C, *sPG = sPT + NW * C;   // [NW][C] partials of dalpha
+    float *sdA = sB1, *sZ = sB1 + C * LDC;   // C x C views of B1 once E is dead
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
+    const int bh = blockIdx.x / nchunks, c = blockIdx.x - bh * nchunks;
+    const long tok0 = (long)bh * L + (long)c * C;
+    const int valid = min(C, L - c * C);
+    const float *Sst = states + ((long)bh * nchunks + c) * DK * DV;
+    const float *dSo = dSout + ((long)bh * nchunks + c) * DK * DV;
+    const float *dEg = dE + ((long)bh * nchunks * C + (long)c * C) * DV;
+
+    // ---- K, per-token scalars; Gamma and N --------------------------------
+    for (int e = tid; e < C * DK; e += NT) {
+        const int row = e / DK, cc = e - row * DK;
+        sK[row * LDK + cc] = row < valid ? to_f32(k[(tok0 + row) * DK + cc]) : 0.f;
+    }
+    for (int e = tid; e < C * LDC; e += NT) sN[e] = 0.f;
+    if (tid < C) {
+        const bool ok = tid < valid;
+        sAl[tid] = ok ? alpha[tok0 + tid] : 0.f;
+        sLam[tid] = ok ? lambda[tok0 + tid] : 0.f;
+        sBeta[tid] = ok ? beta[tok0 + tid] : 0.f;
+    }
+    for (int e = tid; e < 2 * NW * C; e += NT) sPT[e] = 0.f;
+    __syncthreads();
+    for (int t = wv; t < MC * MC; t += NW) {
+        const int it = t / MC, jt = t - it * MC;
+        if (jt > it) continue;
+        const f32x4 acc = mm_lds<float, DK, false, false>(zero4(), sK, LDK, 16 * it, sK, LDK, 16 * jt);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sGam[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = acc[r];
+    }
+    __syncthreads();
+    // diagonal 16x16 blocks: N_ij = delta_ij - alpha_i sum_{m<i} Gamma_im N_mj
+    if (wv == 0 && g < MC) {
+        const int b0 = 16 * g, j = l16;
+        float n[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float acc = 0.f;
+            const float *grow = sGam + (b0 + i) * LDC + b0;
+#pragma unroll
+            for (int m = 0; m < i; ++m) acc = fmaf(grow[m], n[m], acc);
+            n[i] = (i == j ? 1.f : 0.f) - sAl[b0 + i] * acc;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sN[(b0 + i) * LDC + b0 + j] = n[i];
+    }
+    __syncthreads();
+    // blocks below: N_IJ = -N_II D_I sum_{M=J}^{I-1} Gamma_IM N_MJ, by block distance
+    for (int dist = 1; dist < MC; ++dist) {
+        if (wv < MC - dist) {
+            const int bi = dist + wv, bj = wv;
+            f32x4 p = zero4();
+            for (int m = bj; m < bi; ++m) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const float a = sGam[(16 * bi + l16) * LDC + 16 * m + 4 * s + g];
+                    const float b = sN[(16 * m + 4 * s + g) * LDC + 16 * bj + l16];
+                    p = mma(a, b, p);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] *= sAl[16 * bi + 4 * g + r];
+            f32x4 x = zero4();
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float a = sN[(16 * bi + l16) * LDC + 16 * bi + 4 * g + r];
+                x = mma(a, p[r], x);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sN[(16 * bi + 4 * g + r) * LDC + 16 * bj + l16] = -x[r];
+        }
+        __syncthreads();
+    }
+
+    // ---- per d_v column tile (wave wv owns columns 16wv .. 16wv+15) ----------
+    f32x4 E[MC], dX[MC];
+    if (wv < MV) {
+        const int col = 16 * wv + l16;
+        f32x4 S[MK], X[MC], DXv[MC], dEc[MC], Y[MC];
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[mk][r] = Sst[(16 * mk + 4 * g + r) * DV + col];
+#pragma unroll
+        for (int mt = 0; mt < MC; ++mt) {
+            X[mt] = zero4();
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * mt + 4 * g + r;
+                dEc[mt][r] = row < valid ? dEg[row * DV + col] : 0.f;
+            }
+        }
+        mm_acc_b<float, MC, MK, false, false>(X, sK, LDK, S);   // K S
+#pragma unroll
+        for (int mt = 0; mt < MC; ++mt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * mt + 4 * g + r;
+                const float vv = row < valid ? to_f32(v[(tok0 + row) * DV + col]) : 0.f;
+                X[mt][r] = vv - X[mt][r];
+                DXv[mt][r] = sAl[row] * X[mt][r];
+            }
+            E[mt] = zero4();
+            Y[mt] = zero4();
+        }
+        mm_acc_b<float, MC, MC, true, false>(E, sN, LDC, DXv);   // E = N (D X)
+        mm_acc_b<float, MC, MC, false, true>(Y, sN, LDC, dEc);   // Y = N^T dE
+#pragma unroll
+        for (int mt = 0; mt < MC; ++mt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * mt + 4 * g + r;
+                dX[mt][r] = sAl[row] * Y[mt][r];
+                if (row < valid) dv[(tok0 + row) * DV + col] = from_f32<T>(dX[mt][r]);
+                const float part = row16_sum(X[mt][r] * Y[mt][r]);
+                if (l16 == 0) sPT[wv * C + row] = part;
+                sB1[row * LDV + col] = DXv[mt][r];
+                sB2[row * LDV + col] = dEc[mt][r];
+            }
+        }
+    }
+    __syncthreads();
+    // dN = dE (D X)^T on and below the diagonal blocks (zero above)
+    for (int t = wv; t < MC * MC; t += NW) {
+        const int it = t / MC, jt = t - it * MC;
+        f32x4 acc = zero4();
+        if (jt <= it) acc = mm_lds<float, DV, false, false>(zero4(), sB2, LDV, 16 * it, sB1, LDV, 16 * jt);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sD[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = acc[r];
+    }
+    __syncthreads();
+    if (wv < MV) {
+        const int col = 16 * wv + l16;
+#pragma unroll
+        for (int mt = 0; mt < MC; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * mt + 4 * g + r;
+                sB1[row * LDV + col] = E[mt][r];
+                sB2[row * LDV + col] = dX[mt][r];
+            }
+    }
+    __syncthreads();
+
+    // ---- per d_k column tile (wave wv owns output columns 16wv .. 16wv+15) ---
+    f32x4 dQw[MC], dKw[MC], SinT[MV];
+#pragma unroll
+    for (int mt = 0; mt < MC; ++mt) {
+        dQw[mt] = zero4();
+        dKw[mt] = zero4();
+    }
+    if (wv < MK) {
+        const int a = 16 * wv + l16;
+        f32x4 dSoT[MV], t1[MC];
+#pragma unroll
+        for (int kt = 0; kt < MV; ++kt) {   // B operand (k = d_v index, j = d_k index a)
+            SinT[kt] = *reinterpret_cast<const f32x4 *>(Sst + a * DV + 16 * kt + 4 * g);
+            dSoT[kt] = *reinterpret_cast<const f32x4 *>(dSo + a * DV + 16 * kt + 4 * g);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MC; ++mt) t1[mt] = zero4();
+        mm_acc_b<float, MC, MV, false, false>(t1, sB2, LDV, SinT);   // dX S^T
+        mm_acc_b<float, MC, MV, false, false>(dKw, sB1, LDV, dSoT);  // E dS_out^T
+#pragma unroll
+        for (int mt = 0; mt < MC; ++mt) dKw[mt] -= t1[mt];
+    }
+    __syncthreads();
+    for (int e = tid; e < C * DV; e += NT) {
+        const int row = e / DV, cc = e - row * DV;
+        sB2[row * LDV + cc] = row < valid ? to_f32(dout[(tok0 + row) * DV + cc]) : 0.f;
+    }
+    __syncthreads();
+    if (wv < MK) mm_acc_b<float, MC, MV, false, false>(dQw, sB2, LDV, SinT);   // dO S^T
+    // dA = tril(dO E^T), diagonal included
+    f32x4 dAr[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int t = wv + u * NW;
+        const int it = t / MC, jt = t - it * MC;
+        dAr[u] = zero4();
+        if (t < MC * MC && jt <= it) {
+            dAr[u] = mm_lds<float, DV, false, false>(zero4(), sB2, LDV, 16 * it, sB1, LDV, 16 * jt);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (16 * jt + l16 > 16 * it + 4 * g + r) dAr[u][r] = 0.f;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int t = wv + u * NW;
+        if (t < MC * MC) {
+            const int it = t / MC, jt = t - it * MC;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sdA[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = dAr[u][r];
+        }
+    }
+    for (int e = tid; e < C * DK; e += NT) {   // Q into B2
+        const int row = e / DK, cc = e - row * DK;
+        sB2[row * LDK + cc] = row < valid ? to_f32(q[(tok0 + row) * DK + cc]) : 0.f;
+    }
+    // Z = N^T dN
+    for (int t = wv; t < MC * MC; t += NW) {
+        const int it = t / MC, jt = t - it * MC;
+        const f32x4 acc = mm_lds<float, C, true, true>(zero4(), sN, LDC, 16 * it, sD, LDC, 16 * jt);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sZ[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = acc[r];
+    }
+    __syncthreads();
+    if (wv < MK) {
+#pragma unroll
+        for (int mt = 0; mt < MC; ++mt) {
+            // dq += dA K;  dk += dA^T Q
+            dQw[mt] = mm_lds<float, C, false, true>(dQw[mt], sdA, LDC, 16 * mt, sK, LDK, 16 * wv,
+                                                    16 * mt + 16);
+            dKw[mt] = mm_lds<float, C, true, true>(dKw[mt], sdA, LDC, 16 * mt, sB2, LDK, 16 * wv);
+        }
+    }
+    // dG = -strictly_lower(Z N^T); dalpha_i += sum_j dG_ij Gamma_ij; dGam = D dG
+    f32x4 dGr[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int t = wv + u * NW;
+        const int it = t / MC, jt = t - it * MC;
+        dGr[u] = zero4();
+        if (t < MC * MC && jt <= it) {
+            const f32x4 acc = mm_lds<float, C, false, false>(zero4(), sZ, LDC, 16 * it, sN, LDC, 16 * jt);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * it + 4 * g + r, cl = 16 * jt + l16;
+                const float dg = cl < row ? -acc[r] : 0.f;
+                // one tile per row block per wave (t and t + NW lie >= 2 block rows apart)
+                const float part = row16_sum(dg * sGam[row * LDC + cl]);
+                if (l16 == 0) sPG[wv * C + row] = part;
+                dGr[u][r] = sAl[row] * dg;
+            }
+        }
+    }
+    __syncthreads();   // every read of dN (Z) and of dA, Q above is done
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int t = wv + u * NW;
+        if (t < MC * MC) {
+            const int it = t / MC, jt = t - it * MC;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sD[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = dGr[u][r];
+        }
+    }
+    __syncthreads();
+    if (tid < C) {
+        float da_db, da_dl;
+        alpha_partials(euler, sBeta[tid], sLam[tid], da_db, da_dl);
+        float da = 0.f;
+        for (int w = 0; w < NW; ++w) da += sPT[w * C + tid];
+        for (int w = 0; w < NW; ++w) da += sPG[w * C + tid];
+        if (tid < valid) dbeta[tok0 + tid] = da * da_db;
+        sDl[tid] = da * da_dl;
+    }
+    if (wv < MK) {
+#pragma unroll
+        for (int mt = 0; mt < MC; ++mt) {
+            // dk += dGam K + dGam^T K
+            dKw[mt] = mm_lds<float, C, false, true>(dKw[mt], sD, LDC, 16 * mt, sK, LDK, 16 * wv,
+                                                    16 * mt + 16);
+            dKw[mt] = mm_lds<float, C, true, true>(dKw[mt], sD, LDC, 16 * mt, sK, LDK, 16 * wv);
+        }
+    }
+    __syncthreads();
+    if (wv < MK) {
+        const int a = 16 * wv + l16;
+#pragma unroll
+        for (int mt = 0; mt < MC; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * mt + 4 * g + r;
+                if (row < valid) {
+                    const float kk = 2.f * sDl[row] * sK[row * LDK + a];
+                    dq[(tok0 + row) * DK + a] = from_f32<T>(dQw[mt][r]);
+                    dk[(tok0 + row) * DK + a] = from_f32<T>(dKw[mt][r] + kk);
+                }
+            }
+    }
+}
+
+template <typename T, int DK, int DV, int C>
+hipError_t launch_grad(const void *q, const void *k, const void *v, const void *dout,
+                       const float *beta, const float *alpha, const float *lambda,
+                       const float *states, const float *dSout, const float *dE, void *dq,
+                       void *dk, void *dv, float *dbeta, int BH, int L, bool euler, hipStream_t st)
+{
+    using Lay = GradLayout<DK, DV, C>;
+    static_assert(Lay::bytes <= 160 * 1024, "gradient kernel LDS");
+    const int nchunks = (L + C - 1) / C;
+    if (BH == 0 || nchunks == 0) return hipSuccess;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&grad_kernel<T, DK, DV, C>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((grad_kernel<T, DK, DV, C>), dim3((unsigned)(BH * nchunks)), dim3(64 * Lay::NW),
+                       Lay::bytes, st, static_cast<const T *>(q), static_cast<const T *>(k),
+                       static_cast<const T *>(v), static_cast<const T *>(dout), beta, alpha, lambda,
+                       states, dSout, dE, static_cast<T *>(dq), static_cast<T *>(dk),
+                       static_cast<T *>(dv), dbeta, L, nchunks, (int)euler);
+    return hipGetLastError();
+}
+
+hipError_t dispatch_grad(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
+                         const void *v, const void *dout, const float *beta, const float *alpha,
+                         const float *lambda, const float *states, const float *dSout,
+                         const float *dE, void *dq, void *dkp, void *dvp, float *dbeta, int BH,
+                         int L, bool euler, hipStream_t st)
+{
+#define CASE(DKV, DVV, CC)                                                                      \
+    if (dk == DKV && dv == DVV && chunk == CC)                                                  \
+        return bf16 ? launch_grad<__bf16, DKV, DVV, CC>(q, k, v, dout, beta, alpha, lambda,     \
+                                                        states, dSout, dE, dq, dkp, dvp, dbeta, \
+                                                        BH, L, euler, st)                       \
+                    : launch_grad<float, DKV, DVV, CC>(q, k, v, dout, beta, alpha, lambda,      \
+                                                       states, dSout, dE, dq, dkp, dvp, dbeta,  \
+                                                       BH, L, euler, st);
+    EFLA_SHAPE_CASES(CASE)
+#undef CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace efla

@@ -37,6 +37,7 @@ struct SegArgs {
     float *R;          // SUMMARY: [BH, G, DK, DV]
     float *P;          // SUMMARY: [BH, G, DK, DK]
     const float *Sin;  // REPLAY: [BH, G, DK, DV]
+    float *states;     // WHOLE, optional: the entry state of every chunk [BH, nchunks, DK, DV]
 };
 
 template <typename T, int DK, int DV, int C, int NW>
@@ -152,6 +153,14 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
         }
         __syncthreads();
 
+        if (sg.states) {
+            float *st = sg.states + ((long)bh * nchunks + c) * DK * DV;
+#pragma unroll
+            for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[(16 * mk + 4 * g + r) * DV + col] = S[mk][r];
+        }
+
         // E = U - W S
         f32x4 E[MC];
 #pragma unroll
@@ -164,7 +173,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
                 E[mt][r] = (ptile ? 0.f : to_f32(sU[(16 * mt + 4 * g + r) * Lay::LDU + 16 * wv + l16])) -
                            E[mt][r];
 
-        if (sg.mode != SCAN_SUMMARY) {   // a segment's map needs no output
+        if (sg.mode != SCAN_SUMMARY && o) {   // a segment's map needs no output
             // O = Q S + A E
             f32x4 O[MC];
 #pragma unroll
@@ -185,6 +194,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
         mm_acc_b<T, MK, MC, false, true>(S, sK, Lay::LDK, E);
     }
 
+    if (sg.mode == SCAN_WHOLE && !SL) return;
     float *dst = SL + sbase;
     int ld = DV;
     if (sg.mode == SCAN_SUMMARY) {
@@ -289,22 +299,204 @@ hipError_t launch_scan_segmented(const void *q, const void *k, const void *w, co
                                  int nw, hipStream_t st)
 {
     if (BH == 0) return hipSuccess;
-    SegArgs sum{SCAN_SUMMARY, G, seg_chunks, R, P, nullptr};
+    SegArgs sum{SCAN_SUMMARY, G, seg_chunks, R, P, nullptr, nullptr};
     hipError_t e = launch_scan_auto<T, DK, DV, C>(q, k, w, u, aqk, nullptr, o, SL, BH, L, nw, sum, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((seg_combine_kernel<DK, DV>), dim3((unsigned)(BH * (DV / 16))), dim3(256), 0,
                        st, S0, P, R, Sin, G);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    SegArgs rep{SCAN_REPLAY, G, seg_chunks, nullptr, nullptr, Sin};
+    SegArgs rep{SCAN_REPLAY, G, seg_chunks, nullptr, nullptr, Sin, nullptr};
     return launch_scan_auto<T, DK, DV, C>(q, k, w, u, aqk, nullptr, o, SL, BH, L, nw, rep, st);
+}
+
+// ---------------------------------------------------------------------------
+// Reverse state scan of the backward pass.  The chunk map above,
+//   E = U - W S_in,  O = Q S_in + A E,  S_out = S_in + K^T E,
+// sends the gradient dS_out = dLoss/dS_out back through the chunk as
+//   dE    = A^T dO + K dS_out                   (the chunk's dLoss/dE)
+//   dS_in = dS_out + Q^T dO - W^T dE            (W^T dE = K^T T^T dE)
+// which, like the forward, never mixes the d_v columns: a workgroup owns a
+// (sequence, column tile), walks the chunks from last to first with dS in
+// MFMA accumulators, and stores every chunk's dS_out and dE (fp32) for the
+// per-chunk gradient kernel.  dS0 receives dLoss/dS0.
+template <typename T, int DK, int DV, int C, int NW>
+__global__ __launch_bounds__(64 * NW) void rscan_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ w,
+    const T *__restrict__ aqk, const T *__restrict__ dout, const float *__restrict__ dSL,
+    float *__restrict__ dSout, float *__restrict__ dE, float *__restrict__ dS0, int L, int nchunks)
+{
+    using Lay = ScanLayout<T, DK, DV, C, NW>;
+    constexpr int TV = Lay::TV, NTILE = DV / TV, MC = C / 16, MK = DK / 16;
+    constexpr int NT = 64 * NW;
+    extern __shared__ __align__(16) char smem[];
+    T *sW = reinterpret_cast<T *>(smem + Lay::offW);
+    T *sQ = reinterpret_cast<T *>(smem + Lay::offQ);
+    T *sK = reinterpret_cast<T *>(smem + Lay::offK);
+    T *sA = reinterpret_cast<T *>(smem + Lay::offA);
+    T *sO = reinterpret_cast<T *>(smem + Lay::offU);   // the dO column tile
+
+    int bh, tile;
+    xcd_map(blockIdx.x, gridDim.x, NTILE, bh, tile);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
+    const int col = tile * TV + 16 * wv + l16;
+    const long sbase = (long)bh * DK * DV;
+
+    f32x4 dS[MK];
+    if (dSL) {
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dS[mk][r] = dSL[sbase + (16 * mk + 4 * g + r) * DV + col];
+    } else {
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk) dS[mk] = zero4();
+    }
+
+    // As in the forward scan: the previous chunk's tiles are loaded while
+    // this one is computed, unless they would not fit in registers.
+    using RW = TileRegs<T, C, DK, NT>;
+    using RU = TileRegs<T, C, TV, NT>;
+    using RA = TileRegs<T, C, C, NT>;
+    constexpr bool PREFETCH = 3 * RW::PER + RU::PER + RA::PER <= 40;
+    RW rW, rQ, rK;
+    RU rO;
+    RA rA;
+    auto load_all = [&](int cn) {   // chunk cn's tiles (cn < 0 re-loads chunk 0, never stored)
+        cn = max(cn, 0);
+        const long t0 = (long)bh * L + (long)cn * C;
+        const int vn = min(C, L - cn * C);
+        rW.load(w + t0 * DK, DK, vn);
+        rQ.load(q + t0 * DK, DK, vn);
+        rK.load(k + t0 * DK, DK, vn);
+        rO.load(dout + t0 * DV + tile * TV, DV, vn);
+        rA.load(aqk + ((long)bh * nchunks + cn) * C * C, C, C);
+    };
+    if constexpr (PREFETCH) {
+        if (nchunks > 0) load_all(nchunks - 1);
+    }
+
+    for (int c = nchunks - 1; c >= 0; --c) {
+        const int valid = min(C, L - c * C);
+        const long tok0 = (long)bh * L + (long)c * C;
+        __syncthreads();   // the previous chunk is done with LDS
+        if constexpr (PREFETCH) {
+            rW.store(sW, Lay::LDK, valid);
+            rQ.store(sQ, Lay::LDK, valid);
+            rK.store(sK, Lay::LDK, valid);
+            rO.store(sO, Lay::LDU, valid);
+            rA.store(sA, Lay::LDC, C);
+            load_all(c - 1);
+        } else {
+            RW t;
+            t.load(w + tok0 * DK, DK, valid);
+            t.store(sW, Lay::LDK, valid);
+            t.load(q + tok0 * DK, DK, valid);
+            t.store(sQ, Lay::LDK, valid);
+            t.load(k + tok0 * DK, DK, valid);
+            t.store(sK, Lay::LDK, valid);
+            rO.load(dout + tok0 * DV + tile * TV, DV, valid);
+            rO.store(sO, Lay::LDU, valid);
+            rA.load(aqk + ((long)bh * nchunks + c) * C * C, C, C);
+            rA.store(sA, Lay::LDC, C);
+        }
+        __syncthreads();
+
+        float *so = dSout + ((long)bh * nchunks + c) * DK * DV;
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) so[(16 * mk + 4 * g + r) * DV + col] = dS[mk][r];
+
+        f32x4 dO[MC], dEc[MC];
+#pragma unroll
+        for (int mt = 0; mt < MC; ++mt) {
+            dEc[mt] = zero4();
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dO[mt][r] = to_f32(sO[(16 * mt + 4 * g + r) * Lay::LDU + 16 * wv + l16]);
+        }
+        // dE = K dS_out + A^T dO   (A^T: element (i, m) = A[m][i]; A is zero above its diagonal)
+        mm_acc_b<T, MC, MK, false, false>(dEc, sK, Lay::LDK, dS);
+        mm_acc_b<T, MC, MC, false, true>(dEc, sA, Lay::LDC, dO);
+        float *de = dE + ((long)bh * nchunks * C + (long)c * C) * DV;
+#pragma unroll
+        for (int mt = 0; mt < MC; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) de[(16 * mt + 4 * g + r) * DV + col] = dEc[mt][r];
+
+        // dS <- dS + Q^T dO - W^T dE
+        mm_acc_b<T, MK, MC, false, true>(dS, sQ, Lay::LDK, dO);
+#pragma unroll
+        for (int mt = 0; mt < MC; ++mt) dEc[mt] = -dEc[mt];
+        mm_acc_b<T, MK, MC, false, true>(dS, sW, Lay::LDK, dEc);
+    }
+
+    if (dS0) {
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dS0[sbase + (16 * mk + 4 * g + r) * DV + col] = dS[mk][r];
+    }
+}
+
+template <typename T, int DK, int DV, int C>
+hipError_t launch_rscan(const void *q, const void *k, const void *w, const void *aqk,
+                        const void *dout, const float *dSL, float *dSout, float *dE, float *dS0,
+                        int BH, int L, hipStream_t st)
+{
+    constexpr int NW = DV >= 64 ? 4 : DV / 16;
+    using Lay = ScanLayout<T, DK, DV, C, NW>;
+    const int nchunks = (L + C - 1) / C;
+    if (BH == 0) return hipSuccess;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&rscan_kernel<T, DK, DV, C, NW>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((rscan_kernel<T, DK, DV, C, NW>), dim3((unsigned)(BH * (DV / Lay::TV))),
+                       dim3(64 * NW), Lay::bytes, st, static_cast<const T *>(q),
+                       static_cast<const T *>(k), static_cast<const T *>(w),
+                       static_cast<const T *>(aqk), static_cast<const T *>(dout), dSL, dSout, dE,
+                       dS0, L, nchunks);
+    return hipGetLastError();
+}
+
+hipError_t dispatch_rscan(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
+                          const void *w, const void *aqk, const void *dout, const float *dSL,
+                          float *dSout, float *dE, float *dS0, int BH, int L, hipStream_t st)
+{
+#define CASE(DKV, DVV, CC)                                                                      \
+    if (dk == DKV && dv == DVV && chunk == CC)                                                  \
+        return bf16 ? launch_rscan<__bf16, DKV, DVV, CC>(q, k, w, aqk, dout, dSL, dSout, dE,    \
+                                                         dS0, BH, L, st)                        \
+                    : launch_rscan<float, DKV, DVV, CC>(q, k, w, aqk, dout, dSL, dSout, dE,     \
+                                                        dS0, BH, L, st);
+    EFLA_SHAPE_CASES(CASE)
+#undef CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t dispatch_scan_states(bool bf16, int dk, int dv, int chunk, const void *q,
+                                const void *k, const void *w, const void *u, const void *aqk,
+                                const float *S0, float *states, int BH, int L, hipStream_t st)
+{
+    const SegArgs whole{SCAN_WHOLE, 1, 1 << 30, nullptr, nullptr, nullptr, states};
+#define CASE(DKV, DVV, CC)                                                                      \
+    if (dk == DKV && dv == DVV && chunk == CC)                                                  \
+        return bf16 ? launch_scan_auto<__bf16, DKV, DVV, CC>(q, k, w, u, aqk, S0, nullptr,      \
+                                                             nullptr, BH, L, 0, whole, st)      \
+                    : launch_scan_auto<float, DKV, DVV, CC>(q, k, w, u, aqk, S0, nullptr,       \
+                                                            nullptr, BH, L, 0, whole, st);
+    EFLA_SHAPE_CASES(CASE)
+#undef CASE
+    return hipErrorInvalidValue;
 }
 
 hipError_t dispatch_scan(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                          const void *w, const void *u, const void *aqk, const float *S0, void *o,
                          float *SL, int BH, int L, int nw, hipStream_t st)
 {
-    const SegArgs whole{SCAN_WHOLE, 1, 1 << 30, nullptr, nullptr, nullptr};
+    const SegArgs whole{SCAN_WHOLE, 1, 1 << 30, nullptr, nullptr, nullptr, nullptr};
 #define CASE(DKV, DVV, CC)                                                                      \
     if (dk == DKV && dv == DVV && chunk == CC)                                                  \
         return bf16 ? launch_scan_auto<__bf16, DKV, DVV, CC>(q, k, w, u, aqk, S0, o, SL, BH, L, \

@@ -81,6 +81,29 @@ StagedWs staged_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t 
     return s;
 }
 
+// Backward workspace: the forward's coefficient and UT-transform outputs,
+// plus every chunk's entry state, dS_out and dE (fp32).
+struct BackwardWs {
+    size_t alpha, lambda, w, u, aqk, states, dSout, dE, total;
+};
+
+BackwardWs backward_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t dt)
+{
+    const size_t n = (size_t)B * H * L;
+    const size_t nch = (size_t)B * H * ((L + chunk - 1) / chunk);
+    BackwardWs s;
+    s.alpha = 0;
+    s.lambda = s.alpha + align_up(n * sizeof(float));
+    s.w = s.lambda + align_up(n * sizeof(float));
+    s.u = s.w + align_up(n * dk * esize(dt));
+    s.aqk = s.u + align_up(n * dv * esize(dt));
+    s.states = s.aqk + align_up(nch * chunk * chunk * esize(dt));
+    s.dSout = s.states + align_up(nch * dk * dv * sizeof(float));
+    s.dE = s.dSout + align_up(nch * dk * dv * sizeof(float));
+    s.total = s.dE + align_up(nch * chunk * dv * sizeof(float));
+    return s;
+}
+
 // AUTO: the fused kernel where it exists (bf16 inputs); else the segmented
 // scan when it has more than one segment per sequence, else the staged one.
 efla_path_t resolve_path(efla_path_t p, efla_dtype_t dt, int B, int H, int L, int dk, int dv,
@@ -327,6 +350,66 @@ efla_status_t efla_chunk_scan(const void *q, const void *k, const void *w, const
         return EFLA_ERR_INVALID_ARG;
     return hip_status(efla::dispatch_scan(dt == EFLA_BF16, dk, dv, chunk, q, k, w, u, a_qk, S0, o,
                                           S_L, (int)BH, L, scan_waves_override(), st));
+}
+
+size_t efla_backward_workspace_size(int B, int H, int L, int dk, int dv, int chunk,
+                                    efla_dtype_t dt)
+{
+    if (check_shape(B, H, L, dk, dv, chunk, dt) != EFLA_OK) return 0;
+    if (L == 0 || (long long)B * H == 0) return 0;
+    return backward_ws(B, H, L, dk, dv, chunk, dt).total;
+}
+
+efla_status_t efla_backward(const void *q, const void *k, const void *v, const float *beta,
+                            const float *S0, const void *d_o, const float *dS_L, void *dq,
+                            void *dk_out, void *dv_out, float *dbeta, float *dS0, int B, int H,
+                            int L, int dk, int dv, int chunk, efla_dtype_t dt,
+                            efla_update_t update, void *workspace, size_t workspace_bytes,
+                            void *stream)
+{
+    efla_status_t s = check_shape(B, H, L, dk, dv, chunk, dt);
+    if (s != EFLA_OK) return s;
+    if (update != EFLA_EXACT && update != EFLA_EULER) return EFLA_ERR_INVALID_ARG;
+    const bool euler = update == EFLA_EULER;
+    const long long BH = (long long)B * H;
+    if (BH == 0) return EFLA_OK;
+    if ((S0 && !aligned16(S0)) || (dS_L && !aligned16(dS_L)) || (dS0 && !aligned16(dS0)))
+        return EFLA_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (L == 0) {   // S_L = S0: dLoss/dS0 = dS_L
+        if (!dS0) return EFLA_OK;
+        return hip_status(efla::launch_copy_state(dS_L, dS0, BH * dk * dv, st));
+    }
+    if (!q || !k || !v || !beta || !d_o || !dq || !dk_out || !dv_out || !dbeta)
+        return EFLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(d_o) ||
+        !aligned16(dq) || !aligned16(dk_out) || !aligned16(dv_out) || !aligned16(dbeta))
+        return EFLA_ERR_INVALID_ARG;
+    const BackwardWs ws = backward_ws(B, H, L, dk, dv, chunk, dt);
+    if (!workspace || workspace_bytes < ws.total) return EFLA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return EFLA_ERR_INVALID_ARG;
+
+    const bool bf = dt == EFLA_BF16;
+    char *base = static_cast<char *>(workspace);
+    float *alpha = reinterpret_cast<float *>(base + ws.alpha);
+    float *lambda = reinterpret_cast<float *>(base + ws.lambda);
+    void *w = base + ws.w, *u = base + ws.u, *aqk = base + ws.aqk;
+    float *states = reinterpret_cast<float *>(base + ws.states);
+    float *dSout = reinterpret_cast<float *>(base + ws.dSout);
+    float *dE = reinterpret_cast<float *>(base + ws.dE);
+    hipError_t e = efla::dispatch_coef(bf, dk, k, beta, alpha, lambda, BH * L, euler, st);
+    if (e == hipSuccess)
+        e = efla::dispatch_ut(bf, dk, dv, chunk, q, k, v, alpha, w, u, aqk, (int)BH, L, st);
+    if (e == hipSuccess)
+        e = efla::dispatch_scan_states(bf, dk, dv, chunk, q, k, w, u, aqk, S0, states, (int)BH, L,
+                                       st);
+    if (e == hipSuccess)
+        e = efla::dispatch_rscan(bf, dk, dv, chunk, q, k, w, aqk, d_o, dS_L, dSout, dE, dS0,
+                                 (int)BH, L, st);
+    if (e == hipSuccess)
+        e = efla::dispatch_grad(bf, dk, dv, chunk, q, k, v, d_o, beta, alpha, lambda, states,
+                                dSout, dE, dq, dk_out, dv_out, dbeta, (int)BH, L, euler, st);
+    return hip_status(e);
 }
 
 }  // extern "C"

@@ -48,6 +48,7 @@ __all__ = [
     "decode_tokens",
     "varlen_lengths",
     "varlen_inputs",
+    "output_grads",
 ]
 
 
@@ -223,3 +224,17 @@ def varlen_inputs(w: ForwardWorkload, lengths, seed: int = 0):
         rng = np.random.default_rng([seed, 1])
         S0n = torch.from_numpy(_normal(rng, (len(lengths), w.H, w.d_k, w.d_v), 0.02))
     return q[0], k[0], v[0], beta[0], cu, S0n
+
+
+def output_grads(w: ForwardWorkload, seed: int = 0, with_dS_L: bool = True):
+    """Upstream gradients for a backward pass: (dO, dS_L) as CPU tensors.
+
+    dO [B,H,L,d_v] ~ N(0,1)/sqrt(L) in the storage dtype (a loss averaged
+    over tokens); dS_L [B,H,d_k,d_v] fp32 ~ N(0, std 0.02), or None.
+    Drawn from their own stream (seed, 1), independent of the inputs.
+    """
+    rng = np.random.default_rng([seed, 1])
+    B, H, L, dk, dv = w.B, w.H, w.L, w.d_k, w.d_v
+    dO = _normal(rng, (B, H, L, dv), 1.0 / math.sqrt(max(L, 1)))
+    dSL = _normal(rng, (B, H, dk, dv), 0.02) if with_dS_L else None
+    return _store(dO, w.dtype), None if dSL is None else torch.from_numpy(np.ascontiguousarray(dSL))

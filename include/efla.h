@@ -211,6 +211,41 @@ efla_status_t efla_chunk_scan(const void *q, const void *k, const void *w, const
                               int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype_t dt,
                               void *stream);
 
+/*
+ * Backward pass of the chunked forward: the gradients of a scalar loss with
+ * respect to every input, given its gradients with respect to the outputs.
+ * The pages train models with the exact-flow layer (Experiments) but print
+ * no backward; this is the adjoint of the forward defined above, evaluated
+ * chunkwise.
+ *   q, k, v, beta, S0  the forward's inputs, as for efla_forward (S0 NULL =
+ *                      zero initial state)
+ *   d_o   [B,H,L,d_v]   dtype dt   dLoss/do
+ *   dS_L  [B,H,d_k,d_v] fp32       dLoss/dS_L, or NULL for zero
+ *   dq, dk [B,H,L,d_k], dv [B,H,L,d_v]  dtype dt, outputs
+ *   dbeta [B,H,L] fp32, output
+ *   dS0   [B,H,d_k,d_v] fp32 output (dLoss/dS0), or NULL if not wanted
+ *   update  EFLA_EXACT or EFLA_EULER: the update the forward used
+ *   workspace: at least efla_backward_workspace_size() bytes, 256-byte
+ *   aligned, owned by the caller (NULL allowed when that size is 0).
+ * dbeta uses d alpha / d beta = exp(-beta lambda) and dk includes the path
+ * through lambda = |k|^2 (d alpha / d lambda); for EFLA_EULER these are 1
+ * and 0.  The forward is recomputed inside (coefficients, UT transform and
+ * the state scan, which stores every chunk's entry state), then a reverse
+ * scan carries dLoss/dS from the last chunk to the first and a per-chunk
+ * kernel forms dq, dk, dv and dbeta; the per-chunk gradient arithmetic is
+ * fp32 for both dtypes.  No output may alias an input or another output.
+ * With L = 0 only dS0 = dS_L (or zeros) is written.
+ */
+size_t efla_backward_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk,
+                                    efla_dtype_t dt);
+
+efla_status_t efla_backward(const void *q, const void *k, const void *v, const float *beta,
+                            const float *S0, const void *d_o, const float *dS_L,
+                            void *dq, void *dk, void *dv, float *dbeta, float *dS0,
+                            int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype_t dt,
+                            efla_update_t update, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,7 +32,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 14
+    assert len(declared) == 16
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], check=True,
                          capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (efla_[a-z_]+)\b", out))
@@ -179,3 +179,44 @@ def test_auto_path_choice(lib):
     stg = _lib.efla_forward_workspace_size_ex(1, 16, 65536, 128, 128, 64, _lib.EFLA_F32,
                                               _lib.EFLA_PATH_STAGED)
     assert seg > stg > 0
+
+
+def test_backward_workspace_size(lib):
+    # alpha, lambda fp32; W, U, A (dtype); entry states, dS_out (fp32 per chunk); dE (fp32)
+    B, H, L, d, C = 4, 16, 4096, 128, 64
+    n, nch = B * H * L, B * H * (L // C)
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    want = (2 * up(n * 4) + 2 * up(n * d * 2) + up(nch * C * C * 2) + 2 * up(nch * d * d * 4) +
+            up(nch * C * d * 4))
+    assert _lib.efla_backward_workspace_size(B, H, L, d, d, C, _lib.EFLA_BF16) == want
+    assert _lib.efla_backward_workspace_size(1, 1, 0, 16, 16, 16, _lib.EFLA_F32) == 0
+    assert _lib.efla_backward_workspace_size(1, 1, 64, 48, 16, 16, _lib.EFLA_F32) == 0
+
+
+def _bwd(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, S0=None, d_o=FAKE, dS_L=None, dq=FAKE, dk_=FAKE,
+             dv_=FAKE, dbeta=FAKE, dS0=FAKE, B=1, H=1, L=64, dk=16, dv=16, chunk=16,
+             dt=_lib.EFLA_F32, update=_lib.EFLA_EXACT, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    return _lib.efla_backward(a["q"], a["k"], a["v"], a["beta"], a["S0"], a["d_o"], a["dS_L"],
+                              a["dq"], a["dk_"], a["dv_"], a["dbeta"], a["dS0"], a["B"], a["H"],
+                              a["L"], a["dk"], a["dv"], a["chunk"], a["dt"], a["update"], a["ws"],
+                              a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dt=7), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(update=2), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(L=-1), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(dk=48), _lib.EFLA_ERR_UNSUPPORTED),
+    (dict(chunk=128), _lib.EFLA_ERR_UNSUPPORTED),
+    (dict(d_o=None), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(dbeta=None), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(dq=MISALIGNED), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(dS_L=MISALIGNED), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(ws=None), _lib.EFLA_ERR_WORKSPACE),
+    (dict(ws_bytes=100), _lib.EFLA_ERR_WORKSPACE),
+    (dict(ws=FAKE + 16), _lib.EFLA_ERR_INVALID_ARG),
+])
+def test_backward_rejects_bad_arguments(lib, over, status):
+    assert _bwd(lib, **over) == status
