@@ -9,11 +9,13 @@ JSON line.  The decode step (256 sequences x 16 heads, d=128, fp32 state) is
 timed in the same run and reported under "decode".
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload lm1.3b-bf16]
-                  [--path auto|staged|fused] [--no-cpu-baseline] [--no-decode] [--no-compare]
+                  [--path auto|staged|fused|segmented] [--no-cpu-baseline] [--no-decode]
+                  [--no-compare] [--no-backward]
 
 The fused path is also timed with the Euler update (alpha = beta) and both
 kernel times are reported under "update_compare"; a packed (varlen) batch of
-the same token count is timed under "varlen".
+the same token count is timed under "varlen", and the backward pass (dq, dk,
+dv, dbeta, dS0 given dO and dS_L) of the same workload under "backward".
 """
 from __future__ import annotations
 
@@ -336,6 +338,74 @@ def bench_varlen(args, dev, n_seq=16):
             "note": "lm1.3b-bf16 recipe; random lengths; the longest sequence sets the time"}
 
 
+def backward_flops_per_token(dk, dv, C):
+    """The chunked backward as built, per token-head, including the forward
+    recompute it needs (masked halves of C x C products not counted):
+    state scan with stored states (W S, K^T E: 4 dk dv); UT transform
+    (3 C dk + C dv + C^2/3); reverse scan (K dS, Q^T dO, W^T dE: 6 dk dv,
+    A^T dO: C dv); gradient kernel (K S, dX S^T, E dS_out^T, dO S^T: 8 dk dv;
+    Gamma, dA K, dA^T Q, dGam K, dGam^T K: 5 C dk; N D X, N^T dE, dE (DX)^T,
+    dO E^T: 4 C dv; N, N^T dN, Z N^T: C^2)."""
+    return 18 * dk * dv + 8 * C * dk + 6 * C * dv + 4 * C * C / 3.0 + 2 * dk
+
+
+def grad_kernel_work(w, esz):
+    """(flops, bytes) per launch of the per-chunk gradient kernel."""
+    B, H, L, dk, dv, C = w.B, w.H, w.L, w.d_k, w.d_v, w.chunk
+    n = B * H * L
+    nch = B * H * ((L + C - 1) // C)
+    flops = (8 * dk * dv + 5 * C * dk + 4 * C * dv + C * C) * n
+    byts = (n * (2 * dk + 2 * dv) * esz + 12 * n + 2 * nch * dk * dv * 4 + nch * C * dv * 4 +
+            n * (2 * dk + dv) * esz + 4 * n)
+    return flops, byts
+
+
+def bench_backward(args, w, dev):
+    """One backward pass (dq, dk, dv, dbeta, dS0) of the workload, given dO
+    and dS_L; inputs, upstream gradients, outputs and workspace resident."""
+    q, k, v, beta, S0 = wl.forward_inputs(w, seed=0)
+    dO, dSL = wl.output_grads(w, seed=0)
+    qd, kd, vd, bd, s0d, dod, dsld = (None if x is None else x.to(dev)
+                                      for x in (q, k, v, beta, S0, dO, dSL))
+    dt = _lib.EFLA_BF16 if w.dtype == "bf16" else _lib.EFLA_F32
+    B, H, L, dk, dv, C = w.B, w.H, w.L, w.d_k, w.d_v, w.chunk
+    outs = [torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd),
+            torch.empty_like(bd), torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)]
+    need = _lib.efla_backward_workspace_size(B, H, L, dk, dv, C, dt)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    p = lambda x: None if x is None else x.data_ptr()  # noqa: E731
+
+    def step():
+        st = _lib.efla_backward(p(qd), p(kd), p(vd), p(bd), p(s0d), p(dod), p(dsld),
+                                *[p(o) for o in outs], B, H, L, dk, dv, C, dt, _lib.EFLA_EXACT,
+                                p(ws), need, sp)
+        if st:
+            raise RuntimeError(f"backward failed: {_lib.status_string(st)}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    n = B * H * L
+    fl = backward_flops_per_token(dk, dv, C) * n
+    gf, gb = grad_kernel_work(w, 2 if w.dtype == "bf16" else 4)
+    return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3),
+            "tflops": fl / (ms * 1e-3) / 1e12, "flops_per_token_head": fl / n,
+            "workspace_bytes": need,
+            "grad_kernel_algorithmic_flops": gf, "grad_kernel_algorithmic_bytes": gb,
+            "note": "five launches: coefficients, UT transform, state scan storing chunk entry "
+                    "states, reverse state scan, per-chunk gradients (fp32 MFMA); per-kernel "
+                    "times from rocprofv3"}
+
+
 def cpu_baseline(w, host):
     """The fp64 oracle on the host cores, timed on the whole workload."""
     import oracle
@@ -441,6 +511,7 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "staged", "fused", "segmented"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip timing the Euler variant of the fused kernel")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -474,6 +545,9 @@ def main():
     if not args.no_compare and w.dtype == "bf16":
         print("[bench] varlen", file=sys.stderr, flush=True)
         res["varlen"] = bench_varlen(args, dev)
+    if not args.no_backward:
+        print(f"[bench] backward {w.name}", file=sys.stderr, flush=True)
+        res["backward"] = bench_backward(args, w, dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, host)
