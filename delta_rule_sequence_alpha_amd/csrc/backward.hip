@@ -7,7 +7,8 @@
 //   Gamma = K K^T,  N = (I + D strictly_lower(Gamma))^{-1},  T = N D
 //   X = V - K S         (the residuals v_t - S_{t-1}^T k_t, stacked)
 //   E = T X,  O = Q S + (tril(Q K^T)) E,  S_out = S + K^T E.
-// Given the chunk's dE = dLoss/dE and dS_out (both from the reverse scan):
+// Given the chunk's dE = dLoss/dE and dS_out (both from the reverse scan;
+// they and S are stored in the input dtype):
 //   dX = T^T dE = D (N^T dE)                         dv = dX
 //   dq = dO S^T + dA K,   dA = tril(dO E^T)
 //   dk = -dX S^T + E dS_out^T + dA^T Q + dGam K + dGam^T K + 2 dlambda k
@@ -16,7 +17,10 @@
 //   dN  = dE (D X)^T,   dG = -strictly_lower(N^T dN N^T)
 //   dalpha_i += sum_{j<i} dG_ij Gamma_ij,   dGam = D dG
 //   dbeta = dalpha d alpha / d beta,   dlambda = dalpha d alpha / d lambda.
-// All of it in fp32 on fp32 MFMA (16x16x4), one workgroup of 8 waves per
+// fp32 throughout for fp32 inputs (fp32 MFMA 16x16x4).  For bf16 inputs
+// every product with a d_k or d_v dimension rounds its operands to bf16 for
+// bf16 MFMA, as the forward's bf16 path does; N and the C x C chain through
+// it (N^T dN N^T) stay fp32.  One workgroup of 8 waves per
 // chunk.  LDS holds K, two C x max(d_k, d_v) fp32 operand buffers and three
 // C x C matrices; the entry state and dS_out are read from the workspace
 // straight into MFMA registers.
@@ -57,7 +61,8 @@ struct GradLayout {
     static constexpr int NW = 8;
     static constexpr int DM = DK > DV ? DK : DV;
     static constexpr int LDK = DK + 4, LDV = DV + 4, LDC = C + 4;
-    static constexpr int B1 = (C * LDV > 2 * C * LDC) ? C * LDV : 2 * C * LDC;   // floats
+    static constexpr int B1a = (C * LDV > 2 * C * LDC) ? C * LDV : 2 * C * LDC;   // floats
+    static constexpr int B1 = B1a > C * LDK ? B1a : C * LDK;
     static constexpr int B2 = (C * LDV > C * LDK) ? C * LDV : C * LDK;
     static constexpr size_t offK = 0;
     static constexpr size_t offB1 = offK + sizeof(float) * C * LDK;
@@ -70,6 +75,99 @@ struct GradLayout {
     static constexpr size_t offVec = offD + sizeof(float) * C * LDC;
     static constexpr size_t bytes = offVec + sizeof(float) * (4 + 2 * NW) * C;
 };
+
+// bf16 MFMA on fp32 operands held in LDS or registers: each operand is
+// rounded to bf16 as it is fed (fp32 accumulation), which is how the bf16
+// inputs' path multiplies; the fp32 inputs' path keeps fp32 MFMA.
+
+// Four consecutive-k elements of an fp32 operand in LDS, as bf16: element
+// (idx, k) at M[idx*ld + k] (one 16-byte read; ld and k multiples of 4) or,
+// STRIDED, at M[k*ld + idx].
+template <bool STRIDED>
+__device__ __forceinline__ bf16x4 run4f(const float *M, int ld, int idx, int k)
+{
+    if constexpr (!STRIDED) {
+        return to_bf16x4(*reinterpret_cast<const f32x4 *>(M + idx * ld + k));
+    } else {
+        return to_bf16x4(f32x4{M[k * ld + idx], M[(k + 1) * ld + idx], M[(k + 2) * ld + idx],
+                               M[(k + 3) * ld + idx]});
+    }
+}
+
+// out[mt] += A[16mt.., 0:16KT] * B, A fp32 in LDS, B as KT acc tiles (PERM
+// map): the bf16 counterpart of mm_acc_b<float, ...>.
+template <int MT, int KT, bool LOWER, bool A_STRIDED>
+__device__ __forceinline__ void mm_acc_b_bf16(f32x4 (&out)[MT], const float *A, int lda,
+                                              const f32x4 (&Bacc)[KT])
+{
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < (KT + 1) / 2; ++s) {
+        const bool two = 2 * s + 1 < KT;
+        const bf16x8 b = cat(to_bf16x4(Bacc[2 * s]), two ? to_bf16x4(Bacc[2 * s + 1]) : to_bf16x4(zero4()));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if (LOWER && 2 * s > mt) continue;
+            const int i = 16 * mt + l16;
+            const bf16x4 a1 = run4f<A_STRIDED>(A, lda, i, 32 * s + 4 * g);
+            const bf16x4 a2 = two ? run4f<A_STRIDED>(A, lda, i, 32 * s + 16 + 4 * g) : to_bf16x4(zero4());
+            out[mt] = mma(cat(a1, a2), b, out[mt]);
+        }
+    }
+}
+
+// acc += A[i0:i0+16, 0:K] * B[0:K, j0:j0+16], both fp32 in LDS (element
+// (i,k) of A at A[i*lda+k], or A[k*lda+i] if A_STRIDED; (k,j) of B at
+// B[j*ldb+k], or B[k*ldb+j] if B_STRIDED): the bf16 counterpart of
+// mm_lds<float, ...>.  k >= klim (rounded up to 32) is skipped.
+template <int K, bool A_STRIDED, bool B_STRIDED>
+__device__ __forceinline__ f32x4 mm_lds_bf16(f32x4 acc, const float *A, int lda, int i0,
+                                             const float *B, int ldb, int j0, int klim = K)
+{
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < (K + 31) / 32; ++s) {
+        if (32 * s >= klim) break;
+        const int k = 32 * s + 8 * g;
+        bf16x8 a, b;
+        if (k < K) {
+            a = cat(run4f<A_STRIDED>(A, lda, i0 + l16, k), run4f<A_STRIDED>(A, lda, i0 + l16, k + 4));
+            b = cat(run4f<B_STRIDED>(B, ldb, j0 + l16, k), run4f<B_STRIDED>(B, ldb, j0 + l16, k + 4));
+        } else {   // K = 16: the upper half of the k-block is zero
+            a = cat(to_bf16x4(zero4()), to_bf16x4(zero4()));
+            b = a;
+        }
+        acc = mma(a, b, acc);
+    }
+    return acc;
+}
+
+// The products with a d_k or d_v dimension, on bf16 MFMA for bf16 inputs and
+// fp32 MFMA for fp32 inputs.
+template <typename T, int MT, int KT, bool LOWER = false, bool A_STRIDED = false>
+__device__ __forceinline__ void mm_b(f32x4 (&out)[MT], const float *A, int lda,
+                                    const f32x4 (&Bacc)[KT])
+{
+    if constexpr (is_bf16<T>) mm_acc_b_bf16<MT, KT, LOWER, A_STRIDED>(out, A, lda, Bacc);
+    else mm_acc_b<float, MT, KT, LOWER, A_STRIDED>(out, A, lda, Bacc);
+}
+
+template <typename T, int K, bool A_STRIDED, bool B_STRIDED>
+__device__ __forceinline__ f32x4 mm_t(f32x4 acc, const float *A, int lda, int i0, const float *B,
+                                      int ldb, int j0, int klim = K)
+{
+    if constexpr (is_bf16<T>)
+        return mm_lds_bf16<K, A_STRIDED, B_STRIDED>(acc, A, lda, i0, B, ldb, j0, klim);
+    else return mm_lds<float, K, A_STRIDED, B_STRIDED>(acc, A, lda, i0, B, ldb, j0, klim);
+}
+
+// Four consecutive elements (8- or 16-byte aligned) widened to fp32.
+__device__ __forceinline__ f32x4 load4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ f32x4 load4(const __bf16 *p)
+{
+    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
+    return f32x4{to_f32(x[0]), to_f32(x[1]), to_f32(x[2]), to_f32(x[3])};
+}
 
 // Sum over the 16 lanes of a lane group (one acc-tile row).
 __device__ __forceinline__ float row16_sum(float x)
@@ -85,8 +183,8 @@ template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(512) void grad_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ dout, const float *__restrict__ beta, const float *__restrict__ alpha,
-    const float *__restrict__ lambda, const float *__restrict__ states,
-    const float *__restrict__ dSout, const float *__restrict__ dE, T *__restrict__ dq,
+    const float *__restrict__ lambda, const T *__restrict__ states,
+    const T *__restrict__ dSout, const T *__restrict__ dE, T *__restrict__ dq,
     T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ dbeta, int L, int nchunks,
     int euler)
 {
@@ -111,15 +209,41 @@ __global__ __launch_bounds__(512) void grad_kernel(
     const int bh = blockIdx.x / nchunks, c = blockIdx.x - bh * nchunks;
     const long tok0 = (long)bh * L + (long)c * C;
     const int valid = min(C, L - c * C);
-    const float *Sst = states + ((long)bh * nchunks + c) * DK * DV;
-    const float *dSo = dSout + ((long)bh * nchunks + c) * DK * DV;
-    const float *dEg = dE + ((long)bh * nchunks * C + (long)c * C) * DV;
+    const T *Sst = states + ((long)bh * nchunks + c) * DK * DV;
+    const T *dSo = dSout + ((long)bh * nchunks + c) * DK * DV;
+    const T *dEg = dE + ((long)bh * nchunks * C + (long)c * C) * DV;
 
-    // ---- K, per-token scalars; Gamma and N --------------------------------
-    for (int e = tid; e < C * DK; e += NT) {
-        const int row = e / DK, cc = e - row * DK;
-        sK[row * LDK + cc] = row < valid ? to_f32(k[(tok0 + row) * DK + cc]) : 0.f;
+    // ---- every input tile in flight at once (16-byte loads): K, V, dE into
+    // LDS now, dO and Q held in registers until their buffer is free; the
+    // entry-state columns this wave multiplies first straight into registers
+    TileRegs<T, C, DK, NT> rK, rQ;
+    TileRegs<T, C, DV, NT> rV, rO;
+    TileRegs<T, C, DV, NT> rE;
+    rK.load(k + tok0 * DK, DK, valid);
+    rV.load(v + tok0 * DV, DV, valid);
+    rE.load(dEg, DV, valid);
+    rO.load(dout + tok0 * DV, DV, valid);
+    rQ.load(q + tok0 * DK, DK, valid);
+    f32x4 S[MK], SinT[MV], dSoT[MV];
+    if (wv < MV) {
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[mk][r] = to_f32(Sst[(16 * mk + 4 * g + r) * DV + 16 * wv + l16]);
     }
+    if (wv < MK) {   // rows a = 16 wv + l16 of S and dS_out: B operands (k = d_v, j = a)
+        const int a = 16 * wv + l16;
+#pragma unroll
+        for (int kt = 0; kt < MV; ++kt) {
+            SinT[kt] = load4(Sst + a * DV + 16 * kt + 4 * g);
+            dSoT[kt] = load4(dSo + a * DV + 16 * kt + 4 * g);
+        }
+    }
+    rK.store_f32(sK, LDK, valid);
+    rV.store_f32(sB1, LDV, valid);
+    rE.store_f32(sB2, LDV, valid);
+
+    // ---- per-token scalars; Gamma and N -------------------------------------
     for (int e = tid; e < C * LDC; e += NT) sN[e] = 0.f;
     if (tid < C) {
         const bool ok = tid < valid;
@@ -132,7 +256,7 @@ __global__ __launch_bounds__(512) void grad_kernel(
     for (int t = wv; t < MC * MC; t += NW) {
         const int it = t / MC, jt = t - it * MC;
         if (jt > it) continue;
-        const f32x4 acc = mm_lds<float, DK, false, false>(zero4(), sK, LDK, 16 * it, sK, LDK, 16 * jt);
+        const f32x4 acc = mm_t<T, DK, false, false>(zero4(), sK, LDK, 16 * it, sK, LDK, 16 * jt);   // exact products
 #pragma unroll
         for (int r = 0; r < 4; ++r) sGam[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = acc[r];
     }
@@ -184,46 +308,36 @@ __global__ __launch_bounds__(512) void grad_kernel(
     f32x4 E[MC], dX[MC];
     if (wv < MV) {
         const int col = 16 * wv + l16;
-        f32x4 S[MK], X[MC], DXv[MC], dEc[MC], Y[MC];
-#pragma unroll
-        for (int mk = 0; mk < MK; ++mk)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) S[mk][r] = Sst[(16 * mk + 4 * g + r) * DV + col];
+        f32x4 X[MC], DXv[MC], dEc[MC], Y[MC];
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) {
             X[mt] = zero4();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * mt + 4 * g + r;
-                dEc[mt][r] = row < valid ? dEg[row * DV + col] : 0.f;
-            }
+            for (int r = 0; r < 4; ++r) dEc[mt][r] = sB2[(16 * mt + 4 * g + r) * LDV + col];
         }
-        mm_acc_b<float, MC, MK, false, false>(X, sK, LDK, S);   // K S
+        mm_b<T, MC, MK>(X, sK, LDK, S);   // K S
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * mt + 4 * g + r;
-                const float vv = row < valid ? to_f32(v[(tok0 + row) * DV + col]) : 0.f;
-                X[mt][r] = vv - X[mt][r];
+                X[mt][r] = sB1[row * LDV + col] - X[mt][r];   // V - K S
                 DXv[mt][r] = sAl[row] * X[mt][r];
             }
             E[mt] = zero4();
             Y[mt] = zero4();
         }
-        mm_acc_b<float, MC, MC, true, false>(E, sN, LDC, DXv);   // E = N (D X)
-        mm_acc_b<float, MC, MC, false, true>(Y, sN, LDC, dEc);   // Y = N^T dE
+        mm_b<T, MC, MC, true, false>(E, sN, LDC, DXv);   // E = N (D X)
+        mm_b<T, MC, MC, false, true>(Y, sN, LDC, dEc);   // Y = N^T dE
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * mt + 4 * g + r;
                 dX[mt][r] = sAl[row] * Y[mt][r];
-                if (row < valid) dv[(tok0 + row) * DV + col] = from_f32<T>(dX[mt][r]);
                 const float part = row16_sum(X[mt][r] * Y[mt][r]);
                 if (l16 == 0) sPT[wv * C + row] = part;
-                sB1[row * LDV + col] = DXv[mt][r];
-                sB2[row * LDV + col] = dEc[mt][r];
+                sB1[row * LDV + col] = DXv[mt][r];   // dE is already in B2
             }
         }
     }
@@ -232,7 +346,7 @@ __global__ __launch_bounds__(512) void grad_kernel(
     for (int t = wv; t < MC * MC; t += NW) {
         const int it = t / MC, jt = t - it * MC;
         f32x4 acc = zero4();
-        if (jt <= it) acc = mm_lds<float, DV, false, false>(zero4(), sB2, LDV, 16 * it, sB1, LDV, 16 * jt);
+        if (jt <= it) acc = mm_t<T, DV, false, false>(zero4(), sB2, LDV, 16 * it, sB1, LDV, 16 * jt);
 #pragma unroll
         for (int r = 0; r < 4; ++r) sD[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = acc[r];
     }
@@ -249,36 +363,28 @@ __global__ __launch_bounds__(512) void grad_kernel(
             }
     }
     __syncthreads();
+    store_rows<T, C, DV, NT>(dv + tok0 * DV, DV, sB2, LDV, valid);   // dv = dX
 
     // ---- per d_k column tile (wave wv owns output columns 16wv .. 16wv+15) ---
-    f32x4 dQw[MC], dKw[MC], SinT[MV];
+    f32x4 dQw[MC], dKw[MC];
 #pragma unroll
     for (int mt = 0; mt < MC; ++mt) {
         dQw[mt] = zero4();
         dKw[mt] = zero4();
     }
     if (wv < MK) {
-        const int a = 16 * wv + l16;
-        f32x4 dSoT[MV], t1[MC];
-#pragma unroll
-        for (int kt = 0; kt < MV; ++kt) {   // B operand (k = d_v index, j = d_k index a)
-            SinT[kt] = *reinterpret_cast<const f32x4 *>(Sst + a * DV + 16 * kt + 4 * g);
-            dSoT[kt] = *reinterpret_cast<const f32x4 *>(dSo + a * DV + 16 * kt + 4 * g);
-        }
+        f32x4 t1[MC];
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) t1[mt] = zero4();
-        mm_acc_b<float, MC, MV, false, false>(t1, sB2, LDV, SinT);   // dX S^T
-        mm_acc_b<float, MC, MV, false, false>(dKw, sB1, LDV, dSoT);  // E dS_out^T
+        mm_b<T, MC, MV>(t1, sB2, LDV, SinT);    // dX S^T
+        mm_b<T, MC, MV>(dKw, sB1, LDV, dSoT);   // E dS_out^T
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) dKw[mt] -= t1[mt];
     }
     __syncthreads();
-    for (int e = tid; e < C * DV; e += NT) {
-        const int row = e / DV, cc = e - row * DV;
-        sB2[row * LDV + cc] = row < valid ? to_f32(dout[(tok0 + row) * DV + cc]) : 0.f;
-    }
+    rO.store_f32(sB2, LDV, valid);
     __syncthreads();
-    if (wv < MK) mm_acc_b<float, MC, MV, false, false>(dQw, sB2, LDV, SinT);   // dO S^T
+    if (wv < MK) mm_b<T, MC, MV>(dQw, sB2, LDV, SinT);   // dO S^T
     // dA = tril(dO E^T), diagonal included
     f32x4 dAr[TPW];
 #pragma unroll
@@ -287,7 +393,7 @@ __global__ __launch_bounds__(512) void grad_kernel(
         const int it = t / MC, jt = t - it * MC;
         dAr[u] = zero4();
         if (t < MC * MC && jt <= it) {
-            dAr[u] = mm_lds<float, DV, false, false>(zero4(), sB2, LDV, 16 * it, sB1, LDV, 16 * jt);
+            dAr[u] = mm_t<T, DV, false, false>(zero4(), sB2, LDV, 16 * it, sB1, LDV, 16 * jt);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 if (16 * jt + l16 > 16 * it + 4 * g + r) dAr[u][r] = 0.f;
@@ -303,10 +409,7 @@ __global__ __launch_bounds__(512) void grad_kernel(
             for (int r = 0; r < 4; ++r) sdA[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = dAr[u][r];
         }
     }
-    for (int e = tid; e < C * DK; e += NT) {   // Q into B2
-        const int row = e / DK, cc = e - row * DK;
-        sB2[row * LDK + cc] = row < valid ? to_f32(q[(tok0 + row) * DK + cc]) : 0.f;
-    }
+    rQ.store_f32(sB2, LDK, valid);
     // Z = N^T dN
     for (int t = wv; t < MC * MC; t += NW) {
         const int it = t / MC, jt = t - it * MC;
@@ -319,9 +422,9 @@ __global__ __launch_bounds__(512) void grad_kernel(
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) {
             // dq += dA K;  dk += dA^T Q
-            dQw[mt] = mm_lds<float, C, false, true>(dQw[mt], sdA, LDC, 16 * mt, sK, LDK, 16 * wv,
+            dQw[mt] = mm_t<T, C, false, true>(dQw[mt], sdA, LDC, 16 * mt, sK, LDK, 16 * wv,
                                                     16 * mt + 16);
-            dKw[mt] = mm_lds<float, C, true, true>(dKw[mt], sdA, LDC, 16 * mt, sB2, LDK, 16 * wv);
+            dKw[mt] = mm_t<T, C, true, true>(dKw[mt], sdA, LDC, 16 * mt, sB2, LDK, 16 * wv);
         }
     }
     // dG = -strictly_lower(Z N^T); dalpha_i += sum_j dG_ij Gamma_ij; dGam = D dG
@@ -368,12 +471,12 @@ __global__ __launch_bounds__(512) void grad_kernel(
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) {
             // dk += dGam K + dGam^T K
-            dKw[mt] = mm_lds<float, C, false, true>(dKw[mt], sD, LDC, 16 * mt, sK, LDK, 16 * wv,
-                                                    16 * mt + 16);
-            dKw[mt] = mm_lds<float, C, true, true>(dKw[mt], sD, LDC, 16 * mt, sK, LDK, 16 * wv);
+            dKw[mt] = mm_t<T, C, false, true>(dKw[mt], sD, LDC, 16 * mt, sK, LDK, 16 * wv,
+                                              16 * mt + 16);
+            dKw[mt] = mm_t<T, C, true, true>(dKw[mt], sD, LDC, 16 * mt, sK, LDK, 16 * wv);
         }
     }
-    __syncthreads();
+    __syncthreads();   // B1 and B2 are free: stage dq, dk for 16-byte stores
     if (wv < MK) {
         const int a = 16 * wv + l16;
 #pragma unroll
@@ -381,19 +484,19 @@ __global__ __launch_bounds__(512) void grad_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * mt + 4 * g + r;
-                if (row < valid) {
-                    const float kk = 2.f * sDl[row] * sK[row * LDK + a];
-                    dq[(tok0 + row) * DK + a] = from_f32<T>(dQw[mt][r]);
-                    dk[(tok0 + row) * DK + a] = from_f32<T>(dKw[mt][r] + kk);
-                }
+                sB1[row * LDK + a] = dQw[mt][r];
+                sB2[row * LDK + a] = dKw[mt][r] + 2.f * sDl[row] * sK[row * LDK + a];
             }
     }
+    __syncthreads();
+    store_rows<T, C, DK, NT>(dq + tok0 * DK, DK, sB1, LDK, valid);
+    store_rows<T, C, DK, NT>(dk + tok0 * DK, DK, sB2, LDK, valid);
 }
 
 template <typename T, int DK, int DV, int C>
 hipError_t launch_grad(const void *q, const void *k, const void *v, const void *dout,
                        const float *beta, const float *alpha, const float *lambda,
-                       const float *states, const float *dSout, const float *dE, void *dq,
+                       const void *states, const void *dSout, const void *dE, void *dq,
                        void *dk, void *dv, float *dbeta, int BH, int L, bool euler, hipStream_t st)
 {
     using Lay = GradLayout<DK, DV, C>;
@@ -407,15 +510,16 @@ hipError_t launch_grad(const void *q, const void *k, const void *v, const void *
     hipLaunchKernelGGL((grad_kernel<T, DK, DV, C>), dim3((unsigned)(BH * nchunks)), dim3(64 * Lay::NW),
                        Lay::bytes, st, static_cast<const T *>(q), static_cast<const T *>(k),
                        static_cast<const T *>(v), static_cast<const T *>(dout), beta, alpha, lambda,
-                       states, dSout, dE, static_cast<T *>(dq), static_cast<T *>(dk),
+                       static_cast<const T *>(states), static_cast<const T *>(dSout),
+                       static_cast<const T *>(dE), static_cast<T *>(dq), static_cast<T *>(dk),
                        static_cast<T *>(dv), dbeta, L, nchunks, (int)euler);
     return hipGetLastError();
 }
 
 hipError_t dispatch_grad(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                          const void *v, const void *dout, const float *beta, const float *alpha,
-                         const float *lambda, const float *states, const float *dSout,
-                         const float *dE, void *dq, void *dkp, void *dvp, float *dbeta, int BH,
+                         const float *lambda, const void *states, const void *dSout,
+                         const void *dE, void *dq, void *dkp, void *dvp, float *dbeta, int BH,
                          int L, bool euler, hipStream_t st)
 {
 #define CASE(DKV, DVV, CC)                                                                      \

@@ -37,7 +37,8 @@ struct SegArgs {
     float *R;          // SUMMARY: [BH, G, DK, DV]
     float *P;          // SUMMARY: [BH, G, DK, DK]
     const float *Sin;  // REPLAY: [BH, G, DK, DV]
-    float *states;     // WHOLE, optional: the entry state of every chunk [BH, nchunks, DK, DV]
+    void *states;      // WHOLE, optional: the entry state of every chunk [BH, nchunks, DK, DV],
+                       // stored in the input dtype
 };
 
 template <typename T, int DK, int DV, int C, int NW>
@@ -154,11 +155,11 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
         __syncthreads();
 
         if (sg.states) {
-            float *st = sg.states + ((long)bh * nchunks + c) * DK * DV;
+            T *st = static_cast<T *>(sg.states) + ((long)bh * nchunks + c) * DK * DV;
 #pragma unroll
             for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) st[(16 * mk + 4 * g + r) * DV + col] = S[mk][r];
+                for (int r = 0; r < 4; ++r) st[(16 * mk + 4 * g + r) * DV + col] = from_f32<T>(S[mk][r]);
         }
 
         // E = U - W S
@@ -318,13 +319,14 @@ hipError_t launch_scan_segmented(const void *q, const void *k, const void *w, co
 //   dS_in = dS_out + Q^T dO - W^T dE            (W^T dE = K^T T^T dE)
 // which, like the forward, never mixes the d_v columns: a workgroup owns a
 // (sequence, column tile), walks the chunks from last to first with dS in
-// MFMA accumulators, and stores every chunk's dS_out and dE (fp32) for the
+// MFMA accumulators, and stores every chunk's dS_out and dE (in the input
+// dtype: bf16 inputs' products round them to bf16 anyway) for the
 // per-chunk gradient kernel.  dS0 receives dLoss/dS0.
 template <typename T, int DK, int DV, int C, int NW>
 __global__ __launch_bounds__(64 * NW) void rscan_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ w,
     const T *__restrict__ aqk, const T *__restrict__ dout, const float *__restrict__ dSL,
-    float *__restrict__ dSout, float *__restrict__ dE, float *__restrict__ dS0, int L, int nchunks)
+    T *__restrict__ dSout, T *__restrict__ dE, float *__restrict__ dS0, int L, int nchunks)
 {
     using Lay = ScanLayout<T, DK, DV, C, NW>;
     constexpr int TV = Lay::TV, NTILE = DV / TV, MC = C / 16, MK = DK / 16;
@@ -402,11 +404,11 @@ __global__ __launch_bounds__(64 * NW) void rscan_kernel(
         }
         __syncthreads();
 
-        float *so = dSout + ((long)bh * nchunks + c) * DK * DV;
+        T *so = dSout + ((long)bh * nchunks + c) * DK * DV;
 #pragma unroll
         for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) so[(16 * mk + 4 * g + r) * DV + col] = dS[mk][r];
+            for (int r = 0; r < 4; ++r) so[(16 * mk + 4 * g + r) * DV + col] = from_f32<T>(dS[mk][r]);
 
         f32x4 dO[MC], dEc[MC];
 #pragma unroll
@@ -419,11 +421,11 @@ __global__ __launch_bounds__(64 * NW) void rscan_kernel(
         // dE = K dS_out + A^T dO   (A^T: element (i, m) = A[m][i]; A is zero above its diagonal)
         mm_acc_b<T, MC, MK, false, false>(dEc, sK, Lay::LDK, dS);
         mm_acc_b<T, MC, MC, false, true>(dEc, sA, Lay::LDC, dO);
-        float *de = dE + ((long)bh * nchunks * C + (long)c * C) * DV;
+        T *de = dE + ((long)bh * nchunks * C + (long)c * C) * DV;
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) de[(16 * mt + 4 * g + r) * DV + col] = dEc[mt][r];
+            for (int r = 0; r < 4; ++r) de[(16 * mt + 4 * g + r) * DV + col] = from_f32<T>(dEc[mt][r]);
 
         // dS <- dS + Q^T dO - W^T dE
         mm_acc_b<T, MK, MC, false, true>(dS, sQ, Lay::LDK, dO);
@@ -442,7 +444,7 @@ __global__ __launch_bounds__(64 * NW) void rscan_kernel(
 
 template <typename T, int DK, int DV, int C>
 hipError_t launch_rscan(const void *q, const void *k, const void *w, const void *aqk,
-                        const void *dout, const float *dSL, float *dSout, float *dE, float *dS0,
+                        const void *dout, const float *dSL, void *dSout, void *dE, float *dS0,
                         int BH, int L, hipStream_t st)
 {
     constexpr int NW = DV >= 64 ? 4 : DV / 16;
@@ -456,14 +458,15 @@ hipError_t launch_rscan(const void *q, const void *k, const void *w, const void 
     hipLaunchKernelGGL((rscan_kernel<T, DK, DV, C, NW>), dim3((unsigned)(BH * (DV / Lay::TV))),
                        dim3(64 * NW), Lay::bytes, st, static_cast<const T *>(q),
                        static_cast<const T *>(k), static_cast<const T *>(w),
-                       static_cast<const T *>(aqk), static_cast<const T *>(dout), dSL, dSout, dE,
+                       static_cast<const T *>(aqk), static_cast<const T *>(dout), dSL,
+                       static_cast<T *>(dSout), static_cast<T *>(dE),
                        dS0, L, nchunks);
     return hipGetLastError();
 }
 
 hipError_t dispatch_rscan(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                           const void *w, const void *aqk, const void *dout, const float *dSL,
-                          float *dSout, float *dE, float *dS0, int BH, int L, hipStream_t st)
+                          void *dSout, void *dE, float *dS0, int BH, int L, hipStream_t st)
 {
 #define CASE(DKV, DVV, CC)                                                                      \
     if (dk == DKV && dv == DVV && chunk == CC)                                                  \
@@ -478,7 +481,7 @@ hipError_t dispatch_rscan(bool bf16, int dk, int dv, int chunk, const void *q, c
 
 hipError_t dispatch_scan_states(bool bf16, int dk, int dv, int chunk, const void *q,
                                 const void *k, const void *w, const void *u, const void *aqk,
-                                const float *S0, float *states, int BH, int L, hipStream_t st)
+                                const float *S0, void *states, int BH, int L, hipStream_t st)
 {
     const SegArgs whole{SCAN_WHOLE, 1, 1 << 30, nullptr, nullptr, nullptr, states};
 #define CASE(DKV, DVV, CC)                                                                      \

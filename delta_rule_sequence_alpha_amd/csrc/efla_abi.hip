@@ -82,7 +82,7 @@ StagedWs staged_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t 
 }
 
 // Backward workspace: the forward's coefficient and UT-transform outputs,
-// plus every chunk's entry state, dS_out and dE (fp32).
+// plus every chunk's entry state, dS_out and dE (in the input dtype).
 struct BackwardWs {
     size_t alpha, lambda, w, u, aqk, states, dSout, dE, total;
 };
@@ -98,9 +98,9 @@ BackwardWs backward_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtyp
     s.u = s.w + align_up(n * dk * esize(dt));
     s.aqk = s.u + align_up(n * dv * esize(dt));
     s.states = s.aqk + align_up(nch * chunk * chunk * esize(dt));
-    s.dSout = s.states + align_up(nch * dk * dv * sizeof(float));
-    s.dE = s.dSout + align_up(nch * dk * dv * sizeof(float));
-    s.total = s.dE + align_up(nch * chunk * dv * sizeof(float));
+    s.dSout = s.states + align_up(nch * dk * dv * esize(dt));
+    s.dE = s.dSout + align_up(nch * dk * dv * esize(dt));
+    s.total = s.dE + align_up(nch * chunk * dv * esize(dt));
     return s;
 }
 
@@ -394,9 +394,7 @@ efla_status_t efla_backward(const void *q, const void *k, const void *v, const f
     float *alpha = reinterpret_cast<float *>(base + ws.alpha);
     float *lambda = reinterpret_cast<float *>(base + ws.lambda);
     void *w = base + ws.w, *u = base + ws.u, *aqk = base + ws.aqk;
-    float *states = reinterpret_cast<float *>(base + ws.states);
-    float *dSout = reinterpret_cast<float *>(base + ws.dSout);
-    float *dE = reinterpret_cast<float *>(base + ws.dE);
+    void *states = base + ws.states, *dSout = base + ws.dSout, *dE = base + ws.dE;
     hipError_t e = efla::dispatch_coef(bf, dk, k, beta, alpha, lambda, BH * L, euler, st);
     if (e == hipSuccess)
         e = efla::dispatch_ut(bf, dk, dv, chunk, q, k, v, alpha, w, u, aqk, (int)BH, L, st);

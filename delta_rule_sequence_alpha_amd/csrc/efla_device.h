@@ -200,7 +200,56 @@ struct TileRegs {
             if (EXACT || idx < N) *reinterpret_cast<uint4 *>(s + row * s_ld + cv * V) = x;
         }
     }
+
+    // The same tile widened to fp32 in LDS (s_ld a multiple of 4), rows >=
+    // valid as zeros.
+    __device__ __forceinline__ void store_f32(float *s, int s_ld, int valid) const
+    {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int idx = (int)threadIdx.x + j * NT;
+            const int row = idx / VPR, cv = idx % VPR;
+            if (EXACT || idx < N) {
+                const T *e = reinterpret_cast<const T *>(&r[j]);
+                float *d = s + row * s_ld + cv * V;
+#pragma unroll
+                for (int i = 0; i < V; i += 4) {
+                    const bool ok = row < valid;
+                    *reinterpret_cast<float4 *>(d + i) =
+                        make_float4(ok ? to_f32(e[i]) : 0.f, ok ? to_f32(e[i + 1]) : 0.f,
+                                    ok ? to_f32(e[i + 2]) : 0.f, ok ? to_f32(e[i + 3]) : 0.f);
+                }
+            }
+        }
+    }
 };
+
+// Rows [0, valid) of a ROWS x COLS fp32 tile in LDS (row stride s_ld, a
+// multiple of 4) written to global memory as T with 16-byte stores.
+template <typename T, int ROWS, int COLS, int NT>
+__device__ __forceinline__ void store_rows(T *g, long g_ld, const float *s, int s_ld, int valid)
+{
+    constexpr int V = 16 / sizeof(T), VPR = COLS / V, N = ROWS * VPR;
+#pragma unroll
+    for (int j = 0; j < (N + NT - 1) / NT; ++j) {
+        const int idx = (int)threadIdx.x + j * NT;
+        const int row = idx / VPR, cv = idx % VPR;
+        if ((N % NT == 0 || idx < N) && row < valid) {
+            const float *src = s + row * s_ld + cv * V;
+            uint4 out;
+            T *o = reinterpret_cast<T *>(&out);
+#pragma unroll
+            for (int i = 0; i < V; i += 4) {
+                const float4 x = *reinterpret_cast<const float4 *>(src + i);
+                o[i] = from_f32<T>(x.x);
+                o[i + 1] = from_f32<T>(x.y);
+                o[i + 2] = from_f32<T>(x.z);
+                o[i + 3] = from_f32<T>(x.w);
+            }
+            *reinterpret_cast<uint4 *>(g + row * g_ld + cv * V) = out;
+        }
+    }
+}
 
 // alpha from beta and lambda ("Exact Flow Linear Attention: Exact Solution
 // from Continuous-Time Dynamics", Technical Summary, Methodology 3):

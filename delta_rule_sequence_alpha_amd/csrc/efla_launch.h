@@ -44,20 +44,21 @@ hipError_t dispatch_scan_segmented(bool bf16, int dk, int dv, int chunk, const v
 // the entry state of every chunk only (states [BH, nchunks, dk, dv]; no o,
 // no S_L).  dispatch_rscan walks the chunks backwards from dS_L (NULL = 0),
 // writing every chunk's dS_out [BH, nchunks, dk, dv] and dE [BH, nchunks*chunk,
-// dv] (fp32) and, if dS0 is not NULL, dLoss/dS0.  dispatch_grad forms dq, dk,
-// dv (dtype) and dbeta per chunk from them.
+// dv] and, if dS0 is not NULL, dLoss/dS0 (fp32).  states, dS_out and dE are
+// stored in the input dtype.  dispatch_grad forms dq, dk, dv (dtype) and
+// dbeta per chunk from them.
 hipError_t dispatch_scan_states(bool bf16, int dk, int dv, int chunk, const void *q,
                                 const void *k, const void *w, const void *u, const void *aqk,
-                                const float *S0, float *states, int BH, int L, hipStream_t st);
+                                const float *S0, void *states, int BH, int L, hipStream_t st);
 
 hipError_t dispatch_rscan(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                           const void *w, const void *aqk, const void *dout, const float *dSL,
-                          float *dSout, float *dE, float *dS0, int BH, int L, hipStream_t st);
+                          void *dSout, void *dE, float *dS0, int BH, int L, hipStream_t st);
 
 hipError_t dispatch_grad(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                          const void *v, const void *dout, const float *beta, const float *alpha,
-                         const float *lambda, const float *states, const float *dSout,
-                         const float *dE, void *dq, void *dkp, void *dvp, float *dbeta, int BH,
+                         const float *lambda, const void *states, const void *dSout,
+                         const void *dE, void *dq, void *dkp, void *dvp, float *dbeta, int BH,
                          int L, bool euler, hipStream_t st);
 
 bool fused_supported(bool bf16, int dk, int dv, int chunk);

@@ -232,8 +232,10 @@ efla_status_t efla_chunk_scan(const void *q, const void *k, const void *w, const
  * and 0.  The forward is recomputed inside (coefficients, UT transform and
  * the state scan, which stores every chunk's entry state), then a reverse
  * scan carries dLoss/dS from the last chunk to the first and a per-chunk
- * kernel forms dq, dk, dv and dbeta; the per-chunk gradient arithmetic is
- * fp32 for both dtypes.  No output may alias an input or another output.
+ * kernel forms dq, dk, dv and dbeta.  As in the forward, bf16 inputs are
+ * multiplied on bf16 MFMA and fp32 inputs on fp32 MFMA, accumulating in fp32;
+ * the triangular solves stay fp32.  No output may alias an input or another
+ * output.
  * With L = 0 only dS0 = dS_L (or zeros) is written.
  */
 size_t efla_backward_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk,

@@ -182,12 +182,12 @@ def test_auto_path_choice(lib):
 
 
 def test_backward_workspace_size(lib):
-    # alpha, lambda fp32; W, U, A (dtype); entry states, dS_out (fp32 per chunk); dE (fp32)
+    # alpha, lambda fp32; W, U, A, and per chunk the entry state, dS_out and dE (dtype)
     B, H, L, d, C = 4, 16, 4096, 128, 64
     n, nch = B * H * L, B * H * (L // C)
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    want = (2 * up(n * 4) + 2 * up(n * d * 2) + up(nch * C * C * 2) + 2 * up(nch * d * d * 4) +
-            up(nch * C * d * 4))
+    want = (2 * up(n * 4) + 2 * up(n * d * 2) + up(nch * C * C * 2) + 2 * up(nch * d * d * 2) +
+            up(nch * C * d * 2))
     assert _lib.efla_backward_workspace_size(B, H, L, d, d, C, _lib.EFLA_BF16) == want
     assert _lib.efla_backward_workspace_size(1, 1, 0, 16, 16, 16, _lib.EFLA_F32) == 0
     assert _lib.efla_backward_workspace_size(1, 1, 64, 48, 16, 16, _lib.EFLA_F32) == 0
