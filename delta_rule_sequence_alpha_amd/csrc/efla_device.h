@@ -63,19 +63,30 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v)
                   static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
 }
 
-// Four consecutive-k elements of a bf16 operand held in LDS.  The operand
-// element (idx, k) -- idx is the row of A or the column of B -- lives at
-// M[idx*ld + k] when !STRIDED (k contiguous: one 8-byte read), else at
-// M[k*ld + idx] (four 2-byte reads).
-template <bool STRIDED>
-__device__ __forceinline__ bf16x4 run4(const __bf16 *M, int ld, int idx, int k)
+// The strided four-element run for a whole 16-lane group in one transposing
+// LDS read (ds_read_tr16_b64): with k the same across the group, lane l16
+// receives M[(k+e)*ld + i0 + l16] for e = 0..3.  Lane j of the group
+// addresses the four consecutive elements at M[(k + j/4)*ld + i0 + 4(j%4)],
+// and the read gives lane l16 element l16%4 of the run addressed by lane
+// 4e + l16/4.  M must be in LDS; ld and i0 multiples of 4.
+__device__ __forceinline__ bf16x4 run4_tr(const __bf16 *M, int ld, int i0, int k)
 {
-    if constexpr (!STRIDED) {
-        return *reinterpret_cast<const bf16x4 *>(M + idx * ld + k);
-    } else {
-        return bf16x4{M[(k + 0) * ld + idx], M[(k + 1) * ld + idx], M[(k + 2) * ld + idx],
-                      M[(k + 3) * ld + idx]};
-    }
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const int l16 = threadIdx.x & 15;
+    const __bf16 *p = M + (k + (l16 >> 2)) * ld + i0 + 4 * (l16 & 3);
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(p));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// run4 for bf16 operands in LDS, the strided form through run4_tr; idx0 is
+// the tile's first row (of A) or column (of B), idx = idx0 + l16.
+template <bool STRIDED>
+__device__ __forceinline__ bf16x4 run4_lds(const __bf16 *M, int ld, int idx0, int k)
+{
+    const int l16 = threadIdx.x & 15;
+    if constexpr (!STRIDED) return *reinterpret_cast<const bf16x4 *>(M + (idx0 + l16) * ld + k);
+    else return run4_tr(M, ld, idx0, k);
 }
 
 template <bool STRIDED>
@@ -103,9 +114,8 @@ __device__ __forceinline__ void mm_acc_b(f32x4 (&out)[MT], const T *A, int lda,
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 if (LOWER && 2 * s > mt) continue;
-                const int i = 16 * mt + l16;
-                const bf16x4 a1 = run4<A_STRIDED>(A, lda, i, 32 * s + 4 * g);
-                const bf16x4 a2 = two ? run4<A_STRIDED>(A, lda, i, 32 * s + 16 + 4 * g)
+                const bf16x4 a1 = run4_lds<A_STRIDED>(A, lda, 16 * mt, 32 * s + 4 * g);
+                const bf16x4 a2 = two ? run4_lds<A_STRIDED>(A, lda, 16 * mt, 32 * s + 16 + 4 * g)
                                       : to_bf16x4(zero4());
                 out[mt] = mma(cat(a1, a2), b, out[mt]);
             }
@@ -140,15 +150,18 @@ __device__ __forceinline__ f32x4 mm_lds(f32x4 acc, const T *A, int lda, int i0, 
 #pragma unroll
         for (int s = 0; s < (K + 31) / 32; ++s) {
             if (32 * s >= klim) break;
-            const int k = 32 * s + 8 * g;       // NAT map
-            bf16x8 a, b;
-            if (k < K) {
-                a = cat(run4<A_STRIDED>(A, lda, i0 + l16, k), run4<A_STRIDED>(A, lda, i0 + l16, k + 4));
-                b = cat(run4<B_STRIDED>(B, ldb, j0 + l16, k), run4<B_STRIDED>(B, ldb, j0 + l16, k + 4));
-            } else {   // K = 16 (or an odd number of 16-blocks): pad the k-block with zeros
-                a = cat(to_bf16x4(zero4()), to_bf16x4(zero4()));
-                b = a;
-            }
+            // NAT map.  K = 16: lane groups 2, 3 of the 32-wide k-block lie past
+            // K; they read an in-range block (every lane takes part in the
+            // transposing read, which exchanges data across its lane group)
+            // and zero it afterwards.
+            const int k = 32 * s + 8 * g;
+            const bool in = k < K;
+            const int kr = in ? k : k - 16;
+            bf16x8 a = cat(run4_lds<A_STRIDED>(A, lda, i0, kr), run4_lds<A_STRIDED>(A, lda, i0, kr + 4));
+            bf16x8 b = cat(run4_lds<B_STRIDED>(B, ldb, j0, kr), run4_lds<B_STRIDED>(B, ldb, j0, kr + 4));
+            const bf16x8 z = cat(to_bf16x4(zero4()), to_bf16x4(zero4()));
+            a = in ? a : z;
+            b = in ? b : z;
             acc = mma(a, b, acc);
         }
     } else {
