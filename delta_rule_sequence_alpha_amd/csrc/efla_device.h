@@ -237,6 +237,22 @@ struct TileRegs {
     }
 };
 
+// Rows [0, valid) of a ROWS x COLS tile of T in LDS (row stride s_ld, 16-byte
+// aligned rows) copied to global memory with 16-byte stores.
+template <typename T, int ROWS, int COLS, int NT>
+__device__ __forceinline__ void store_rows_t(T *g, long g_ld, const T *s, int s_ld, int valid)
+{
+    constexpr int V = 16 / sizeof(T), VPR = COLS / V, N = ROWS * VPR;
+#pragma unroll
+    for (int j = 0; j < (N + NT - 1) / NT; ++j) {
+        const int idx = (int)threadIdx.x + j * NT;
+        const int row = idx / VPR, cv = idx % VPR;
+        if ((N % NT == 0 || idx < N) && row < valid)
+            *reinterpret_cast<uint4 *>(g + row * g_ld + cv * V) =
+                *reinterpret_cast<const uint4 *>(s + row * s_ld + cv * V);
+    }
+}
+
 // Rows [0, valid) of a ROWS x COLS fp32 tile in LDS (row stride s_ld, a
 // multiple of 4) written to global memory as T with 16-byte stores.
 template <typename T, int ROWS, int COLS, int NT>

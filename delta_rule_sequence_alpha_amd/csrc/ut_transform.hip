@@ -25,10 +25,15 @@ struct UtLayout {
     static constexpr int LDK = DK + PADE, LDV = DV + PADE;
     static constexpr int LDG = C + 1;                  // fp32, scalar access only
     static constexpr int LDTB = C + PADE;              // T converted to T-type
+    // Q is only needed for A = tril(Q K^T), V only for U = T V: they share a
+    // buffer (V waits in registers), which keeps bf16 chunks of 64 tokens at
+    // d = 128 within two workgroups per CU.  K's buffer later stages W, the
+    // Q/V buffer U, for 16-byte stores.
+    static constexpr int LDQV = LDK > LDV ? LDK : LDV;
     static constexpr size_t offK = 0;
     static constexpr size_t offQ = offK + sizeof(T) * C * LDK;
-    static constexpr size_t offV = offQ + sizeof(T) * C * LDK;
-    static constexpr size_t offG = offV + sizeof(T) * C * LDV;
+    static constexpr size_t offV = offQ;
+    static constexpr size_t offG = offQ + sizeof(T) * C * LDQV;
     static constexpr size_t offT = offG + sizeof(float) * C * LDG;
     static constexpr size_t offTb = offT + sizeof(float) * C * LDG;
     static constexpr size_t offA = offTb + (is_bf16<T> ? sizeof(T) * C * LDTB : 0);
@@ -59,16 +64,14 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
     const long tok0 = (long)bh * L + (long)c * C;
     const int valid = min(C, L - c * C);
 
-    {   // every load of the chunk in flight before the first LDS store
-        TileRegs<T, C, DK, 256> tk, tq;
-        TileRegs<T, C, DV, 256> tv;
-        tk.load(k + tok0 * DK, DK, valid);
-        tq.load(q + tok0 * DK, DK, valid);
-        tv.load(v + tok0 * DV, DV, valid);
-        tk.store(sK, Lay::LDK, valid);
-        tq.store(sQ, Lay::LDK, valid);
-        tv.store(sV, Lay::LDV, valid);
-    }
+    // every load of the chunk in flight before the first LDS store
+    TileRegs<T, C, DK, 256> tk, tq;
+    TileRegs<T, C, DV, 256> tv;
+    tk.load(k + tok0 * DK, DK, valid);
+    tq.load(q + tok0 * DK, DK, valid);
+    tv.load(v + tok0 * DV, DV, valid);
+    tk.store(sK, Lay::LDK, valid);
+    tq.store(sQ, Lay::LDK, valid);
     for (int i = threadIdx.x; i < C * Lay::LDG; i += 256) sT[i] = 0.f;
     for (int i = threadIdx.x; i < C; i += 256) sAl[i] = (i < valid) ? alpha[tok0 + i] : 0.f;
     __syncthreads();
@@ -150,36 +153,56 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
             const int r = i / C, cc = i - r * C;
             sTb[r * Lay::LDTB + cc] = from_f32<T>(sT[r * Lay::LDG + cc]);
         }
-        __syncthreads();
         sTop = sTb;
         ldTop = Lay::LDTB;
     } else {
         sTop = reinterpret_cast<const T *>(sT);
         ldTop = Lay::LDG;
     }
+    tv.store(sV, Lay::LDV, valid);   // A = tril(Q K^T) is done with Q
+    __syncthreads();
 
-    // W = T K and U = T V (T lower triangular: k range of row tile mt is [0, 16mt+16)).
+    // W = T K and U = T V (T lower triangular: k range of row tile mt is
+    // [0, 16mt+16)).  Each product is staged in LDS over the operand it no
+    // longer needs (W over K, U over V) and written with 16-byte stores.
     constexpr int NTK = DK / 16, NTV = DV / 16;
-    for (int t = wv; t < MC * (NTK + NTV); t += 4) {
-        const bool isw = t < MC * NTK;
-        const int tt = isw ? t : t - MC * NTK;
-        const int nt_count = isw ? NTK : NTV;
-        const int mt = tt / nt_count, nt = tt - mt * nt_count;
-        f32x4 acc;
-        if (isw)
-            acc = mm_lds<T, C, false, true>(zero4(), sTop, ldTop, 16 * mt, sK, Lay::LDK, 16 * nt,
-                                            16 * mt + 16);
-        else
-            acc = mm_lds<T, C, false, true>(zero4(), sTop, ldTop, 16 * mt, sV, Lay::LDV, 16 * nt,
-                                            16 * mt + 16);
-        T *dst = isw ? w + tok0 * DK : u + tok0 * DV;
-        const int ld = isw ? DK : DV;
+    constexpr int WPW = (MC * NTK + 3) / 4, UPW = (MC * NTV + 3) / 4;   // tiles per wave
+    f32x4 acc[WPW > UPW ? WPW : UPW];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * mt + 4 * g + r;
-            if (row < valid) dst[(long)row * ld + 16 * nt + l16] = from_f32<T>(acc[r]);
-        }
+    for (int j = 0; j < WPW; ++j) {
+        const int t = wv + 4 * j, mt = t / NTK, nt = t - mt * NTK;
+        if (t < MC * NTK)
+            acc[j] = mm_lds<T, C, false, true>(zero4(), sTop, ldTop, 16 * mt, sK, Lay::LDK, 16 * nt,
+                                               16 * mt + 16);
     }
+    __syncthreads();   // every read of K is done
+#pragma unroll
+    for (int j = 0; j < WPW; ++j) {
+        const int t = wv + 4 * j, mt = t / NTK, nt = t - mt * NTK;
+        if (t < MC * NTK)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sK[(16 * mt + 4 * g + r) * Lay::LDK + 16 * nt + l16] = from_f32<T>(acc[j][r]);
+    }
+#pragma unroll
+    for (int j = 0; j < UPW; ++j) {
+        const int t = wv + 4 * j, mt = t / NTV, nt = t - mt * NTV;
+        if (t < MC * NTV)
+            acc[j] = mm_lds<T, C, false, true>(zero4(), sTop, ldTop, 16 * mt, sV, Lay::LDV, 16 * nt,
+                                               16 * mt + 16);
+    }
+    __syncthreads();   // every read of V is done; W is staged
+#pragma unroll
+    for (int j = 0; j < UPW; ++j) {
+        const int t = wv + 4 * j, mt = t / NTV, nt = t - mt * NTV;
+        if (t < MC * NTV)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sV[(16 * mt + 4 * g + r) * Lay::LDV + 16 * nt + l16] = from_f32<T>(acc[j][r]);
+    }
+    __syncthreads();
+    store_rows_t<T, C, DK, 256>(w + tok0 * DK, DK, sK, Lay::LDK, valid);
+    store_rows_t<T, C, DV, 256>(u + tok0 * DV, DV, sV, Lay::LDV, valid);
 }
 
 template <typename T, int DK, int DV, int C>
