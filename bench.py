@@ -355,7 +355,9 @@ def grad_kernel_work(w, esz):
     n = B * H * L
     nch = B * H * ((L + C - 1) // C)
     flops = (8 * dk * dv + 5 * C * dk + 4 * C * dv + C * C) * n
-    byts = (n * (2 * dk + 2 * dv) * esz + 12 * n + 2 * nch * dk * dv * 4 + nch * C * dv * 4 +
+    # reads q, k, v, dO; alpha, lambda, beta; each chunk's entry state, dS_out
+    # and dE (stored in the input dtype); writes dq, dk, dv, dbeta
+    byts = (n * (2 * dk + 2 * dv) * esz + 12 * n + 2 * nch * dk * dv * esz + nch * C * dv * esz +
             n * (2 * dk + dv) * esz + 4 * n)
     return flops, byts
 
@@ -402,8 +404,8 @@ def bench_backward(args, w, dev):
             "workspace_bytes": need,
             "grad_kernel_algorithmic_flops": gf, "grad_kernel_algorithmic_bytes": gb,
             "note": "five launches: coefficients, UT transform, state scan storing chunk entry "
-                    "states, reverse state scan, per-chunk gradients (fp32 MFMA); per-kernel "
-                    "times from rocprofv3"}
+                    "states, reverse state scan, per-chunk gradients (bf16 MFMA for bf16 inputs, "
+                    "fp32 for the triangular chain); per-kernel times from rocprofv3"}
 
 
 def cpu_baseline(w, host):
