@@ -116,43 +116,53 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
     RW rW, rQ, rK;
     RU rU;
     RA rA;
+    // (with no o to write, Q and A are not needed)
+    const bool want_o = sg.mode != SCAN_SUMMARY && o;
     auto load_all = [&](int cn) {
         cn = min(cn, c_end - 1);
         const long t0 = (long)bh * L + (long)cn * C;
         const int vn = min(C, L - cn * C);
         rW.load(w + t0 * DK, DK, vn);
-        rQ.load(q + t0 * DK, DK, vn);
         rK.load(k + t0 * DK, DK, vn);
         rU.load(u + t0 * DV + utile * TV, DV, vn);
-        rA.load(aqk + ((long)bh * nchunks + cn) * C * C, C, C);
+        if (want_o) {
+            rQ.load(q + t0 * DK, DK, vn);
+            rA.load(aqk + ((long)bh * nchunks + cn) * C * C, C, C);
+        }
     };
     if constexpr (PREFETCH) load_all(c_begin);
 
     for (int c = c_begin; c < c_end; ++c) {
         const long tok0 = (long)bh * L + (long)c * C;
         const int valid = min(C, L - c * C);
-        __syncthreads();   // the previous chunk is done with LDS
+        __syncthreads();   // the previous chunk is done with LDS (and this chunk's loads have landed)
         if constexpr (PREFETCH) {
             rW.store(sW, Lay::LDK, valid);
-            rQ.store(sQ, Lay::LDK, valid);
             rK.store(sK, Lay::LDK, valid);
             rU.store(sU, Lay::LDU, valid);
-            rA.store(sA, Lay::LDC, C);
-            load_all(c + 1);
+            if (want_o) {
+                rQ.store(sQ, Lay::LDK, valid);
+                rA.store(sA, Lay::LDC, C);
+            }
         } else {
             RW t;
             t.load(w + tok0 * DK, DK, valid);
             t.store(sW, Lay::LDK, valid);
-            t.load(q + tok0 * DK, DK, valid);
-            t.store(sQ, Lay::LDK, valid);
             t.load(k + tok0 * DK, DK, valid);
             t.store(sK, Lay::LDK, valid);
             rU.load(u + tok0 * DV + utile * TV, DV, valid);
             rU.store(sU, Lay::LDU, valid);
-            rA.load(aqk + ((long)bh * nchunks + c) * C * C, C, C);
-            rA.store(sA, Lay::LDC, C);
+            if (want_o) {
+                t.load(q + tok0 * DK, DK, valid);
+                t.store(sQ, Lay::LDK, valid);
+                rA.load(aqk + ((long)bh * nchunks + c) * C * C, C, C);
+                rA.store(sA, Lay::LDC, C);
+            }
         }
         __syncthreads();
+        // the next chunk's loads fly while this one is computed (a workgroup
+        // barrier waits for every outstanding load, so they are issued after it)
+        if constexpr (PREFETCH) load_all(c + 1);
 
         if (sg.states) {
             T *st = static_cast<T *>(sg.states) + ((long)bh * nchunks + c) * DK * DV;
@@ -174,7 +184,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
                 E[mt][r] = (ptile ? 0.f : to_f32(sU[(16 * mt + 4 * g + r) * Lay::LDU + 16 * wv + l16])) -
                            E[mt][r];
 
-        if (sg.mode != SCAN_SUMMARY && o) {   // a segment's map needs no output
+        if (want_o) {   // a segment's map needs no output
             // O = Q S + A E
             f32x4 O[MC];
 #pragma unroll
@@ -388,7 +398,6 @@ __global__ __launch_bounds__(64 * NW) void rscan_kernel(
             rK.store(sK, Lay::LDK, valid);
             rO.store(sO, Lay::LDU, valid);
             rA.store(sA, Lay::LDC, C);
-            load_all(c - 1);
         } else {
             RW t;
             t.load(w + tok0 * DK, DK, valid);
@@ -403,6 +412,7 @@ __global__ __launch_bounds__(64 * NW) void rscan_kernel(
             rA.store(sA, Lay::LDC, C);
         }
         __syncthreads();
+        if constexpr (PREFETCH) load_all(c - 1);   // in flight during this chunk
 
         T *so = dSout + ((long)bh * nchunks + c) * DK * DV;
 #pragma unroll
@@ -442,12 +452,11 @@ __global__ __launch_bounds__(64 * NW) void rscan_kernel(
     }
 }
 
-template <typename T, int DK, int DV, int C>
-hipError_t launch_rscan(const void *q, const void *k, const void *w, const void *aqk,
-                        const void *dout, const float *dSL, void *dSout, void *dE, float *dS0,
-                        int BH, int L, hipStream_t st)
+template <typename T, int DK, int DV, int C, int NW>
+hipError_t launch_rscan_nw(const void *q, const void *k, const void *w, const void *aqk,
+                           const void *dout, const float *dSL, void *dSout, void *dE, float *dS0,
+                           int BH, int L, hipStream_t st)
 {
-    constexpr int NW = DV >= 64 ? 4 : DV / 16;
     using Lay = ScanLayout<T, DK, DV, C, NW>;
     const int nchunks = (L + C - 1) / C;
     if (BH == 0) return hipSuccess;
@@ -464,16 +473,31 @@ hipError_t launch_rscan(const void *q, const void *k, const void *w, const void 
     return hipGetLastError();
 }
 
+// Waves per workgroup (each owns 16 columns): 4 unless nw > 0 caps it.
+template <typename T, int DK, int DV, int C>
+hipError_t launch_rscan(const void *q, const void *k, const void *w, const void *aqk,
+                        const void *dout, const float *dSL, void *dSout, void *dE, float *dS0,
+                        int BH, int L, int nw, hipStream_t st)
+{
+    if (nw <= 0) nw = 4;
+    if (nw >= 4 && DV >= 64)
+        return launch_rscan_nw<T, DK, DV, C, 4>(q, k, w, aqk, dout, dSL, dSout, dE, dS0, BH, L, st);
+    if (nw >= 2 && DV >= 32)
+        return launch_rscan_nw<T, DK, DV, C, 2>(q, k, w, aqk, dout, dSL, dSout, dE, dS0, BH, L, st);
+    return launch_rscan_nw<T, DK, DV, C, 1>(q, k, w, aqk, dout, dSL, dSout, dE, dS0, BH, L, st);
+}
+
 hipError_t dispatch_rscan(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                           const void *w, const void *aqk, const void *dout, const float *dSL,
-                          void *dSout, void *dE, float *dS0, int BH, int L, hipStream_t st)
+                          void *dSout, void *dE, float *dS0, int BH, int L, int nw,
+                          hipStream_t st)
 {
 #define CASE(DKV, DVV, CC)                                                                      \
     if (dk == DKV && dv == DVV && chunk == CC)                                                  \
         return bf16 ? launch_rscan<__bf16, DKV, DVV, CC>(q, k, w, aqk, dout, dSL, dSout, dE,    \
-                                                         dS0, BH, L, st)                        \
+                                                         dS0, BH, L, nw, st)                    \
                     : launch_rscan<float, DKV, DVV, CC>(q, k, w, aqk, dout, dSL, dSout, dE,     \
-                                                        dS0, BH, L, st);
+                                                        dS0, BH, L, nw, st);
     EFLA_SHAPE_CASES(CASE)
 #undef CASE
     return hipErrorInvalidValue;
@@ -481,15 +505,16 @@ hipError_t dispatch_rscan(bool bf16, int dk, int dv, int chunk, const void *q, c
 
 hipError_t dispatch_scan_states(bool bf16, int dk, int dv, int chunk, const void *q,
                                 const void *k, const void *w, const void *u, const void *aqk,
-                                const float *S0, void *states, int BH, int L, hipStream_t st)
+                                const float *S0, void *states, int BH, int L, int nw,
+                                hipStream_t st)
 {
     const SegArgs whole{SCAN_WHOLE, 1, 1 << 30, nullptr, nullptr, nullptr, states};
 #define CASE(DKV, DVV, CC)                                                                      \
     if (dk == DKV && dv == DVV && chunk == CC)                                                  \
         return bf16 ? launch_scan_auto<__bf16, DKV, DVV, CC>(q, k, w, u, aqk, S0, nullptr,      \
-                                                             nullptr, BH, L, 0, whole, st)      \
+                                                             nullptr, BH, L, nw, whole, st)     \
                     : launch_scan_auto<float, DKV, DVV, CC>(q, k, w, u, aqk, S0, nullptr,       \
-                                                            nullptr, BH, L, 0, whole, st);
+                                                            nullptr, BH, L, nw, whole, st);
     EFLA_SHAPE_CASES(CASE)
 #undef CASE
     return hipErrorInvalidValue;

@@ -49,11 +49,13 @@ hipError_t dispatch_scan_segmented(bool bf16, int dk, int dv, int chunk, const v
 // dbeta per chunk from them.
 hipError_t dispatch_scan_states(bool bf16, int dk, int dv, int chunk, const void *q,
                                 const void *k, const void *w, const void *u, const void *aqk,
-                                const float *S0, void *states, int BH, int L, hipStream_t st);
+                                const float *S0, void *states, int BH, int L, int nw,
+                                hipStream_t st);
 
 hipError_t dispatch_rscan(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                           const void *w, const void *aqk, const void *dout, const float *dSL,
-                          void *dSout, void *dE, float *dS0, int BH, int L, hipStream_t st);
+                          void *dSout, void *dE, float *dS0, int BH, int L, int nw,
+                          hipStream_t st);
 
 hipError_t dispatch_grad(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                          const void *v, const void *dout, const float *beta, const float *alpha,
