@@ -205,7 +205,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
         mm_acc_b<T, MK, MC, false, true>(S, sK, Lay::LDK, E);
     }
 
-    if (sg.mode == SCAN_WHOLE && !SL) return;
+    if (sg.mode != SCAN_SUMMARY && !SL) return;
     float *dst = SL + sbase;
     int ld = DV;
     if (sg.mode == SCAN_SUMMARY) {
@@ -332,11 +332,21 @@ hipError_t launch_scan_segmented(const void *q, const void *k, const void *w, co
 // MFMA accumulators, and stores every chunk's dS_out and dE (in the input
 // dtype: bf16 inputs' products round them to bf16 anyway) for the
 // per-chunk gradient kernel.  dS0 receives dLoss/dS0.
+//
+// Segments, as in the forward: the chunk sends dS_out to
+// dS_in = (I - W^T K) dS_out + (Q^T - W^T A^T) dO, an affine map whose
+// matrix is the transpose of the forward one, so a sequence split into G
+// segments is scanned backwards in three launches: SUMMARY forms each
+// segment's map (R from dS = 0, the matrix from dS = I with dO = 0), the
+// combine pass runs the maps from the last segment to the first (stored in
+// reverse segment order, so the forward combine kernel serves), and REPLAY
+// walks every segment from its true end gradient, storing dS_out and dE.
 template <typename T, int DK, int DV, int C, int NW>
 __global__ __launch_bounds__(64 * NW) void rscan_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ w,
     const T *__restrict__ aqk, const T *__restrict__ dout, const float *__restrict__ dSL,
-    T *__restrict__ dSout, T *__restrict__ dE, float *__restrict__ dS0, int L, int nchunks)
+    T *__restrict__ dSout, T *__restrict__ dE, float *__restrict__ dS0, int L, int nchunks,
+    SegArgs sg)
 {
     using Lay = ScanLayout<T, DK, DV, C, NW>;
     constexpr int TV = Lay::TV, NTILE = DV / TV, MC = C / 16, MK = DK / 16;
@@ -348,14 +358,31 @@ __global__ __launch_bounds__(64 * NW) void rscan_kernel(
     T *sA = reinterpret_cast<T *>(smem + Lay::offA);
     T *sO = reinterpret_cast<T *>(smem + Lay::offU);   // the dO column tile
 
-    int bh, tile;
-    xcd_map(blockIdx.x, gridDim.x, NTILE, bh, tile);
+    const bool summary = sg.mode == SCAN_SUMMARY;
+    const int ntiles = NTILE + (summary ? DK / TV : 0);
+    int bhs, tile;
+    xcd_map(blockIdx.x, gridDim.x, ntiles, bhs, tile);
+    const int bh = bhs / sg.G, gs = bhs - bh * sg.G;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
-    const int col = tile * TV + 16 * wv + l16;
+    const bool ptile = tile >= NTILE;                 // a column of the map's matrix (dO = 0, from I)
+    const int utile = ptile ? 0 : tile;
+    const int col = (ptile ? tile - NTILE : tile) * TV + 16 * wv + l16;
     const long sbase = (long)bh * DK * DV;
+    const int c_begin = gs * sg.seg_chunks, c_end = min(nchunks, c_begin + sg.seg_chunks);
+    const long segbase = ((long)bh * sg.G + (sg.G - 1 - gs)) * DK * DV;   // reverse order
 
     f32x4 dS[MK];
-    if (dSL) {
+    if (sg.mode == SCAN_REPLAY) {
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dS[mk][r] = sg.Sin[segbase + (16 * mk + 4 * g + r) * DV + col];
+    } else if (summary) {
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dS[mk][r] = (ptile && 16 * mk + 4 * g + r == col) ? 1.f : 0.f;
+    } else if (dSL) {
 #pragma unroll
         for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
@@ -374,21 +401,21 @@ __global__ __launch_bounds__(64 * NW) void rscan_kernel(
     RW rW, rQ, rK;
     RU rO;
     RA rA;
-    auto load_all = [&](int cn) {   // chunk cn's tiles (cn < 0 re-loads chunk 0, never stored)
-        cn = max(cn, 0);
+    auto load_all = [&](int cn) {   // chunk cn's tiles (cn < c_begin re-loads c_begin, never stored)
+        cn = max(cn, c_begin);
         const long t0 = (long)bh * L + (long)cn * C;
         const int vn = min(C, L - cn * C);
         rW.load(w + t0 * DK, DK, vn);
         rQ.load(q + t0 * DK, DK, vn);
         rK.load(k + t0 * DK, DK, vn);
-        rO.load(dout + t0 * DV + tile * TV, DV, vn);
+        rO.load(dout + t0 * DV + utile * TV, DV, vn);
         rA.load(aqk + ((long)bh * nchunks + cn) * C * C, C, C);
     };
     if constexpr (PREFETCH) {
-        if (nchunks > 0) load_all(nchunks - 1);
+        if (c_end > c_begin) load_all(c_end - 1);
     }
 
-    for (int c = nchunks - 1; c >= 0; --c) {
+    for (int c = c_end - 1; c >= c_begin; --c) {
         const int valid = min(C, L - c * C);
         const long tok0 = (long)bh * L + (long)c * C;
         __syncthreads();   // the previous chunk is done with LDS
@@ -406,7 +433,7 @@ __global__ __launch_bounds__(64 * NW) void rscan_kernel(
             t.store(sQ, Lay::LDK, valid);
             t.load(k + tok0 * DK, DK, valid);
             t.store(sK, Lay::LDK, valid);
-            rO.load(dout + tok0 * DV + tile * TV, DV, valid);
+            rO.load(dout + tok0 * DV + utile * TV, DV, valid);
             rO.store(sO, Lay::LDU, valid);
             rA.load(aqk + ((long)bh * nchunks + c) * C * C, C, C);
             rA.store(sA, Lay::LDC, C);
@@ -414,11 +441,13 @@ __global__ __launch_bounds__(64 * NW) void rscan_kernel(
         __syncthreads();
         if constexpr (PREFETCH) load_all(c - 1);   // in flight during this chunk
 
-        T *so = dSout + ((long)bh * nchunks + c) * DK * DV;
+        if (!summary) {   // a segment's map stores nothing per chunk
+            T *so = dSout + ((long)bh * nchunks + c) * DK * DV;
 #pragma unroll
-        for (int mk = 0; mk < MK; ++mk)
+            for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) so[(16 * mk + 4 * g + r) * DV + col] = from_f32<T>(dS[mk][r]);
+                for (int r = 0; r < 4; ++r) so[(16 * mk + 4 * g + r) * DV + col] = from_f32<T>(dS[mk][r]);
+        }
 
         f32x4 dO[MC], dEc[MC];
 #pragma unroll
@@ -426,16 +455,18 @@ __global__ __launch_bounds__(64 * NW) void rscan_kernel(
             dEc[mt] = zero4();
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                dO[mt][r] = to_f32(sO[(16 * mt + 4 * g + r) * Lay::LDU + 16 * wv + l16]);
+                dO[mt][r] = ptile ? 0.f : to_f32(sO[(16 * mt + 4 * g + r) * Lay::LDU + 16 * wv + l16]);
         }
         // dE = K dS_out + A^T dO   (A^T: element (i, m) = A[m][i]; A is zero above its diagonal)
         mm_acc_b<T, MC, MK, false, false>(dEc, sK, Lay::LDK, dS);
         mm_acc_b<T, MC, MC, false, true>(dEc, sA, Lay::LDC, dO);
-        T *de = dE + ((long)bh * nchunks * C + (long)c * C) * DV;
+        if (!summary) {
+            T *de = dE + ((long)bh * nchunks * C + (long)c * C) * DV;
 #pragma unroll
-        for (int mt = 0; mt < MC; ++mt)
+            for (int mt = 0; mt < MC; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) de[(16 * mt + 4 * g + r) * DV + col] = from_f32<T>(dEc[mt][r]);
+                for (int r = 0; r < 4; ++r) de[(16 * mt + 4 * g + r) * DV + col] = from_f32<T>(dEc[mt][r]);
+        }
 
         // dS <- dS + Q^T dO - W^T dE
         mm_acc_b<T, MK, MC, false, true>(dS, sQ, Lay::LDK, dO);
@@ -444,60 +475,103 @@ __global__ __launch_bounds__(64 * NW) void rscan_kernel(
         mm_acc_b<T, MK, MC, false, true>(dS, sW, Lay::LDK, dEc);
     }
 
-    if (dS0) {
+    float *dst = dS0 ? dS0 + sbase : nullptr;
+    int ld = DV;
+    if (summary) {
+        dst = ptile ? sg.P + ((long)bh * sg.G + (sg.G - 1 - gs)) * DK * DK : sg.R + segbase;
+        ld = ptile ? DK : DV;
+    } else if (gs != 0) {
+        return;   // only the first segment's final gradient is dLoss/dS0
+    }
+    if (dst) {
 #pragma unroll
         for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dS0[sbase + (16 * mk + 4 * g + r) * DV + col] = dS[mk][r];
+            for (int r = 0; r < 4; ++r) dst[(16 * mk + 4 * g + r) * ld + col] = dS[mk][r];
     }
 }
 
 template <typename T, int DK, int DV, int C, int NW>
 hipError_t launch_rscan_nw(const void *q, const void *k, const void *w, const void *aqk,
                            const void *dout, const float *dSL, void *dSout, void *dE, float *dS0,
-                           int BH, int L, hipStream_t st)
+                           int BH, int L, SegArgs sg, hipStream_t st)
 {
     using Lay = ScanLayout<T, DK, DV, C, NW>;
+    const int ntiles = DV / Lay::TV + (sg.mode == SCAN_SUMMARY ? DK / Lay::TV : 0);
     const int nchunks = (L + C - 1) / C;
     if (BH == 0) return hipSuccess;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&rscan_kernel<T, DK, DV, C, NW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((rscan_kernel<T, DK, DV, C, NW>), dim3((unsigned)(BH * (DV / Lay::TV))),
+    hipLaunchKernelGGL((rscan_kernel<T, DK, DV, C, NW>), dim3((unsigned)(BH * sg.G * ntiles)),
                        dim3(64 * NW), Lay::bytes, st, static_cast<const T *>(q),
                        static_cast<const T *>(k), static_cast<const T *>(w),
                        static_cast<const T *>(aqk), static_cast<const T *>(dout), dSL,
                        static_cast<T *>(dSout), static_cast<T *>(dE),
-                       dS0, L, nchunks);
+                       dS0, L, nchunks, sg);
     return hipGetLastError();
 }
 
-// Waves per workgroup (each owns 16 columns): 4 unless nw > 0 caps it.
+// Waves per workgroup (each owns 16 columns): 4 unless nw > 0 caps it; the
+// segment summary also tiles the d_k columns of the map's matrix.
+template <typename T, int DK, int DV, int C>
+hipError_t launch_rscan_mode(const void *q, const void *k, const void *w, const void *aqk,
+                             const void *dout, const float *dSL, void *dSout, void *dE,
+                             float *dS0, int BH, int L, int nw, SegArgs sg, hipStream_t st)
+{
+    constexpr int DMIN = DK < DV ? DK : DV;
+    const int wmax = sg.mode == SCAN_SUMMARY ? DMIN : DV;
+    if (nw <= 0) nw = 4;
+    if (nw >= 4 && wmax >= 64)
+        return launch_rscan_nw<T, DK, DV, C, 4>(q, k, w, aqk, dout, dSL, dSout, dE, dS0, BH, L, sg, st);
+    if (nw >= 2 && wmax >= 32)
+        return launch_rscan_nw<T, DK, DV, C, 2>(q, k, w, aqk, dout, dSL, dSout, dE, dS0, BH, L, sg, st);
+    return launch_rscan_nw<T, DK, DV, C, 1>(q, k, w, aqk, dout, dSL, dSout, dE, dS0, BH, L, sg, st);
+}
+
+// G == 1: one walk over each sequence.  G > 1: segment maps (R [BH,G,dk,dv],
+// P [BH,G,dk,dk]), their composition from dS_L into each segment's end
+// gradient (Sin [BH,G,dk,dv]), then every segment replayed in parallel; all
+// three in reverse segment order.
 template <typename T, int DK, int DV, int C>
 hipError_t launch_rscan(const void *q, const void *k, const void *w, const void *aqk,
                         const void *dout, const float *dSL, void *dSout, void *dE, float *dS0,
-                        int BH, int L, int nw, hipStream_t st)
+                        int BH, int L, int nw, int G, int seg_chunks, float *R, float *P,
+                        float *Sin, hipStream_t st)
 {
-    if (nw <= 0) nw = 4;
-    if (nw >= 4 && DV >= 64)
-        return launch_rscan_nw<T, DK, DV, C, 4>(q, k, w, aqk, dout, dSL, dSout, dE, dS0, BH, L, st);
-    if (nw >= 2 && DV >= 32)
-        return launch_rscan_nw<T, DK, DV, C, 2>(q, k, w, aqk, dout, dSL, dSout, dE, dS0, BH, L, st);
-    return launch_rscan_nw<T, DK, DV, C, 1>(q, k, w, aqk, dout, dSL, dSout, dE, dS0, BH, L, st);
+    if (G <= 1) {
+        const SegArgs whole{SCAN_WHOLE, 1, 1 << 30, nullptr, nullptr, nullptr, nullptr};
+        return launch_rscan_mode<T, DK, DV, C>(q, k, w, aqk, dout, dSL, dSout, dE, dS0, BH, L, nw,
+                                               whole, st);
+    }
+    if (BH == 0) return hipSuccess;
+    const SegArgs sum{SCAN_SUMMARY, G, seg_chunks, R, P, nullptr, nullptr};
+    hipError_t e = launch_rscan_mode<T, DK, DV, C>(q, k, w, aqk, dout, nullptr, dSout, dE, nullptr,
+                                                   BH, L, nw, sum, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((seg_combine_kernel<DK, DV>), dim3((unsigned)(BH * (DV / 16))), dim3(256), 0,
+                       st, dSL, P, R, Sin, G);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const SegArgs rep{SCAN_REPLAY, G, seg_chunks, nullptr, nullptr, Sin, nullptr};
+    return launch_rscan_mode<T, DK, DV, C>(q, k, w, aqk, dout, nullptr, dSout, dE, dS0, BH, L, nw,
+                                           rep, st);
 }
 
 hipError_t dispatch_rscan(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                           const void *w, const void *aqk, const void *dout, const float *dSL,
-                          void *dSout, void *dE, float *dS0, int BH, int L, int nw,
-                          hipStream_t st)
+                          void *dSout, void *dE, float *dS0, int BH, int L, int nw, int G,
+                          int seg_chunks, float *R, float *P, float *Sin, hipStream_t st)
 {
 #define CASE(DKV, DVV, CC)                                                                      \
     if (dk == DKV && dv == DVV && chunk == CC)                                                  \
         return bf16 ? launch_rscan<__bf16, DKV, DVV, CC>(q, k, w, aqk, dout, dSL, dSout, dE,    \
-                                                         dS0, BH, L, nw, st)                    \
+                                                         dS0, BH, L, nw, G, seg_chunks, R, P,   \
+                                                         Sin, st)                               \
                     : launch_rscan<float, DKV, DVV, CC>(q, k, w, aqk, dout, dSL, dSout, dE,     \
-                                                        dS0, BH, L, nw, st);
+                                                        dS0, BH, L, nw, G, seg_chunks, R, P,    \
+                                                        Sin, st);
     EFLA_SHAPE_CASES(CASE)
 #undef CASE
     return hipErrorInvalidValue;
@@ -505,9 +579,32 @@ hipError_t dispatch_rscan(bool bf16, int dk, int dv, int chunk, const void *q, c
 
 hipError_t dispatch_scan_states(bool bf16, int dk, int dv, int chunk, const void *q,
                                 const void *k, const void *w, const void *u, const void *aqk,
-                                const float *S0, void *states, int BH, int L, int nw,
-                                hipStream_t st)
+                                const float *S0, void *states, int BH, int L, int nw, int G,
+                                int seg_chunks, float *R, float *P, float *Sin, hipStream_t st)
 {
+    if (G > 1) {   // segment maps, their composition, then the segments replayed storing states
+        const SegArgs sum{SCAN_SUMMARY, G, seg_chunks, R, P, nullptr, nullptr};
+        const SegArgs rep{SCAN_REPLAY, G, seg_chunks, nullptr, nullptr, Sin, states};
+#define CASE(DKV, DVV, CC)                                                                      \
+        if (dk == DKV && dv == DVV && chunk == CC) {                                            \
+            hipError_t e = bf16 ? launch_scan_auto<__bf16, DKV, DVV, CC>(q, k, w, u, aqk, nullptr, \
+                                      nullptr, nullptr, BH, L, nw, sum, st)                     \
+                                : launch_scan_auto<float, DKV, DVV, CC>(q, k, w, u, aqk, nullptr, \
+                                      nullptr, nullptr, BH, L, nw, sum, st);                    \
+            if (e != hipSuccess) return e;                                                      \
+            hipLaunchKernelGGL((seg_combine_kernel<DKV, DVV>), dim3((unsigned)(BH * (DVV / 16))), \
+                               dim3(256), 0, st, S0, P, R, Sin, G);                             \
+            e = hipGetLastError();                                                              \
+            if (e != hipSuccess) return e;                                                      \
+            return bf16 ? launch_scan_auto<__bf16, DKV, DVV, CC>(q, k, w, u, aqk, nullptr,      \
+                                                                 nullptr, nullptr, BH, L, nw, rep, st) \
+                        : launch_scan_auto<float, DKV, DVV, CC>(q, k, w, u, aqk, nullptr,       \
+                                                                nullptr, nullptr, BH, L, nw, rep, st); \
+        }
+        EFLA_SHAPE_CASES(CASE)
+#undef CASE
+        return hipErrorInvalidValue;
+    }
     const SegArgs whole{SCAN_WHOLE, 1, 1 << 30, nullptr, nullptr, nullptr, states};
 #define CASE(DKV, DVV, CC)                                                                      \
     if (dk == DKV && dv == DVV && chunk == CC)                                                  \

@@ -82,15 +82,18 @@ StagedWs staged_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t 
 }
 
 // Backward workspace: the forward's coefficient and UT-transform outputs,
-// plus every chunk's entry state, dS_out and dE (in the input dtype).
+// plus every chunk's entry state, dS_out and dE (in the input dtype), and for
+// G > 1 segments the segment maps and boundary states (fp32) that the two
+// segmented scans use one after the other.
 struct BackwardWs {
-    size_t alpha, lambda, w, u, aqk, states, dSout, dE, total;
+    size_t alpha, lambda, w, u, aqk, states, dSout, dE, R, P, Sin, total;
 };
 
-BackwardWs backward_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t dt)
+BackwardWs backward_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t dt, int G)
 {
     const size_t n = (size_t)B * H * L;
     const size_t nch = (size_t)B * H * ((L + chunk - 1) / chunk);
+    const size_t segs = (size_t)B * H * G;
     BackwardWs s;
     s.alpha = 0;
     s.lambda = s.alpha + align_up(n * sizeof(float));
@@ -100,7 +103,13 @@ BackwardWs backward_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtyp
     s.states = s.aqk + align_up(nch * chunk * chunk * esize(dt));
     s.dSout = s.states + align_up(nch * dk * dv * esize(dt));
     s.dE = s.dSout + align_up(nch * dk * dv * esize(dt));
-    s.total = s.dE + align_up(nch * chunk * dv * esize(dt));
+    s.R = s.dE + align_up(nch * chunk * dv * esize(dt));
+    s.total = s.P = s.Sin = s.R;
+    if (G > 1) {
+        s.P = s.R + align_up(segs * dk * dv * sizeof(float));
+        s.Sin = s.P + align_up(segs * dk * dk * sizeof(float));
+        s.total = s.Sin + align_up(segs * dk * dv * sizeof(float));
+    }
     return s;
 }
 
@@ -367,7 +376,8 @@ size_t efla_backward_workspace_size(int B, int H, int L, int dk, int dv, int chu
 {
     if (check_shape(B, H, L, dk, dv, chunk, dt) != EFLA_OK) return 0;
     if (L == 0 || (long long)B * H == 0) return 0;
-    return backward_ws(B, H, L, dk, dv, chunk, dt).total;
+    return backward_ws(B, H, L, dk, dv, chunk, dt,
+                       seg_plan((long long)B * H, L, dk, dv, chunk).G).total;
 }
 
 efla_status_t efla_backward(const void *q, const void *k, const void *v, const float *beta,
@@ -395,7 +405,9 @@ efla_status_t efla_backward(const void *q, const void *k, const void *v, const f
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(d_o) ||
         !aligned16(dq) || !aligned16(dk_out) || !aligned16(dv_out) || !aligned16(dbeta))
         return EFLA_ERR_INVALID_ARG;
-    const BackwardWs ws = backward_ws(B, H, L, dk, dv, chunk, dt);
+    // few long sequences: both scans split over L, as the forward's AUTO path
+    const SegPlan plan = seg_plan(BH, L, dk, dv, chunk);
+    const BackwardWs ws = backward_ws(B, H, L, dk, dv, chunk, dt, plan.G);
     if (!workspace || workspace_bytes < ws.total) return EFLA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return EFLA_ERR_INVALID_ARG;
 
@@ -405,15 +417,19 @@ efla_status_t efla_backward(const void *q, const void *k, const void *v, const f
     float *lambda = reinterpret_cast<float *>(base + ws.lambda);
     void *w = base + ws.w, *u = base + ws.u, *aqk = base + ws.aqk;
     void *states = base + ws.states, *dSout = base + ws.dSout, *dE = base + ws.dE;
+    float *R = reinterpret_cast<float *>(base + ws.R), *P = reinterpret_cast<float *>(base + ws.P);
+    float *Sin = reinterpret_cast<float *>(base + ws.Sin);
     hipError_t e = efla::dispatch_coef(bf, dk, k, beta, alpha, lambda, BH * L, euler, st);
     if (e == hipSuccess)
         e = efla::dispatch_ut(bf, dk, dv, chunk, q, k, v, alpha, w, u, aqk, (int)BH, L, st);
     if (e == hipSuccess)
         e = efla::dispatch_scan_states(bf, dk, dv, chunk, q, k, w, u, aqk, S0, states, (int)BH, L,
-                                       bwd_scan_waves(BH, dv), st);
+                                       bwd_scan_waves(BH, dv), plan.G, plan.seg_chunks, R, P, Sin,
+                                       st);
     if (e == hipSuccess)
         e = efla::dispatch_rscan(bf, dk, dv, chunk, q, k, w, aqk, d_o, dS_L, dSout, dE, dS0,
-                                 (int)BH, L, bwd_scan_waves(BH, dv), st);
+                                 (int)BH, L, bwd_scan_waves(BH, dv), plan.G, plan.seg_chunks, R, P,
+                                 Sin, st);
     if (e == hipSuccess)
         e = efla::dispatch_grad(bf, dk, dv, chunk, q, k, v, d_o, beta, alpha, lambda, states,
                                 dSout, dE, dq, dk_out, dv_out, dbeta, (int)BH, L, euler, st);

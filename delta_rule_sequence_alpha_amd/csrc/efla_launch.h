@@ -45,17 +45,19 @@ hipError_t dispatch_scan_segmented(bool bf16, int dk, int dv, int chunk, const v
 // no S_L).  dispatch_rscan walks the chunks backwards from dS_L (NULL = 0),
 // writing every chunk's dS_out [BH, nchunks, dk, dv] and dE [BH, nchunks*chunk,
 // dv] and, if dS0 is not NULL, dLoss/dS0 (fp32).  states, dS_out and dE are
-// stored in the input dtype.  dispatch_grad forms dq, dk, dv (dtype) and
+// stored in the input dtype.  With G > 1 both scans run over G segments of
+// seg_chunks chunks (maps R, P and composed boundary states Sin in fp32
+// scratch, reused by the two).  dispatch_grad forms dq, dk, dv (dtype) and
 // dbeta per chunk from them.
 hipError_t dispatch_scan_states(bool bf16, int dk, int dv, int chunk, const void *q,
                                 const void *k, const void *w, const void *u, const void *aqk,
-                                const float *S0, void *states, int BH, int L, int nw,
-                                hipStream_t st);
+                                const float *S0, void *states, int BH, int L, int nw, int G,
+                                int seg_chunks, float *R, float *P, float *Sin, hipStream_t st);
 
 hipError_t dispatch_rscan(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                           const void *w, const void *aqk, const void *dout, const float *dSL,
-                          void *dSout, void *dE, float *dS0, int BH, int L, int nw,
-                          hipStream_t st);
+                          void *dSout, void *dE, float *dS0, int BH, int L, int nw, int G,
+                          int seg_chunks, float *R, float *P, float *Sin, hipStream_t st);
 
 hipError_t dispatch_grad(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                          const void *v, const void *dout, const float *beta, const float *alpha,

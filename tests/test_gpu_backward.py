@@ -136,3 +136,14 @@ def test_autograd_function(dtype):
     torch.cuda.synchronize()
     got = [x.grad for x in leaves]
     _compare((q, k, v, beta, S0, dO, dSL), got, TOL[dtype])
+
+
+@pytest.mark.parametrize("recipe,dtype,H,L", [("long-stiff-f32", "f32", 2, 64 * 20 + 7),
+                                              ("lm1.3b-bf16", "bf16", 2, 64 * 20 + 7),
+                                              ("long-stiff-f32", "f32", 4, 4096)])
+def test_backward_segmented_few_long_sequences(recipe, dtype, H, L):
+    # few long sequences: both backward scans run split over L into segments
+    # (segment maps, their composition, replay), as the forward's segmented path
+    w = wl.FORWARD_WORKLOADS[recipe].with_(name="bwd-seg", B=1, H=H, L=L, dtype=dtype)
+    inputs, got = _case(w, seed=9)
+    _compare(inputs, got, TOL[dtype])
