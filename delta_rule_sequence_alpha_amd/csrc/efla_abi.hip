@@ -140,11 +140,13 @@ int scan_waves_override() { return waves_override("EFLA_SCAN_WAVES"); }
 // Waves per workgroup of the backward's two scans: 4-wave workgroups (64
 // columns) unless that leaves CUs idle, then 2 (measured on lm1.3b-bf16:
 // 233 vs 260 us for the reverse scan, 197 vs 214 us for the state scan).
-int bwd_scan_waves(long long BH, int dv)
+// Segmented scans have workgroups to spare: 4 (long-stiff-f32: 1.6 vs 2.6 ms
+// per state-scan pass).
+int bwd_scan_waves(long long BH, int dv, int G)
 {
     const int o = waves_override("EFLA_BWD_SCAN_WAVES");
     if (o > 0) return o;
-    return BH * ((dv + 63) / 64) >= 256 ? 4 : 2;
+    return (G > 1 || BH * ((dv + 63) / 64) >= 256) ? 4 : 2;
 }
 
 efla_status_t hip_status(hipError_t e) { return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP; }
@@ -424,11 +426,11 @@ efla_status_t efla_backward(const void *q, const void *k, const void *v, const f
         e = efla::dispatch_ut(bf, dk, dv, chunk, q, k, v, alpha, w, u, aqk, (int)BH, L, st);
     if (e == hipSuccess)
         e = efla::dispatch_scan_states(bf, dk, dv, chunk, q, k, w, u, aqk, S0, states, (int)BH, L,
-                                       bwd_scan_waves(BH, dv), plan.G, plan.seg_chunks, R, P, Sin,
+                                       bwd_scan_waves(BH, dv, plan.G), plan.G, plan.seg_chunks, R, P, Sin,
                                        st);
     if (e == hipSuccess)
         e = efla::dispatch_rscan(bf, dk, dv, chunk, q, k, w, aqk, d_o, dS_L, dSout, dE, dS0,
-                                 (int)BH, L, bwd_scan_waves(BH, dv), plan.G, plan.seg_chunks, R, P,
+                                 (int)BH, L, bwd_scan_waves(BH, dv, plan.G), plan.G, plan.seg_chunks, R, P,
                                  Sin, st);
     if (e == hipSuccess)
         e = efla::dispatch_grad(bf, dk, dv, chunk, q, k, v, d_o, beta, alpha, lambda, states,
