@@ -10,16 +10,20 @@ timed in the same run and reported under "decode".
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload lm1.3b-bf16]
                   [--path auto|staged|fused|segmented] [--no-cpu-baseline] [--no-decode]
-                  [--no-compare] [--no-backward]
+                  [--no-compare] [--no-backward] [--no-cold] [--no-peaks]
 
 The fused path is also timed with the Euler update (alpha = beta) and both
 kernel times are reported under "update_compare"; a packed (varlen) batch of
 the same token count is timed under "varlen", and the backward pass (dq, dk,
 dv, dbeta, dS0 given dO and dS_L) of the same workload under "backward".
+"call_ms" has per-call median/p10/p90 times, warm and cold (1 GiB written
+between calls); "decode_512" the decode step with a state twice the Infinity
+Cache; "measured_peaks" a device copy and vendor GEMMs for reference.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -205,6 +209,30 @@ def bench_forward(args, w, dev):
 
     elapsed, per_kernel = timed(args.steps)
 
+    # Per-call times (an event pair around each call): warm, back to back; and
+    # cold, with a 1 GiB buffer written between calls so that neither the L2s
+    # nor the 256 MiB Infinity Cache hold any input.
+    def per_call(n, cold):
+        scratch = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev) if cold else None
+        timer = Timer(stream, names)
+        ms = []
+        for i in range(n):
+            if cold:
+                scratch.fill_(i & 0xff)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step(timer.marks() if path == "staged" else None, timer)
+            b.record(stream)
+            ms.append((a, b))
+        torch.cuda.synchronize()
+        t = sorted(x.elapsed_time(y) for x, y in ms)
+        pick = lambda f: t[min(len(t) - 1, int(f * (len(t) - 1) + 0.5))]  # noqa: E731
+        return {"calls": n, "median_ms": pick(0.5), "p10_ms": pick(0.1), "p90_ms": pick(0.9)}
+    call_stats = {"warm": per_call(max(args.steps, 10), False)}
+    if not args.no_cold:
+        call_stats["cold"] = per_call(10, True)
+
     # The same kernel with the explicit Euler step (alpha = beta, the delta
     # rule the exact flow is compared against), timed the same way.
     compare = None
@@ -258,14 +286,17 @@ def bench_forward(args, w, dev):
         "flops_per_token_head": flops_per_token(dk, dv, C),
         "kernel_ms": per_kernel,
         "roofline": roof,
+        "call_ms": call_stats,
     }
     if compare is not None:
         res["update_compare"] = compare
     return res, host
 
 
-def bench_decode(args, dev, n_distinct=8):
+def bench_decode(args, dev, n_distinct=8, n_seq=None):
     w = wl.DECODE_WORKLOADS["decode-f32"]
+    if n_seq is not None:
+        w = dataclasses.replace(w, N=n_seq)
     S = wl.decode_state(w, seed=0).to(dev)
     toks = []
     for s in range(n_distinct):
@@ -298,8 +329,8 @@ def bench_decode(args, dev, n_distinct=8):
     return {"workload": w.name, "N": w.N, "H": w.H, "d_k": w.d_k, "d_v": w.d_v,
             "steps": w.steps, "ms_per_step": ms, "GB_s": by / (ms * 1e-3) / 1e9,
             "hbm_frac": by / (ms * 1e-3) / HBM_PEAK, "algorithmic_bytes": by,
-            "note": f"{n_distinct} distinct token sets cycled over the steps; the state "
-                    f"({nh * w.d_k * w.d_v * 4} B) equals the 256 MiB Infinity Cache size"}
+            "note": f"{n_distinct} distinct token sets cycled over the steps; the state is "
+                    f"{nh * w.d_k * w.d_v * 4} B against the 256 MiB Infinity Cache"}
 
 
 def bench_varlen(args, dev, n_seq=16):
@@ -423,6 +454,37 @@ def cpu_baseline(w, host):
                       f"OpenMP over heads; inputs converted to fp64 before timing"}
 
 
+def measured_peaks(dev):
+    """What this GPU reaches in practice, beside the published peaks: a 1 GiB
+    device copy (bytes read + written per second) and large square GEMMs in
+    torch (the vendor BLAS) in bf16 and fp32."""
+    def time_ms(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = time_ms(lambda: dst.copy_(src), 10)
+    del src, dst
+    out = {"hbm_copy_GB_s": 2 * COPY_BYTES / (t_copy * 1e-3) / 1e9}
+    for name, dtype, n in (("bf16", torch.bfloat16, 8192), ("f32", torch.float32, 4096)):
+        a = torch.randn(n, n, device=dev).to(dtype)
+        b = torch.randn(n, n, device=dev).to(dtype)
+        t = time_ms(lambda: torch.mm(a, b), 10)
+        out[f"{name}_gemm_TFLOP_s"] = 2 * n ** 3 / (t * 1e-3) / 1e12
+        del a, b
+    out["note"] = ("1 GiB device copy; torch.mm of square contiguous matrices (8192^3 bf16, "
+                   "4096^3 fp32); published peaks: 8 TB/s, 2.5 PFLOP/s bf16, 157.3 TFLOP/s fp32")
+    return out
+
+
 # --- HBM traffic from rocprofv3 --pmc ----------------------------------------
 
 COPY_BYTES = 1 << 30
@@ -514,6 +576,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache per-call timing")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy/GEMM peaks")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip timing the Euler variant of the fused kernel")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -544,12 +608,23 @@ def main():
     if not args.no_decode:
         print("[bench] decode-f32", file=sys.stderr, flush=True)
         res["decode"] = bench_decode(args, dev)
+        print("[bench] decode-f32 at N=512 (state twice the Infinity Cache)", file=sys.stderr,
+              flush=True)
+        res["decode_512"] = bench_decode(args, dev, n_seq=512)
     if not args.no_compare and w.dtype == "bf16":
         print("[bench] varlen", file=sys.stderr, flush=True)
         res["varlen"] = bench_varlen(args, dev)
     if not args.no_backward:
         print(f"[bench] backward {w.name}", file=sys.stderr, flush=True)
         res["backward"] = bench_backward(args, w, dev)
+    if not args.no_peaks:
+        print("[bench] measured peaks", file=sys.stderr, flush=True)
+        pk = measured_peaks(dev)
+        res["measured_peaks"] = pk
+        rf = res["roofline"]
+        ref = pk["hbm_copy_GB_s"] if rf["bound"] == "hbm" else pk[f"{w.dtype}_gemm_TFLOP_s"]
+        rf["measured_peak"] = ref
+        rf["frac_of_measured_peak"] = rf["achieved"] / ref
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, host)
