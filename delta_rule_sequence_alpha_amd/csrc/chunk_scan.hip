@@ -54,11 +54,14 @@ struct ScanLayout {
     static constexpr size_t bytes = offU + sizeof(T) * C * LDU;
 };
 
+// The scan of workgroup `bid` of `nblocks` (a kernel body, so that a launch
+// can also host another scan's workgroups).
 template <typename T, int DK, int DV, int C, int NW>
-__global__ __launch_bounds__(64 * NW) void scan_kernel(
+__device__ __forceinline__ void scan_body(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ w,
     const T *__restrict__ u, const T *__restrict__ aqk, const float *__restrict__ S0,
-    T *__restrict__ o, float *__restrict__ SL, int L, int nchunks, SegArgs sg)
+    T *__restrict__ o, float *__restrict__ SL, int L, int nchunks, SegArgs sg, int bid,
+    int nblocks)
 {
     using Lay = ScanLayout<T, DK, DV, C, NW>;
     constexpr int TV = Lay::TV, NTILE = DV / TV, MC = C / 16, MK = DK / 16;
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
     // DK / TV tiles of P after the NTILE tiles of R
     const int ntiles = NTILE + (sg.mode == SCAN_SUMMARY ? DK / TV : 0);
     int bhs, tile;
-    xcd_map(blockIdx.x, gridDim.x, ntiles, bhs, tile);
+    xcd_map(bid, nblocks, ntiles, bhs, tile);
     const int bh = bhs / sg.G, gs = bhs - bh * sg.G;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
     const bool ptile = tile >= NTILE;                 // a column of P (U = 0, from S = I)
@@ -220,6 +223,15 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
         for (int r = 0; r < 4; ++r) dst[(16 * mk + 4 * g + r) * ld + col] = S[mk][r];
 }
 
+template <typename T, int DK, int DV, int C, int NW>
+__global__ __launch_bounds__(64 * NW) void scan_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ w,
+    const T *__restrict__ u, const T *__restrict__ aqk, const float *__restrict__ S0,
+    T *__restrict__ o, float *__restrict__ SL, int L, int nchunks, SegArgs sg)
+{
+    scan_body<T, DK, DV, C, NW>(q, k, w, u, aqk, S0, o, SL, L, nchunks, sg, blockIdx.x, gridDim.x);
+}
+
 // S_in(0) = S0 (or 0); S_in(g) = P_{g-1} S_in(g-1) + R_{g-1} for g = 1 .. G-1.
 // One workgroup per (sequence, 16 columns); S_in(g-1)'s columns stay in LDS,
 // P rows are read from L2; fp32 FMAs (G - 1 small products per sequence).
@@ -342,11 +354,11 @@ hipError_t launch_scan_segmented(const void *q, const void *k, const void *w, co
 // reverse segment order, so the forward combine kernel serves), and REPLAY
 // walks every segment from its true end gradient, storing dS_out and dE.
 template <typename T, int DK, int DV, int C, int NW>
-__global__ __launch_bounds__(64 * NW) void rscan_kernel(
+__device__ __forceinline__ void rscan_body(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ w,
     const T *__restrict__ aqk, const T *__restrict__ dout, const float *__restrict__ dSL,
     T *__restrict__ dSout, T *__restrict__ dE, float *__restrict__ dS0, int L, int nchunks,
-    SegArgs sg)
+    SegArgs sg, int bid, int nblocks)
 {
     using Lay = ScanLayout<T, DK, DV, C, NW>;
     constexpr int TV = Lay::TV, NTILE = DV / TV, MC = C / 16, MK = DK / 16;
@@ -361,7 +373,7 @@ __global__ __launch_bounds__(64 * NW) void rscan_kernel(
     const bool summary = sg.mode == SCAN_SUMMARY;
     const int ntiles = NTILE + (summary ? DK / TV : 0);
     int bhs, tile;
-    xcd_map(blockIdx.x, gridDim.x, ntiles, bhs, tile);
+    xcd_map(bid, nblocks, ntiles, bhs, tile);
     const int bh = bhs / sg.G, gs = bhs - bh * sg.G;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
     const bool ptile = tile >= NTILE;                 // a column of the map's matrix (dO = 0, from I)
@@ -492,6 +504,41 @@ __global__ __launch_bounds__(64 * NW) void rscan_kernel(
 }
 
 template <typename T, int DK, int DV, int C, int NW>
+__global__ __launch_bounds__(64 * NW) void rscan_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ w,
+    const T *__restrict__ aqk, const T *__restrict__ dout, const float *__restrict__ dSL,
+    T *__restrict__ dSout, T *__restrict__ dE, float *__restrict__ dS0, int L, int nchunks,
+    SegArgs sg)
+{
+    rscan_body<T, DK, DV, C, NW>(q, k, w, aqk, dout, dSL, dSout, dE, dS0, L, nchunks, sg,
+                                 blockIdx.x, gridDim.x);
+}
+
+// The backward's two scans in one launch: they are independent (the reverse
+// scan needs no chunk state), and each is latency-bound on its own chain of
+// chunks, so workgroups of both sharing the CUs hide each other's waits.
+// Workgroups [0, nfwd) run the state scan, the rest the reverse scan.
+template <typename T, int DK, int DV, int C, int NW>
+__global__ __launch_bounds__(64 * NW) void scan_pair_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ w,
+    const T *__restrict__ u, const T *__restrict__ aqk, const float *__restrict__ S0,
+    void *states, const T *__restrict__ dout, const float *__restrict__ dSL,
+    T *__restrict__ dSout, T *__restrict__ dE, float *__restrict__ dS0, int L, int nchunks,
+    int nfwd)
+{
+    const int b = blockIdx.x;
+    if (b < nfwd) {
+        const SegArgs whole{SCAN_WHOLE, 1, 1 << 30, nullptr, nullptr, nullptr, states};
+        scan_body<T, DK, DV, C, NW>(q, k, w, u, aqk, S0, nullptr, nullptr, L, nchunks, whole, b,
+                                    nfwd);
+    } else {
+        const SegArgs whole{SCAN_WHOLE, 1, 1 << 30, nullptr, nullptr, nullptr, nullptr};
+        rscan_body<T, DK, DV, C, NW>(q, k, w, aqk, dout, dSL, dSout, dE, dS0, L, nchunks, whole,
+                                     b - nfwd, (int)gridDim.x - nfwd);
+    }
+}
+
+template <typename T, int DK, int DV, int C, int NW>
 hipError_t launch_rscan_nw(const void *q, const void *k, const void *w, const void *aqk,
                            const void *dout, const float *dSL, void *dSout, void *dE, float *dS0,
                            int BH, int L, SegArgs sg, hipStream_t st)
@@ -612,6 +659,62 @@ hipError_t dispatch_scan_states(bool bf16, int dk, int dv, int chunk, const void
                                                              nullptr, BH, L, nw, whole, st)     \
                     : launch_scan_auto<float, DKV, DVV, CC>(q, k, w, u, aqk, S0, nullptr,       \
                                                             nullptr, BH, L, nw, whole, st);
+    EFLA_SHAPE_CASES(CASE)
+#undef CASE
+    return hipErrorInvalidValue;
+}
+
+template <typename T, int DK, int DV, int C, int NW>
+hipError_t launch_scan_pair_nw(const void *q, const void *k, const void *w, const void *u,
+                               const void *aqk, const float *S0, void *states, const void *dout,
+                               const float *dSL, void *dSout, void *dE, float *dS0, int BH, int L,
+                               hipStream_t st)
+{
+    using Lay = ScanLayout<T, DK, DV, C, NW>;
+    const int nchunks = (L + C - 1) / C;
+    const int nfwd = BH * (DV / Lay::TV);
+    if (BH == 0) return hipSuccess;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&scan_pair_kernel<T, DK, DV, C, NW>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((scan_pair_kernel<T, DK, DV, C, NW>), dim3((unsigned)(2 * nfwd)),
+                       dim3(64 * NW), Lay::bytes, st, static_cast<const T *>(q),
+                       static_cast<const T *>(k), static_cast<const T *>(w),
+                       static_cast<const T *>(u), static_cast<const T *>(aqk), S0, states,
+                       static_cast<const T *>(dout), dSL, static_cast<T *>(dSout),
+                       static_cast<T *>(dE), dS0, L, nchunks, nfwd);
+    return hipGetLastError();
+}
+
+template <typename T, int DK, int DV, int C>
+hipError_t launch_scan_pair(const void *q, const void *k, const void *w, const void *u,
+                            const void *aqk, const float *S0, void *states, const void *dout,
+                            const float *dSL, void *dSout, void *dE, float *dS0, int BH, int L,
+                            int nw, hipStream_t st)
+{
+    if (nw <= 0) nw = 4;
+    if (nw >= 4 && DV >= 64)
+        return launch_scan_pair_nw<T, DK, DV, C, 4>(q, k, w, u, aqk, S0, states, dout, dSL, dSout,
+                                                     dE, dS0, BH, L, st);
+    if (nw >= 2 && DV >= 32)
+        return launch_scan_pair_nw<T, DK, DV, C, 2>(q, k, w, u, aqk, S0, states, dout, dSL, dSout,
+                                                     dE, dS0, BH, L, st);
+    return launch_scan_pair_nw<T, DK, DV, C, 1>(q, k, w, u, aqk, S0, states, dout, dSL, dSout, dE,
+                                                 dS0, BH, L, st);
+}
+
+hipError_t dispatch_scan_pair(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
+                              const void *w, const void *u, const void *aqk, const float *S0,
+                              void *states, const void *dout, const float *dSL, void *dSout,
+                              void *dE, float *dS0, int BH, int L, int nw, hipStream_t st)
+{
+#define CASE(DKV, DVV, CC)                                                                      \
+    if (dk == DKV && dv == DVV && chunk == CC)                                                  \
+        return bf16 ? launch_scan_pair<__bf16, DKV, DVV, CC>(q, k, w, u, aqk, S0, states, dout, \
+                                                             dSL, dSout, dE, dS0, BH, L, nw, st) \
+                    : launch_scan_pair<float, DKV, DVV, CC>(q, k, w, u, aqk, S0, states, dout,  \
+                                                            dSL, dSout, dE, dS0, BH, L, nw, st);
     EFLA_SHAPE_CASES(CASE)
 #undef CASE
     return hipErrorInvalidValue;

@@ -137,16 +137,16 @@ int waves_override(const char *name)
 }
 int scan_waves_override() { return waves_override("EFLA_SCAN_WAVES"); }
 
-// Waves per workgroup of the backward's two scans: 4-wave workgroups (64
-// columns) unless that leaves CUs idle, then 2 (measured on lm1.3b-bf16:
-// 233 vs 260 us for the reverse scan, 197 vs 214 us for the state scan).
-// Segmented scans have workgroups to spare: 4 (long-stiff-f32: 1.6 vs 2.6 ms
-// per state-scan pass).
-int bwd_scan_waves(long long BH, int dv, int G)
+// Waves per workgroup of the backward's two scans (64-column workgroups).
+// Unsegmented they share one launch, whose workgroups then fill the CUs
+// (lm1.3b-bf16: 270 us for both at 4 waves, 297 at 2; run one after the
+// other they took 197 + 232 us at 2 waves).  Segmented scans have
+// workgroups to spare (long-stiff-f32: 1.5 vs 2.6 ms per state-scan pass
+// at 4 vs 2 waves).
+int bwd_scan_waves()
 {
     const int o = waves_override("EFLA_BWD_SCAN_WAVES");
-    if (o > 0) return o;
-    return (G > 1 || BH * ((dv + 63) / 64) >= 256) ? 4 : 2;
+    return o > 0 ? o : 4;
 }
 
 efla_status_t hip_status(hipError_t e) { return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP; }
@@ -424,14 +424,17 @@ efla_status_t efla_backward(const void *q, const void *k, const void *v, const f
     hipError_t e = efla::dispatch_coef(bf, dk, k, beta, alpha, lambda, BH * L, euler, st);
     if (e == hipSuccess)
         e = efla::dispatch_ut(bf, dk, dv, chunk, q, k, v, alpha, w, u, aqk, (int)BH, L, st);
-    if (e == hipSuccess)
+    const int nw = bwd_scan_waves();
+    if (e == hipSuccess && plan.G == 1) {   // the two scans are independent: one launch
+        e = efla::dispatch_scan_pair(bf, dk, dv, chunk, q, k, w, u, aqk, S0, states, d_o, dS_L,
+                                     dSout, dE, dS0, (int)BH, L, nw, st);
+    } else if (e == hipSuccess) {           // segmented: one after the other (shared scratch)
         e = efla::dispatch_scan_states(bf, dk, dv, chunk, q, k, w, u, aqk, S0, states, (int)BH, L,
-                                       bwd_scan_waves(BH, dv, plan.G), plan.G, plan.seg_chunks, R, P, Sin,
-                                       st);
-    if (e == hipSuccess)
-        e = efla::dispatch_rscan(bf, dk, dv, chunk, q, k, w, aqk, d_o, dS_L, dSout, dE, dS0,
-                                 (int)BH, L, bwd_scan_waves(BH, dv, plan.G), plan.G, plan.seg_chunks, R, P,
-                                 Sin, st);
+                                       nw, plan.G, plan.seg_chunks, R, P, Sin, st);
+        if (e == hipSuccess)
+            e = efla::dispatch_rscan(bf, dk, dv, chunk, q, k, w, aqk, d_o, dS_L, dSout, dE, dS0,
+                                     (int)BH, L, nw, plan.G, plan.seg_chunks, R, P, Sin, st);
+    }
     if (e == hipSuccess)
         e = efla::dispatch_grad(bf, dk, dv, chunk, q, k, v, d_o, beta, alpha, lambda, states,
                                 dSout, dE, dq, dk_out, dv_out, dbeta, (int)BH, L, euler, st);

@@ -65,6 +65,12 @@ hipError_t dispatch_grad(bool bf16, int dk, int dv, int chunk, const void *q, co
                          const void *dE, void *dq, void *dkp, void *dvp, float *dbeta, int BH,
                          int L, bool euler, hipStream_t st);
 
+// dispatch_scan_states and dispatch_rscan (unsegmented) in one launch.
+hipError_t dispatch_scan_pair(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
+                              const void *w, const void *u, const void *aqk, const float *S0,
+                              void *states, const void *dout, const float *dSL, void *dSout,
+                              void *dE, float *dS0, int BH, int L, int nw, hipStream_t st);
+
 bool fused_supported(bool bf16, int dk, int dv, int chunk);
 
 hipError_t dispatch_fused(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
