@@ -434,9 +434,10 @@ def bench_backward(args, w, dev):
             "tflops": fl / (ms * 1e-3) / 1e12, "flops_per_token_head": fl / n,
             "workspace_bytes": need,
             "grad_kernel_algorithmic_flops": gf, "grad_kernel_algorithmic_bytes": gb,
-            "note": "five launches: coefficients, UT transform, state scan storing chunk entry "
-                    "states, reverse state scan, per-chunk gradients (bf16 MFMA for bf16 inputs, "
-                    "fp32 for the triangular chain); per-kernel times from rocprofv3"}
+            "note": "four launches: coefficients, UT transform, the state scan storing chunk "
+                    "entry states and the reverse state scan sharing one launch, per-chunk "
+                    "gradients (bf16 MFMA for bf16 inputs, fp32 for the triangular chain); "
+                    "per-kernel times from rocprofv3"}
 
 
 def cpu_baseline(w, host):
