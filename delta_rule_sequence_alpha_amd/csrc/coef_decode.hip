@@ -144,7 +144,12 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
         float4 x = s[i];
         x.x = fmaf(ak, r.x, x.x); x.y = fmaf(ak, r.y, x.y);
         x.z = fmaf(ak, r.z, x.z); x.w = fmaf(ak, r.w, x.w);
-        Sp[(rg + i * RG) * CG + c] = x;
+        // non-temporal: the new state is not read again by this launch, and
+        // write-allocating it would evict the state still to be read (at
+        // N = 512, 16 heads, d = 128: 6.74 vs 5.15 TB/s; at N = 256, where
+        // the state fits the Infinity Cache, 6.68 vs 6.44 TB/s)
+        __builtin_nontemporal_store(f32x4{x.x, x.y, x.z, x.w},
+                                    reinterpret_cast<f32x4 *>(Sp) + (rg + i * RG) * CG + c);
     }
     if (rg == 0) {
         const float akq = al * s_kq;
