@@ -61,6 +61,7 @@ constexpr int NP = 3;                 // prep waves per workgroup
 enum Role { K_WAVE = 0, Q_WAVE = 1, T_WAVE = 2 };   // prep wave NS + role
 constexpr int kSpinMax = 1 << 22;     // bound on the prep-wave wait (never reached in practice)
 constexpr int kRsrcWord3 = 0x00020000;   // raw (unswizzled, stride 0) buffer resource
+constexpr int kStoreNT = 2;              // cache policy of the output stores: non-temporal
 
 // Buffer resource over the first `bytes` bytes at p: loads past the end
 // return zeros, stores past the end are dropped.
@@ -477,7 +478,7 @@ __device__ __attribute__((always_inline)) inline void prep_store_out(const PrepC
         const bf *p = os + (8 * cv + (l16 >> 2)) * Lay::LDO + 16 * rb + 4 * (l16 & 3);
         const bf16x8 row = cat(ds_read_tr(p), ds_read_tr(p + 4 * Lay::LDO));
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, row), ro,
-                                               ((16 * rb + l16) * DV + 8 * cv) * 2, 0, 0);
+                                               ((16 * rb + l16) * DV + 8 * cv) * 2, 0, kStoreNT);
     }
 }
 
