@@ -254,7 +254,8 @@ __device__ __forceinline__ void store_rows_t(T *g, long g_ld, const T *s, int s_
 }
 
 // Rows [0, valid) of a ROWS x COLS fp32 tile in LDS (row stride s_ld, a
-// multiple of 4) written to global memory as T with 16-byte stores.
+// multiple of 4) written to global memory as T with 16-byte non-temporal
+// stores (final outputs, not read again by the writer).
 template <typename T, int ROWS, int COLS, int NT>
 __device__ __forceinline__ void store_rows(T *g, long g_ld, const float *s, int s_ld, int valid)
 {
@@ -275,7 +276,9 @@ __device__ __forceinline__ void store_rows(T *g, long g_ld, const float *s, int 
                 o[i + 2] = from_f32<T>(x.z);
                 o[i + 3] = from_f32<T>(x.w);
             }
-            *reinterpret_cast<uint4 *>(g + row * g_ld + cv * V) = out;
+            typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, out),
+                                        reinterpret_cast<u32x4_t *>(g + row * g_ld + cv * V));
         }
     }
 }
