@@ -21,9 +21,9 @@
 // every product with a d_k or d_v dimension rounds its operands to bf16 for
 // bf16 MFMA, as the forward's bf16 path does; N and the C x C chain through
 // it (N^T dN N^T) stay fp32.  One workgroup of 8 waves per
-// chunk.  LDS holds K, two C x max(d_k, d_v) fp32 operand buffers and three
-// C x C matrices; the entry state and dS_out are read from the workspace
-// straight into MFMA registers.
+// chunk.  LDS holds K and two C x max(d_k, d_v) operand buffers in the input
+// dtype and three fp32 C x C matrices; the entry state and dS_out are read
+// from the workspace straight into MFMA registers.
 #include "efla_device.h"
 #include "efla_launch.h"
 
@@ -56,36 +56,47 @@ __device__ __forceinline__ void alpha_partials(int euler, float beta, float lamb
     da_dl = -beta * beta * gx;
 }
 
-template <int DK, int DV, int C>
+// LDS of the gradient kernel.  K and the two C x max(d_k, d_v) operand
+// buffers are held in the input dtype T: for bf16 inputs every reader of them
+// feeds bf16 MFMA or rounds to the bf16 output, so storing them rounded
+// changes no result and halves their LDS traffic.  Rows are padded by 16
+// bytes.  The C x C matrices are fp32.
+template <typename T, int DK, int DV, int C>
 struct GradLayout {
     static constexpr int NW = 8;
-    static constexpr int DM = DK > DV ? DK : DV;
-    static constexpr int LDK = DK + 4, LDV = DV + 4, LDC = C + 4;
-    static constexpr int B1a = (C * LDV > 2 * C * LDC) ? C * LDV : 2 * C * LDC;   // floats
-    static constexpr int B1 = B1a > C * LDK ? B1a : C * LDK;
-    static constexpr int B2 = (C * LDV > C * LDK) ? C * LDV : C * LDK;
+    static constexpr int PAD = 16 / (int)sizeof(T);
+    static constexpr int LDK = DK + PAD, LDV = DV + PAD, LDC = C + 4;
+    static constexpr size_t kBytes = sizeof(T) * C * LDK, vBytes = sizeof(T) * C * LDV;
+    static constexpr size_t ccBytes = sizeof(float) * C * LDC;
+    static constexpr size_t dBytes = kBytes > vBytes ? kBytes : vBytes;
+    // B1 also holds two fp32 C x C matrices (dA and N^T dN) once E is dead
+    static constexpr size_t b1Bytes = dBytes > 2 * ccBytes ? dBytes : 2 * ccBytes;
     static constexpr size_t offK = 0;
-    static constexpr size_t offB1 = offK + sizeof(float) * C * LDK;
-    static constexpr size_t offB2 = offB1 + sizeof(float) * B1;
-    static constexpr size_t offGam = offB2 + sizeof(float) * B2;
-    static constexpr size_t offN = offGam + sizeof(float) * C * LDC;
-    static constexpr size_t offD = offN + sizeof(float) * C * LDC;
+    static constexpr size_t offB1 = offK + kBytes;
+    static constexpr size_t offB2 = offB1 + b1Bytes;
+    static constexpr size_t offGam = offB2 + dBytes;
+    static constexpr size_t offN = offGam + ccBytes;
+    static constexpr size_t offD = offN + ccBytes;
     // alpha, lambda, beta, dlambda [C] and two [NW][C] tables of per-wave
     // partial sums of dalpha (summed in a fixed order: deterministic)
-    static constexpr size_t offVec = offD + sizeof(float) * C * LDC;
+    static constexpr size_t offVec = offD + ccBytes;
     static constexpr size_t bytes = offVec + sizeof(float) * (4 + 2 * NW) * C;
+    static_assert(kBytes % 16 == 0 && vBytes % 16 == 0 && ccBytes % 16 == 0, "16-byte aligned buffers");
 };
 
-// bf16 MFMA on fp32 operands held in LDS or registers: each operand is
-// rounded to bf16 as it is fed (fp32 accumulation), which is how the bf16
-// inputs' path multiplies; the fp32 inputs' path keeps fp32 MFMA.
+// bf16 MFMA on operands held in LDS or registers: an fp32 operand is rounded
+// to bf16 as it is fed (fp32 accumulation), a bf16 one is read as it is; the
+// fp32 inputs' path keeps fp32 MFMA.
 
-// Four consecutive-k elements of an fp32 operand in LDS, as bf16: element
-// (idx, k) at M[idx*ld + k] (one 16-byte read; ld and k multiples of 4) or,
-// STRIDED, at M[k*ld + idx].
+// Four consecutive-k elements (idx, k .. k+3) of an LDS operand as bf16,
+// idx = idx0 + l16: element (idx, k) at M[idx*ld + k] or, STRIDED, at
+// M[k*ld + idx].  fp32: one 16-byte read or four 4-byte reads, rounded; bf16:
+// one 8-byte read or one transposing read (every lane of the group must take
+// part).
 template <bool STRIDED>
-__device__ __forceinline__ bf16x4 run4f(const float *M, int ld, int idx, int k)
+__device__ __forceinline__ bf16x4 op4(const float *M, int ld, int idx0, int k)
 {
+    const int idx = idx0 + (threadIdx.x & 15);
     if constexpr (!STRIDED) {
         return to_bf16x4(*reinterpret_cast<const f32x4 *>(M + idx * ld + k));
     } else {
@@ -93,67 +104,81 @@ __device__ __forceinline__ bf16x4 run4f(const float *M, int ld, int idx, int k)
                                M[(k + 3) * ld + idx]});
     }
 }
-
-// out[mt] += A[16mt.., 0:16KT] * B, A fp32 in LDS, B as KT acc tiles (PERM
-// map): the bf16 counterpart of mm_acc_b<float, ...>.
-template <int MT, int KT, bool LOWER, bool A_STRIDED>
-__device__ __forceinline__ void mm_acc_b_bf16(f32x4 (&out)[MT], const float *A, int lda,
-                                              const f32x4 (&Bacc)[KT])
+template <bool STRIDED>
+__device__ __forceinline__ bf16x4 op4(const __bf16 *M, int ld, int idx0, int k)
 {
-    const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+    return run4_lds<STRIDED>(M, ld, idx0, k);
+}
+
+// Four elements of T in registers: bf16x4 for bf16, f32x4 for fp32.
+template <typename T> struct QuadOf { using type = f32x4; };
+template <> struct QuadOf<__bf16> { using type = bf16x4; };
+template <typename T> using Quad = typename QuadOf<T>::type;
+
+// out[mt] += A[16mt.., 0:16KT] * B, A in LDS, B as KT acc tiles (PERM map):
+// the bf16 counterpart of mm_acc_b<float, ...>.  B is given in fp32 (rounded
+// as it is fed) or already in bf16.
+__device__ __forceinline__ bf16x4 as_bf16x4(f32x4 x) { return to_bf16x4(x); }
+__device__ __forceinline__ bf16x4 as_bf16x4(bf16x4 x) { return x; }
+
+template <int MT, int KT, bool LOWER, bool A_STRIDED, typename TA, typename TB>
+__device__ __forceinline__ void mm_acc_b_bf16(f32x4 (&out)[MT], const TA *A, int lda,
+                                              const TB (&Bacc)[KT])
+{
+    const int lane = threadIdx.x & 63, g = lane >> 4;
 #pragma unroll
     for (int s = 0; s < (KT + 1) / 2; ++s) {
         const bool two = 2 * s + 1 < KT;
-        const bf16x8 b = cat(to_bf16x4(Bacc[2 * s]), two ? to_bf16x4(Bacc[2 * s + 1]) : to_bf16x4(zero4()));
+        const bf16x8 b = cat(as_bf16x4(Bacc[2 * s]), two ? as_bf16x4(Bacc[2 * s + 1]) : to_bf16x4(zero4()));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             if (LOWER && 2 * s > mt) continue;
-            const int i = 16 * mt + l16;
-            const bf16x4 a1 = run4f<A_STRIDED>(A, lda, i, 32 * s + 4 * g);
-            const bf16x4 a2 = two ? run4f<A_STRIDED>(A, lda, i, 32 * s + 16 + 4 * g) : to_bf16x4(zero4());
+            const bf16x4 a1 = op4<A_STRIDED>(A, lda, 16 * mt, 32 * s + 4 * g);
+            const bf16x4 a2 = two ? op4<A_STRIDED>(A, lda, 16 * mt, 32 * s + 16 + 4 * g) : to_bf16x4(zero4());
             out[mt] = mma(cat(a1, a2), b, out[mt]);
         }
     }
 }
 
-// acc += A[i0:i0+16, 0:K] * B[0:K, j0:j0+16], both fp32 in LDS (element
-// (i,k) of A at A[i*lda+k], or A[k*lda+i] if A_STRIDED; (k,j) of B at
-// B[j*ldb+k], or B[k*ldb+j] if B_STRIDED): the bf16 counterpart of
-// mm_lds<float, ...>.  k >= klim (rounded up to 32) is skipped.
-template <int K, bool A_STRIDED, bool B_STRIDED>
-__device__ __forceinline__ f32x4 mm_lds_bf16(f32x4 acc, const float *A, int lda, int i0,
-                                             const float *B, int ldb, int j0, int klim = K)
+// acc += A[i0:i0+16, 0:K] * B[0:K, j0:j0+16], both in LDS (element (i,k) of
+// A at A[i*lda+k], or A[k*lda+i] if A_STRIDED; (k,j) of B at B[j*ldb+k], or
+// B[k*ldb+j] if B_STRIDED): the bf16 counterpart of mm_lds<float, ...>.
+// k >= klim (rounded up to 32) is skipped.  K = 16: lane groups 2 and 3 of
+// the 32-wide k-block lie past K; they read an in-range block (no lane may
+// skip a transposing read) and zero it.
+template <int K, bool A_STRIDED, bool B_STRIDED, typename TA, typename TB>
+__device__ __forceinline__ f32x4 mm_lds_bf16(f32x4 acc, const TA *A, int lda, int i0,
+                                             const TB *B, int ldb, int j0, int klim = K)
 {
-    const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+    const int lane = threadIdx.x & 63, g = lane >> 4;
 #pragma unroll
     for (int s = 0; s < (K + 31) / 32; ++s) {
         if (32 * s >= klim) break;
         const int k = 32 * s + 8 * g;
-        bf16x8 a, b;
-        if (k < K) {
-            a = cat(run4f<A_STRIDED>(A, lda, i0 + l16, k), run4f<A_STRIDED>(A, lda, i0 + l16, k + 4));
-            b = cat(run4f<B_STRIDED>(B, ldb, j0 + l16, k), run4f<B_STRIDED>(B, ldb, j0 + l16, k + 4));
-        } else {   // K = 16: the upper half of the k-block is zero
-            a = cat(to_bf16x4(zero4()), to_bf16x4(zero4()));
-            b = a;
-        }
+        const bool in = k < K;
+        const int kr = in ? k : k - 16;
+        bf16x8 a = cat(op4<A_STRIDED>(A, lda, i0, kr), op4<A_STRIDED>(A, lda, i0, kr + 4));
+        bf16x8 b = cat(op4<B_STRIDED>(B, ldb, j0, kr), op4<B_STRIDED>(B, ldb, j0, kr + 4));
+        const bf16x8 z = cat(to_bf16x4(zero4()), to_bf16x4(zero4()));
+        a = in ? a : z;
+        b = in ? b : z;
         acc = mma(a, b, acc);
     }
     return acc;
 }
 
 // The products with a d_k or d_v dimension, on bf16 MFMA for bf16 inputs and
-// fp32 MFMA for fp32 inputs.
-template <typename T, int MT, int KT, bool LOWER = false, bool A_STRIDED = false>
-__device__ __forceinline__ void mm_b(f32x4 (&out)[MT], const float *A, int lda,
-                                    const f32x4 (&Bacc)[KT])
+// fp32 MFMA for fp32 inputs (whose operands are then all fp32).
+template <typename T, int MT, int KT, bool LOWER = false, bool A_STRIDED = false, typename TA,
+          typename TB>
+__device__ __forceinline__ void mm_b(f32x4 (&out)[MT], const TA *A, int lda, const TB (&Bacc)[KT])
 {
     if constexpr (is_bf16<T>) mm_acc_b_bf16<MT, KT, LOWER, A_STRIDED>(out, A, lda, Bacc);
     else mm_acc_b<float, MT, KT, LOWER, A_STRIDED>(out, A, lda, Bacc);
 }
 
-template <typename T, int K, bool A_STRIDED, bool B_STRIDED>
-__device__ __forceinline__ f32x4 mm_t(f32x4 acc, const float *A, int lda, int i0, const float *B,
+template <typename T, int K, bool A_STRIDED, bool B_STRIDED, typename TA, typename TB>
+__device__ __forceinline__ f32x4 mm_t(f32x4 acc, const TA *A, int lda, int i0, const TB *B,
                                       int ldb, int j0, int klim = K)
 {
     if constexpr (is_bf16<T>)
@@ -161,12 +186,31 @@ __device__ __forceinline__ f32x4 mm_t(f32x4 acc, const float *A, int lda, int i0
     else return mm_lds<float, K, A_STRIDED, B_STRIDED>(acc, A, lda, i0, B, ldb, j0, klim);
 }
 
-// Four consecutive elements (8- or 16-byte aligned) widened to fp32.
-__device__ __forceinline__ f32x4 load4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
-__device__ __forceinline__ f32x4 load4(const __bf16 *p)
+// Rows [0, valid) of a ROWS x COLS tile of T in LDS (row stride s_ld, 16-byte
+// aligned rows) to global memory with 16-byte non-temporal stores (final
+// outputs, not read again by the writer).
+template <typename T, int ROWS, int COLS, int NT>
+__device__ __forceinline__ void store_rows_nt(T *g, long g_ld, const T *s, int s_ld, int valid)
 {
-    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
-    return f32x4{to_f32(x[0]), to_f32(x[1]), to_f32(x[2]), to_f32(x[3])};
+    constexpr int V = 16 / sizeof(T), VPR = COLS / V, N = ROWS * VPR;
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int j = 0; j < (N + NT - 1) / NT; ++j) {
+        const int idx = (int)threadIdx.x + j * NT;
+        const int row = idx / VPR, cv = idx % VPR;
+        if ((N % NT == 0 || idx < N) && row < valid)
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t *>(s + row * s_ld + cv * V),
+                                        reinterpret_cast<u32x4_t *>(g + row * g_ld + cv * V));
+    }
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses complete,
+// then every wave arrives.  Unlike __syncthreads it does not wait for the
+// wave's global loads, which may stay in flight into later phases (the
+// compiler waits for each load where its register is first read).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Sum over the 16 lanes of a lane group (one acc-tile row).
@@ -188,22 +232,22 @@ __global__ __launch_bounds__(512) void grad_kernel(
     T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ dbeta, int L, int nchunks,
     int euler)
 {
-    using Lay = GradLayout<DK, DV, C>;
+    using Lay = GradLayout<T, DK, DV, C>;
     constexpr int NW = Lay::NW, NT = 64 * NW, MC = C / 16, MK = DK / 16, MV = DV / 16;
     constexpr int LDK = Lay::LDK, LDV = Lay::LDV, LDC = Lay::LDC;
     constexpr int TPW = (MC * MC + NW - 1) / NW;   // C x C tiles per wave
     static_assert(MC <= 4 && NW == 8, "a wave's C x C tiles t, t + NW lie in distinct block rows");
     extern __shared__ __align__(16) char smem[];
-    float *sK = reinterpret_cast<float *>(smem + Lay::offK);
-    float *sB1 = reinterpret_cast<float *>(smem + Lay::offB1);
-    float *sB2 = reinterpret_cast<float *>(smem + Lay::offB2);
+    T *sK = reinterpret_cast<T *>(smem + Lay::offK);
+    T *sB1 = reinterpret_cast<T *>(smem + Lay::offB1);
+    T *sB2 = reinterpret_cast<T *>(smem + Lay::offB2);
     float *sGam = reinterpret_cast<float *>(smem + Lay::offGam);
     float *sN = reinterpret_cast<float *>(smem + Lay::offN);
     float *sD = reinterpret_cast<float *>(smem + Lay::offD);
     float *sAl = reinterpret_cast<float *>(smem + Lay::offVec);
     float *sLam = sAl + C, *sBeta = sAl + 2 * C, *sDl = sAl + 3 * C;
     float *sPT = sAl + 4 * C, *sPG = sPT + NW * C;   // [NW][C] partials of dalpha
-    float *sdA = sB1, *sZ = sB1 + C * LDC;   // C x C views of B1 once E is dead
+    float *sdA = reinterpret_cast<float *>(smem + Lay::offB1), *sZ = sdA + C * LDC;   // B1 once E is dead
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
     const int bh = blockIdx.x / nchunks, c = blockIdx.x - bh * nchunks;
@@ -213,46 +257,55 @@ __global__ __launch_bounds__(512) void grad_kernel(
     const T *dSo = dSout + ((long)bh * nchunks + c) * DK * DV;
     const T *dEg = dE + ((long)bh * nchunks * C + (long)c * C) * DV;
 
-    // ---- every input tile in flight at once (16-byte loads): K, V, dE into
-    // LDS now, dO and Q held in registers until their buffer is free; the
-    // entry-state columns this wave multiplies first straight into registers
+    // ---- every input in flight at once, in the order of first use: the
+    // per-token scalars and K (Gamma, N), the entry-state columns this wave
+    // multiplies first (straight into registers), V and dE, the rows of S and
+    // dS_out, then dO and Q.  Loads return in order and the barriers below wait
+    // for LDS only, so each wait covers just the loads a phase needs and the
+    // rest stay in flight under the earlier phases.
+    float al0 = 0.f, la0 = 0.f, be0 = 0.f;
+    if (tid < C && tid < valid) {
+        al0 = alpha[tok0 + tid];
+        la0 = lambda[tok0 + tid];
+        be0 = beta[tok0 + tid];
+    }
     TileRegs<T, C, DK, NT> rK, rQ;
     TileRegs<T, C, DV, NT> rV, rO;
     TileRegs<T, C, DV, NT> rE;
     rK.load(k + tok0 * DK, DK, valid);
-    rV.load(v + tok0 * DV, DV, valid);
-    rE.load(dEg, DV, valid);
-    rO.load(dout + tok0 * DV, DV, valid);
-    rQ.load(q + tok0 * DK, DK, valid);
-    f32x4 S[MK], SinT[MV], dSoT[MV];
-    if (wv < MV) {
+    // kept in the input dtype until the phase that reads them: widening
+    // them here would wait for the loads at once
+    T Sr[MK][4];
+    Quad<T> SinT[MV], dSoT[MV];
+    if (MV >= NW || wv < MV) {
 #pragma unroll
         for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) S[mk][r] = to_f32(Sst[(16 * mk + 4 * g + r) * DV + 16 * wv + l16]);
+            for (int r = 0; r < 4; ++r) Sr[mk][r] = Sst[(16 * mk + 4 * g + r) * DV + 16 * wv + l16];
     }
-    if (wv < MK) {   // rows a = 16 wv + l16 of S and dS_out: B operands (k = d_v, j = a)
+    rV.load(v + tok0 * DV, DV, valid);
+    rE.load(dEg, DV, valid);
+    if (MK >= NW || wv < MK) {   // rows a = 16 wv + l16 of S and dS_out: B operands (k = d_v, j = a)
         const int a = 16 * wv + l16;
 #pragma unroll
         for (int kt = 0; kt < MV; ++kt) {
-            SinT[kt] = load4(Sst + a * DV + 16 * kt + 4 * g);
-            dSoT[kt] = load4(dSo + a * DV + 16 * kt + 4 * g);
+            SinT[kt] = *reinterpret_cast<const Quad<T> *>(Sst + a * DV + 16 * kt + 4 * g);
+            dSoT[kt] = *reinterpret_cast<const Quad<T> *>(dSo + a * DV + 16 * kt + 4 * g);
         }
     }
-    rK.store_f32(sK, LDK, valid);
-    rV.store_f32(sB1, LDV, valid);
-    rE.store_f32(sB2, LDV, valid);
+    rO.load(dout + tok0 * DV, DV, valid);
+    rQ.load(q + tok0 * DK, DK, valid);
+    rK.store(sK, LDK, valid);
 
     // ---- per-token scalars; Gamma and N -------------------------------------
     for (int e = tid; e < C * LDC; e += NT) sN[e] = 0.f;
     if (tid < C) {
-        const bool ok = tid < valid;
-        sAl[tid] = ok ? alpha[tok0 + tid] : 0.f;
-        sLam[tid] = ok ? lambda[tok0 + tid] : 0.f;
-        sBeta[tid] = ok ? beta[tok0 + tid] : 0.f;
+        sAl[tid] = al0;
+        sLam[tid] = la0;
+        sBeta[tid] = be0;
     }
     for (int e = tid; e < 2 * NW * C; e += NT) sPT[e] = 0.f;
-    __syncthreads();
+    lds_barrier();
     for (int t = wv; t < MC * MC; t += NW) {
         const int it = t / MC, jt = t - it * MC;
         if (jt > it) continue;
@@ -260,7 +313,7 @@ __global__ __launch_bounds__(512) void grad_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) sGam[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = acc[r];
     }
-    __syncthreads();
+    lds_barrier();
     // diagonal 16x16 blocks: N_ij = delta_ij - alpha_i sum_{m<i} Gamma_im N_mj
     if (wv == 0 && g < MC) {
         const int b0 = 16 * g, j = l16;
@@ -276,7 +329,7 @@ __global__ __launch_bounds__(512) void grad_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) sN[(b0 + i) * LDC + b0 + j] = n[i];
     }
-    __syncthreads();
+    lds_barrier();
     // blocks below: N_IJ = -N_II D_I sum_{M=J}^{I-1} Gamma_IM N_MJ, by block distance
     for (int dist = 1; dist < MC; ++dist) {
         if (wv < MC - dist) {
@@ -301,7 +354,16 @@ __global__ __launch_bounds__(512) void grad_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) sN[(16 * bi + 4 * g + r) * LDC + 16 * bj + l16] = -x[r];
         }
-        __syncthreads();
+        if (dist == MC - 1) {   // V and dE to LDS, for the first phase that reads them
+            rV.store(sB1, LDV, valid);
+            rE.store(sB2, LDV, valid);
+        }
+        lds_barrier();
+    }
+    if constexpr (MC == 1) {
+        rV.store(sB1, LDV, valid);
+        rE.store(sB2, LDV, valid);
+        lds_barrier();
     }
 
     // ---- per d_v column tile (wave wv owns columns 16wv .. 16wv+15) ----------
@@ -313,15 +375,19 @@ __global__ __launch_bounds__(512) void grad_kernel(
         for (int mt = 0; mt < MC; ++mt) {
             X[mt] = zero4();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dEc[mt][r] = sB2[(16 * mt + 4 * g + r) * LDV + col];
+            for (int r = 0; r < 4; ++r) dEc[mt][r] = to_f32(sB2[(16 * mt + 4 * g + r) * LDV + col]);
         }
+        f32x4 S[MK];
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk)
+            S[mk] = f32x4{to_f32(Sr[mk][0]), to_f32(Sr[mk][1]), to_f32(Sr[mk][2]), to_f32(Sr[mk][3])};
         mm_b<T, MC, MK>(X, sK, LDK, S);   // K S
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * mt + 4 * g + r;
-                X[mt][r] = sB1[row * LDV + col] - X[mt][r];   // V - K S
+                X[mt][r] = to_f32(sB1[row * LDV + col]) - X[mt][r];   // V - K S
                 DXv[mt][r] = sAl[row] * X[mt][r];
             }
             E[mt] = zero4();
@@ -337,11 +403,11 @@ __global__ __launch_bounds__(512) void grad_kernel(
                 dX[mt][r] = sAl[row] * Y[mt][r];
                 const float part = row16_sum(X[mt][r] * Y[mt][r]);
                 if (l16 == 0) sPT[wv * C + row] = part;
-                sB1[row * LDV + col] = DXv[mt][r];   // dE is already in B2
+                sB1[row * LDV + col] = from_f32<T>(DXv[mt][r]);   // dE is already in B2
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     // dN = dE (D X)^T on and below the diagonal blocks (zero above)
     for (int t = wv; t < MC * MC; t += NW) {
         const int it = t / MC, jt = t - it * MC;
@@ -350,7 +416,7 @@ __global__ __launch_bounds__(512) void grad_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) sD[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = acc[r];
     }
-    __syncthreads();
+    lds_barrier();
     if (wv < MV) {
         const int col = 16 * wv + l16;
 #pragma unroll
@@ -358,12 +424,12 @@ __global__ __launch_bounds__(512) void grad_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * mt + 4 * g + r;
-                sB1[row * LDV + col] = E[mt][r];
-                sB2[row * LDV + col] = dX[mt][r];
+                sB1[row * LDV + col] = from_f32<T>(E[mt][r]);
+                sB2[row * LDV + col] = from_f32<T>(dX[mt][r]);
             }
     }
-    __syncthreads();
-    store_rows<T, C, DV, NT>(dv + tok0 * DV, DV, sB2, LDV, valid);   // dv = dX
+    lds_barrier();
+    store_rows_nt<T, C, DV, NT>(dv + tok0 * DV, DV, sB2, LDV, valid);   // dv = dX
 
     // ---- per d_k column tile (wave wv owns output columns 16wv .. 16wv+15) ---
     f32x4 dQw[MC], dKw[MC];
@@ -381,9 +447,9 @@ __global__ __launch_bounds__(512) void grad_kernel(
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) dKw[mt] -= t1[mt];
     }
-    __syncthreads();
-    rO.store_f32(sB2, LDV, valid);
-    __syncthreads();
+    lds_barrier();
+    rO.store(sB2, LDV, valid);
+    lds_barrier();
     if (wv < MK) mm_b<T, MC, MV>(dQw, sB2, LDV, SinT);   // dO S^T
     // dA = tril(dO E^T), diagonal included
     f32x4 dAr[TPW];
@@ -399,7 +465,7 @@ __global__ __launch_bounds__(512) void grad_kernel(
                 if (16 * jt + l16 > 16 * it + 4 * g + r) dAr[u][r] = 0.f;
         }
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         const int t = wv + u * NW;
@@ -409,7 +475,7 @@ __global__ __launch_bounds__(512) void grad_kernel(
             for (int r = 0; r < 4; ++r) sdA[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = dAr[u][r];
         }
     }
-    rQ.store_f32(sB2, LDK, valid);
+    rQ.store(sB2, LDK, valid);
     // Z = N^T dN
     for (int t = wv; t < MC * MC; t += NW) {
         const int it = t / MC, jt = t - it * MC;
@@ -417,7 +483,7 @@ __global__ __launch_bounds__(512) void grad_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) sZ[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = acc[r];
     }
-    __syncthreads();
+    lds_barrier();
     if (wv < MK) {
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) {
@@ -447,7 +513,7 @@ __global__ __launch_bounds__(512) void grad_kernel(
             }
         }
     }
-    __syncthreads();   // every read of dN (Z) and of dA, Q above is done
+    lds_barrier();   // every read of dN (Z) and of dA, Q above is done
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         const int t = wv + u * NW;
@@ -457,7 +523,7 @@ __global__ __launch_bounds__(512) void grad_kernel(
             for (int r = 0; r < 4; ++r) sD[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = dGr[u][r];
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < C) {
         float da_db, da_dl;
         alpha_partials(euler, sBeta[tid], sLam[tid], da_db, da_dl);
@@ -476,7 +542,7 @@ __global__ __launch_bounds__(512) void grad_kernel(
             dKw[mt] = mm_t<T, C, true, true>(dKw[mt], sD, LDC, 16 * mt, sK, LDK, 16 * wv);
         }
     }
-    __syncthreads();   // B1 and B2 are free: stage dq, dk for 16-byte stores
+    lds_barrier();   // B1 and B2 are free: stage dq, dk for 16-byte stores
     if (wv < MK) {
         const int a = 16 * wv + l16;
 #pragma unroll
@@ -484,13 +550,13 @@ __global__ __launch_bounds__(512) void grad_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * mt + 4 * g + r;
-                sB1[row * LDK + a] = dQw[mt][r];
-                sB2[row * LDK + a] = dKw[mt][r] + 2.f * sDl[row] * sK[row * LDK + a];
+                sB1[row * LDK + a] = from_f32<T>(dQw[mt][r]);
+                sB2[row * LDK + a] = from_f32<T>(dKw[mt][r] + 2.f * sDl[row] * to_f32(sK[row * LDK + a]));
             }
     }
-    __syncthreads();
-    store_rows<T, C, DK, NT>(dq + tok0 * DK, DK, sB1, LDK, valid);
-    store_rows<T, C, DK, NT>(dk + tok0 * DK, DK, sB2, LDK, valid);
+    lds_barrier();
+    store_rows_nt<T, C, DK, NT>(dq + tok0 * DK, DK, sB1, LDK, valid);
+    store_rows_nt<T, C, DK, NT>(dk + tok0 * DK, DK, sB2, LDK, valid);
 }
 
 template <typename T, int DK, int DV, int C>
@@ -499,7 +565,7 @@ hipError_t launch_grad(const void *q, const void *k, const void *v, const void *
                        const void *states, const void *dSout, const void *dE, void *dq,
                        void *dk, void *dv, float *dbeta, int BH, int L, bool euler, hipStream_t st)
 {
-    using Lay = GradLayout<DK, DV, C>;
+    using Lay = GradLayout<T, DK, DV, C>;
     static_assert(Lay::bytes <= 160 * 1024, "gradient kernel LDS");
     const int nchunks = (L + C - 1) / C;
     if (BH == 0 || nchunks == 0) return hipSuccess;
