@@ -69,8 +69,15 @@ struct GradLayout {
     static constexpr size_t kBytes = sizeof(T) * C * LDK, vBytes = sizeof(T) * C * LDV;
     static constexpr size_t ccBytes = sizeof(float) * C * LDC;
     static constexpr size_t dBytes = kBytes > vBytes ? kBytes : vBytes;
+    // bf16 inputs: the entry state is staged through B1 (d_k x d_v) before V
+    // is, and N has a bf16 copy (the operand of the products with d_v)
+    static constexpr bool BF = is_bf16<T>;
+    static constexpr int LDN = C + 8;
+    static constexpr size_t sBytes = BF ? sizeof(T) * DK * LDV : 0;
+    static constexpr size_t nbBytes = BF ? 2 * C * LDN : 0;
     // B1 also holds two fp32 C x C matrices (dA and N^T dN) once E is dead
-    static constexpr size_t b1Bytes = dBytes > 2 * ccBytes ? dBytes : 2 * ccBytes;
+    static constexpr size_t b1a = dBytes > 2 * ccBytes ? dBytes : 2 * ccBytes;
+    static constexpr size_t b1Bytes = b1a > sBytes ? b1a : sBytes;
     static constexpr size_t offK = 0;
     static constexpr size_t offB1 = offK + kBytes;
     static constexpr size_t offB2 = offB1 + b1Bytes;
@@ -79,9 +86,11 @@ struct GradLayout {
     static constexpr size_t offD = offN + ccBytes;
     // alpha, lambda, beta, dlambda [C] and two [NW][C] tables of per-wave
     // partial sums of dalpha (summed in a fixed order: deterministic)
-    static constexpr size_t offVec = offD + ccBytes;
+    static constexpr size_t offNb = offD + ccBytes;
+    static constexpr size_t offVec = offNb + nbBytes;
     static constexpr size_t bytes = offVec + sizeof(float) * (4 + 2 * NW) * C;
-    static_assert(kBytes % 16 == 0 && vBytes % 16 == 0 && ccBytes % 16 == 0, "16-byte aligned buffers");
+    static_assert(kBytes % 16 == 0 && vBytes % 16 == 0 && ccBytes % 16 == 0 && nbBytes % 16 == 0,
+                  "16-byte aligned buffers");
 };
 
 // bf16 MFMA on operands held in LDS or registers: an fp32 operand is rounded
@@ -213,13 +222,23 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Sum over the 16 lanes of a lane group (one acc-tile row).
+// Sum over the 16 lanes of a lane group (one acc-tile row), by DPP moves
+// within the row: pairs, then quads, then lane 0 adds lane 4 (a rotation of
+// the row by 12) and lane 8 (by 8).  Lane 0 holds the butterfly sum
+// ((x0 + x1) + (x2 + x3)) + ((x4 + x5) + (x6 + x7)) + (lanes 8 .. 15 alike);
+// the other lanes hold partial sums.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf,
+                                                              0xf, false));
+}
 __device__ __forceinline__ float row16_sum(float x)
 {
-    x += __shfl_xor(x, 1, 64);
-    x += __shfl_xor(x, 2, 64);
-    x += __shfl_xor(x, 4, 64);
-    x += __shfl_xor(x, 8, 64);
+    x += dpp_mov<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    x += dpp_mov<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    x += dpp_mov<0x12C>(x);   // row_ror:12
+    x += dpp_mov<0x128>(x);   // row_ror:8
     return x;
 }
 
@@ -244,6 +263,10 @@ __global__ __launch_bounds__(512) void grad_kernel(
     float *sGam = reinterpret_cast<float *>(smem + Lay::offGam);
     float *sN = reinterpret_cast<float *>(smem + Lay::offN);
     float *sD = reinterpret_cast<float *>(smem + Lay::offD);
+    __bf16 *sNb = reinterpret_cast<__bf16 *>(smem + Lay::offNb);   // bf16 inputs only
+    T *sS = sB1;                                                      // bf16 inputs: S, phases 0-1
+    constexpr bool BF = Lay::BF;
+    constexpr int LDN = Lay::LDN;
     float *sAl = reinterpret_cast<float *>(smem + Lay::offVec);
     float *sLam = sAl + C, *sBeta = sAl + 2 * C, *sDl = sAl + 3 * C;
     float *sPT = sAl + 4 * C, *sPG = sPT + NW * C;   // [NW][C] partials of dalpha
@@ -272,33 +295,52 @@ __global__ __launch_bounds__(512) void grad_kernel(
     TileRegs<T, C, DK, NT> rK, rQ;
     TileRegs<T, C, DV, NT> rV, rO;
     TileRegs<T, C, DV, NT> rE;
+    TileRegs<T, DK, DV, NT> rS;
     rK.load(k + tok0 * DK, DK, valid);
-    // kept in the input dtype until the phase that reads them: widening
-    // them here would wait for the loads at once
+    // The entry state S: the columns 16 wv .. of this wave (the B operand of
+    // K S, tiles kt = rows 16 kt ..) and its rows 16 wv + l16 (of S^T).
+    // bf16: staged through LDS with 16-byte loads (then one transposing or
+    // 8-byte read per tile); fp32: straight from memory, kept in the input
+    // dtype until the phase that reads them (widening them here would wait
+    // for the loads at once).
     T Sr[MK][4];
-    Quad<T> SinT[MV], dSoT[MV];
-    if (MV >= NW || wv < MV) {
+    Quad<T> Sb[MK], SinT[MV], dSoT[MV];
+    if constexpr (BF) {
+        rS.load(Sst, DV, DK);
+    } else if (MV >= NW || wv < MV) {
 #pragma unroll
         for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
             for (int r = 0; r < 4; ++r) Sr[mk][r] = Sst[(16 * mk + 4 * g + r) * DV + 16 * wv + l16];
     }
+    if constexpr (BF) __builtin_amdgcn_sched_barrier(0);   // keep the issue order of the load groups
     rV.load(v + tok0 * DV, DV, valid);
     rE.load(dEg, DV, valid);
-    if (MK >= NW || wv < MK) {   // rows a = 16 wv + l16 of S and dS_out: B operands (k = d_v, j = a)
-        const int a = 16 * wv + l16;
+    if constexpr (BF) __builtin_amdgcn_sched_barrier(0);
+    // rows a = 16 wv + l16 of S and dS_out: B operands (k = d_v, j = a).
+    // fp32: issued after the X / E / Y phase, whose registers they would crowd
+    auto load_rows = [&]() {
+        if (MK >= NW || wv < MK) {
+            const int a = 16 * wv + l16;
 #pragma unroll
-        for (int kt = 0; kt < MV; ++kt) {
-            SinT[kt] = *reinterpret_cast<const Quad<T> *>(Sst + a * DV + 16 * kt + 4 * g);
-            dSoT[kt] = *reinterpret_cast<const Quad<T> *>(dSo + a * DV + 16 * kt + 4 * g);
+            for (int kt = 0; kt < MV; ++kt) {
+                if constexpr (!BF) SinT[kt] = *reinterpret_cast<const Quad<T> *>(Sst + a * DV + 16 * kt + 4 * g);
+                dSoT[kt] = *reinterpret_cast<const Quad<T> *>(dSo + a * DV + 16 * kt + 4 * g);
+            }
         }
-    }
+    };
+    if constexpr (BF) load_rows();
+    if constexpr (BF) __builtin_amdgcn_sched_barrier(0);
     rO.load(dout + tok0 * DV, DV, valid);
     rQ.load(q + tok0 * DK, DK, valid);
+    if constexpr (BF) __builtin_amdgcn_sched_barrier(0);
     rK.store(sK, LDK, valid);
+    if constexpr (BF) rS.store(sS, LDV, DK);
 
     // ---- per-token scalars; Gamma and N -------------------------------------
     for (int e = tid; e < C * LDC; e += NT) sN[e] = 0.f;
+    if constexpr (BF)
+        for (int e = tid; e < C * LDN / 2; e += NT) reinterpret_cast<unsigned *>(sNb)[e] = 0u;
     if (tid < C) {
         sAl[tid] = al0;
         sLam[tid] = la0;
@@ -306,6 +348,16 @@ __global__ __launch_bounds__(512) void grad_kernel(
     }
     for (int e = tid; e < 2 * NW * C; e += NT) sPT[e] = 0.f;
     lds_barrier();
+    if constexpr (BF) {   // S from its LDS staging (B1 is free again after the N phases)
+        if (MV >= NW || wv < MV) {
+#pragma unroll
+            for (int kt = 0; kt < MK; ++kt) Sb[kt] = run4_lds<true>(sS, LDV, 16 * wv, 16 * kt + 4 * g);
+        }
+        if (MK >= NW || wv < MK) {
+#pragma unroll
+            for (int kt = 0; kt < MV; ++kt) SinT[kt] = run4_lds<false>(sS, LDV, 16 * wv, 16 * kt + 4 * g);
+        }
+    }
     for (int t = wv; t < MC * MC; t += NW) {
         const int it = t / MC, jt = t - it * MC;
         if (jt > it) continue;
@@ -327,7 +379,10 @@ __global__ __launch_bounds__(512) void grad_kernel(
             n[i] = (i == j ? 1.f : 0.f) - sAl[b0 + i] * acc;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sN[(b0 + i) * LDC + b0 + j] = n[i];
+        for (int i = 0; i < 16; ++i) {
+            sN[(b0 + i) * LDC + b0 + j] = n[i];
+            if constexpr (BF) sNb[(b0 + i) * LDN + b0 + j] = static_cast<__bf16>(n[i]);
+        }
     }
     lds_barrier();
     // blocks below: N_IJ = -N_II D_I sum_{M=J}^{I-1} Gamma_IM N_MJ, by block distance
@@ -352,7 +407,10 @@ __global__ __launch_bounds__(512) void grad_kernel(
                 x = mma(a, p[r], x);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sN[(16 * bi + 4 * g + r) * LDC + 16 * bj + l16] = -x[r];
+            for (int r = 0; r < 4; ++r) {
+                sN[(16 * bi + 4 * g + r) * LDC + 16 * bj + l16] = -x[r];
+                if constexpr (BF) sNb[(16 * bi + 4 * g + r) * LDN + 16 * bj + l16] = static_cast<__bf16>(-x[r]);
+            }
         }
         if (dist == MC - 1) {   // V and dE to LDS, for the first phase that reads them
             rV.store(sB1, LDV, valid);
@@ -377,11 +435,11 @@ __global__ __launch_bounds__(512) void grad_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) dEc[mt][r] = to_f32(sB2[(16 * mt + 4 * g + r) * LDV + col]);
         }
-        f32x4 S[MK];
+        if constexpr (!BF) {
 #pragma unroll
-        for (int mk = 0; mk < MK; ++mk)
-            S[mk] = f32x4{to_f32(Sr[mk][0]), to_f32(Sr[mk][1]), to_f32(Sr[mk][2]), to_f32(Sr[mk][3])};
-        mm_b<T, MC, MK>(X, sK, LDK, S);   // K S
+            for (int mk = 0; mk < MK; ++mk) Sb[mk] = Quad<T>{Sr[mk][0], Sr[mk][1], Sr[mk][2], Sr[mk][3]};
+        }
+        mm_b<T, MC, MK>(X, sK, LDK, Sb);   // K S
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) {
 #pragma unroll
@@ -393,8 +451,13 @@ __global__ __launch_bounds__(512) void grad_kernel(
             E[mt] = zero4();
             Y[mt] = zero4();
         }
-        mm_b<T, MC, MC, true, false>(E, sN, LDC, DXv);   // E = N (D X)
-        mm_b<T, MC, MC, false, true>(Y, sN, LDC, dEc);   // Y = N^T dE
+        if constexpr (BF) {
+            mm_b<T, MC, MC, true, false>(E, sNb, LDN, DXv);   // E = N (D X)
+            mm_b<T, MC, MC, false, true>(Y, sNb, LDN, dEc);   // Y = N^T dE
+        } else {
+            mm_b<T, MC, MC, true, false>(E, sN, LDC, DXv);
+            mm_b<T, MC, MC, false, true>(Y, sN, LDC, dEc);
+        }
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) {
 #pragma unroll
@@ -407,6 +470,7 @@ __global__ __launch_bounds__(512) void grad_kernel(
             }
         }
     }
+    if constexpr (!BF) load_rows();
     lds_barrier();
     // dN = dE (D X)^T on and below the diagonal blocks (zero above)
     for (int t = wv; t < MC * MC; t += NW) {
