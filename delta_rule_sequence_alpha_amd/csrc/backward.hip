@@ -271,6 +271,9 @@ __global__ __launch_bounds__(512) void grad_kernel(
     float *sLam = sAl + C, *sBeta = sAl + 2 * C, *sDl = sAl + 3 * C;
     float *sPT = sAl + 4 * C, *sPG = sPT + NW * C;   // [NW][C] partials of dalpha
     float *sdA = reinterpret_cast<float *>(smem + Lay::offB1), *sZ = sdA + C * LDC;   // B1 once E is dead
+    // bf16 inputs: dA (in B1) and dGam (in N's bf16 copy, free after the
+    // X / E / Y phase) are stored in bf16 -- they only feed bf16 MFMA
+    __bf16 *sdAb = reinterpret_cast<__bf16 *>(smem + Lay::offB1), *sdGb = sNb;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
     const int bh = blockIdx.x / nchunks, c = blockIdx.x - bh * nchunks;
@@ -536,7 +539,10 @@ __global__ __launch_bounds__(512) void grad_kernel(
         if (t < MC * MC) {
             const int it = t / MC, jt = t - it * MC;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sdA[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = dAr[u][r];
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (BF) sdAb[(16 * it + 4 * g + r) * LDN + 16 * jt + l16] = static_cast<__bf16>(dAr[u][r]);
+                else sdA[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = dAr[u][r];
+            }
         }
     }
     rQ.store(sB2, LDK, valid);
@@ -552,9 +558,13 @@ __global__ __launch_bounds__(512) void grad_kernel(
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) {
             // dq += dA K;  dk += dA^T Q
-            dQw[mt] = mm_t<T, C, false, true>(dQw[mt], sdA, LDC, 16 * mt, sK, LDK, 16 * wv,
-                                                    16 * mt + 16);
-            dKw[mt] = mm_t<T, C, true, true>(dKw[mt], sdA, LDC, 16 * mt, sB2, LDK, 16 * wv);
+            if constexpr (BF) {
+                dQw[mt] = mm_t<T, C, false, true>(dQw[mt], sdAb, LDN, 16 * mt, sK, LDK, 16 * wv, 16 * mt + 16);
+                dKw[mt] = mm_t<T, C, true, true>(dKw[mt], sdAb, LDN, 16 * mt, sB2, LDK, 16 * wv);
+            } else {
+                dQw[mt] = mm_t<T, C, false, true>(dQw[mt], sdA, LDC, 16 * mt, sK, LDK, 16 * wv, 16 * mt + 16);
+                dKw[mt] = mm_t<T, C, true, true>(dKw[mt], sdA, LDC, 16 * mt, sB2, LDK, 16 * wv);
+            }
         }
     }
     // dG = -strictly_lower(Z N^T); dalpha_i += sum_j dG_ij Gamma_ij; dGam = D dG
@@ -584,7 +594,10 @@ __global__ __launch_bounds__(512) void grad_kernel(
         if (t < MC * MC) {
             const int it = t / MC, jt = t - it * MC;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sD[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = dGr[u][r];
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (BF) sdGb[(16 * it + 4 * g + r) * LDN + 16 * jt + l16] = static_cast<__bf16>(dGr[u][r]);
+                else sD[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = dGr[u][r];
+            }
         }
     }
     lds_barrier();
@@ -601,9 +614,13 @@ __global__ __launch_bounds__(512) void grad_kernel(
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) {
             // dk += dGam K + dGam^T K
-            dKw[mt] = mm_t<T, C, false, true>(dKw[mt], sD, LDC, 16 * mt, sK, LDK, 16 * wv,
-                                              16 * mt + 16);
-            dKw[mt] = mm_t<T, C, true, true>(dKw[mt], sD, LDC, 16 * mt, sK, LDK, 16 * wv);
+            if constexpr (BF) {
+                dKw[mt] = mm_t<T, C, false, true>(dKw[mt], sdGb, LDN, 16 * mt, sK, LDK, 16 * wv, 16 * mt + 16);
+                dKw[mt] = mm_t<T, C, true, true>(dKw[mt], sdGb, LDN, 16 * mt, sK, LDK, 16 * wv);
+            } else {
+                dKw[mt] = mm_t<T, C, false, true>(dKw[mt], sD, LDC, 16 * mt, sK, LDK, 16 * wv, 16 * mt + 16);
+                dKw[mt] = mm_t<T, C, true, true>(dKw[mt], sD, LDC, 16 * mt, sK, LDK, 16 * wv);
+            }
         }
     }
     lds_barrier();   // B1 and B2 are free: stage dq, dk for 16-byte stores
