@@ -546,12 +546,25 @@ __global__ __launch_bounds__(512) void grad_kernel(
         }
     }
     rQ.store(sB2, LDK, valid);
-    // Z = N^T dN
-    for (int t = wv; t < MC * MC; t += NW) {
-        const int it = t / MC, jt = t - it * MC;
-        const f32x4 acc = mm_lds<float, C, true, true>(zero4(), sN, LDC, 16 * it, sD, LDC, 16 * jt);
+    // Z = N^T dN, only its tiles on and below the diagonal (the ones dG
+    // reads).  Row p of N is zero past p, so tile row it sums over p >= 16 it
+    // only (the products skipped are exact zeros: the sums are unchanged).
+    // Lower tile u (row-major) goes to wave u, then to wave 2 NW - 1 - u, so
+    // the long rows pair with the short ones.
+    constexpr int NZ = MC * (MC + 1) / 2;
+    static_assert(NZ <= 2 * NW, "two lower tiles of Z per wave at most");
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sZ[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = acc[r];
+    for (int h = 0; h < 2; ++h) {
+        const int u = h == 0 ? wv : 2 * NW - 1 - wv;
+        if (u < NZ) {
+            int it = 0;
+            while ((it + 1) * (it + 2) / 2 <= u) ++it;
+            const int jt = u - it * (it + 1) / 2;
+            const f32x4 acc = mm_lds<float, C, true, true>(zero4(), sN + 16 * it * LDC, LDC, 16 * it,
+                                                           sD + 16 * it * LDC, LDC, 16 * jt, C - 16 * it);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sZ[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = acc[r];
+        }
     }
     lds_barrier();
     if (wv < MK) {
@@ -575,7 +588,9 @@ __global__ __launch_bounds__(512) void grad_kernel(
         const int it = t / MC, jt = t - it * MC;
         dGr[u] = zero4();
         if (t < MC * MC && jt <= it) {
-            const f32x4 acc = mm_lds<float, C, false, false>(zero4(), sZ, LDC, 16 * it, sN, LDC, 16 * jt);
+            // N^T is zero past column 16 jt + 15 of tile column jt: k < 16 (jt + 1)
+            const f32x4 acc = mm_lds<float, C, false, false>(zero4(), sZ, LDC, 16 * it, sN, LDC, 16 * jt,
+                                                             16 * jt + 16);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * it + 4 * g + r, cl = 16 * jt + l16;
