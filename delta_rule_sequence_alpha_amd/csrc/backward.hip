@@ -24,6 +24,8 @@
 // chunk.  LDS holds K and two C x max(d_k, d_v) operand buffers in the input
 // dtype and three fp32 C x C matrices; the entry state and dS_out are read
 // from the workspace straight into MFMA registers.
+#include <utility>
+
 #include "efla_device.h"
 #include "efla_launch.h"
 
@@ -242,6 +244,54 @@ __device__ __forceinline__ float row16_sum(float x)
     return x;
 }
 
+// Row broadcast within each 16-lane row of the wave: every lane receives
+// lane I's x (DPP row_newbcast).
+template <int I>
+__device__ __forceinline__ float row_bcast(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + I,
+                                                              0xf, 0xf, false));
+}
+
+// Column j = l16 of the diagonal block N_bb (rows b0 .. b0+15), by the
+// right-looking substitution: once N[i][j] is known it is added into every
+// later row's sum, sum_m += Gamma[m][i] N[i][j], with Gamma[m][i] taken from
+// lane i, which holds column i of the block.  Each row's sum gets its terms
+// in the order i = 0, 1, .. and the same fused multiply-adds as the
+// left-looking loop  N[i][j] = delta_ij - alpha_i sum_{m<i} Gamma_im N[m][j].
+template <int I>
+__device__ __forceinline__ void diag_step(float (&acc)[16], const float (&gc)[16], const float (&al)[16],
+                                          int j, float (&n)[16])
+{
+    n[I] = (I == j ? 1.f : 0.f) - al[I] * acc[I];
+#pragma unroll
+    for (int m = I + 1; m < 16; ++m) acc[m] = fmaf(row_bcast<I>(gc[m]), n[I], acc[m]);
+}
+template <int... I>
+__device__ __forceinline__ void diag_steps(float (&acc)[16], const float (&gc)[16], const float (&al)[16],
+                                           int j, float (&n)[16], std::integer_sequence<int, I...>)
+{
+    (diag_step<I>(acc, gc, al, j, n), ...);
+}
+template <bool BF>
+__device__ __forceinline__ void diag_block_solve(const float *sGam, const float *sAl, float *sN,
+                                                 __bf16 *sNb, int ldc, int ldn, int b0, int j)
+{
+    float gc[16], al[16], acc[16], n[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        gc[m] = sGam[(b0 + m) * ldc + b0 + j];   // Gamma[m][j], below the diagonal for m > j
+        al[m] = sAl[b0 + m];
+        acc[m] = 0.f;
+    }
+    diag_steps(acc, gc, al, j, n, std::make_integer_sequence<int, 16>{});
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        sN[(b0 + i) * ldc + b0 + j] = n[i];
+        if constexpr (BF) sNb[(b0 + i) * ldn + b0 + j] = static_cast<__bf16>(n[i]);
+    }
+}
+
 template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(512) void grad_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
@@ -369,24 +419,9 @@ __global__ __launch_bounds__(512) void grad_kernel(
         for (int r = 0; r < 4; ++r) sGam[(16 * it + 4 * g + r) * LDC + 16 * jt + l16] = acc[r];
     }
     lds_barrier();
-    // diagonal 16x16 blocks: N_ij = delta_ij - alpha_i sum_{m<i} Gamma_im N_mj
-    if (wv == 0 && g < MC) {
-        const int b0 = 16 * g, j = l16;
-        float n[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float acc = 0.f;
-            const float *grow = sGam + (b0 + i) * LDC + b0;
-#pragma unroll
-            for (int m = 0; m < i; ++m) acc = fmaf(grow[m], n[m], acc);
-            n[i] = (i == j ? 1.f : 0.f) - sAl[b0 + i] * acc;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            sN[(b0 + i) * LDC + b0 + j] = n[i];
-            if constexpr (BF) sNb[(b0 + i) * LDN + b0 + j] = static_cast<__bf16>(n[i]);
-        }
-    }
+    // diagonal 16x16 blocks: N_ij = delta_ij - alpha_i sum_{m<i} Gamma_im N_mj,
+    // lane group g solving block g, lane j its column j
+    if (wv == 0 && g < MC) diag_block_solve<BF>(sGam, sAl, sN, sNb, LDC, LDN, 16 * g, l16);
     lds_barrier();
     // blocks below: N_IJ = -N_II D_I sum_{M=J}^{I-1} Gamma_IM N_MJ, by block distance
     for (int dist = 1; dist < MC; ++dist) {
@@ -435,8 +470,14 @@ __global__ __launch_bounds__(512) void grad_kernel(
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) {
             X[mt] = zero4();
+            if constexpr (BF) {   // rows 16 mt + 4 g + r of column col: one transposing read
+                const bf16x4 e4 = run4_lds<true>(sB2, LDV, 16 * wv, 16 * mt + 4 * g);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dEc[mt][r] = to_f32(sB2[(16 * mt + 4 * g + r) * LDV + col]);
+                for (int r = 0; r < 4; ++r) dEc[mt][r] = to_f32(e4[r]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dEc[mt][r] = to_f32(sB2[(16 * mt + 4 * g + r) * LDV + col]);
+            }
         }
         if constexpr (!BF) {
 #pragma unroll
@@ -445,10 +486,19 @@ __global__ __launch_bounds__(512) void grad_kernel(
         mm_b<T, MC, MK>(X, sK, LDK, Sb);   // K S
 #pragma unroll
         for (int mt = 0; mt < MC; ++mt) {
+            f32x4 vv;
+            if constexpr (BF) {
+                const bf16x4 v4 = run4_lds<true>(sB1, LDV, 16 * wv, 16 * mt + 4 * g);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vv[r] = to_f32(v4[r]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vv[r] = to_f32(sB1[(16 * mt + 4 * g + r) * LDV + col]);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * mt + 4 * g + r;
-                X[mt][r] = to_f32(sB1[row * LDV + col]) - X[mt][r];   // V - K S
+                X[mt][r] = vv[r] - X[mt][r];   // V - K S
                 DXv[mt][r] = sAl[row] * X[mt][r];
             }
             E[mt] = zero4();
