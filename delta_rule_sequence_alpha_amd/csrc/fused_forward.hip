@@ -59,7 +59,6 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NP = 3;                 // prep waves per workgroup
 enum Role { K_WAVE = 0, Q_WAVE = 1, T_WAVE = 2 };   // prep wave NS + role
-constexpr int kSpinMax = 1 << 22;     // bound on the prep-wave wait (never reached in practice)
 constexpr int kRsrcWord3 = 0x00020000;   // raw (unswizzled, stride 0) buffer resource
 constexpr int kStoreNT = 2;              // cache policy of the output stores: non-temporal
 
