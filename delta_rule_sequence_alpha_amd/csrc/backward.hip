@@ -22,8 +22,12 @@
 // bf16 MFMA, as the forward's bf16 path does; N and the C x C chain through
 // it (N^T dN N^T) stay fp32.  One workgroup of 8 waves per
 // chunk.  LDS holds K and two C x max(d_k, d_v) operand buffers in the input
-// dtype and three fp32 C x C matrices; the entry state and dS_out are read
-// from the workspace straight into MFMA registers.
+// dtype and three fp32 C x C matrices (Gamma, N, dN); for bf16 inputs also a
+// bf16 copy of N (later dGam) and dA in bf16, all of which only feed bf16
+// MFMA.  The rows of dS_out go from the workspace straight into MFMA
+// registers; the entry state does too for fp32 inputs and is staged through
+// LDS for bf16 ones.  Wherever N's zeros make a block of a product exactly
+// zero, the block is skipped.
 #include <utility>
 
 #include "efla_device.h"
@@ -334,11 +338,10 @@ __global__ __launch_bounds__(512) void grad_kernel(
     const T *dEg = dE + ((long)bh * nchunks * C + (long)c * C) * DV;
 
     // ---- every input in flight at once, in the order of first use: the
-    // per-token scalars and K (Gamma, N), the entry-state columns this wave
-    // multiplies first (straight into registers), V and dE, the rows of S and
-    // dS_out, then dO and Q.  Loads return in order and the barriers below wait
-    // for LDS only, so each wait covers just the loads a phase needs and the
-    // rest stay in flight under the earlier phases.
+    // per-token scalars and K (Gamma, N), the entry state, V and dE, the rows
+    // of dS_out (and for fp32 of S), then dO and Q.  Loads return in order and
+    // the barriers below wait for LDS only, so each wait covers just the loads
+    // a phase needs and the rest stay in flight under the earlier phases.
     float al0 = 0.f, la0 = 0.f, be0 = 0.f;
     if (tid < C && tid < valid) {
         al0 = alpha[tok0 + tid];
