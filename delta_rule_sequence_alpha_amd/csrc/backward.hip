@@ -404,7 +404,7 @@ __global__ __launch_bounds__(512) void grad_kernel(
     }
     for (int e = tid; e < 2 * NW * C; e += NT) sPT[e] = 0.f;
     lds_barrier();
-    if constexpr (BF) {   // S from its LDS staging (B1 is free again after the N phases)
+    if constexpr (BF) {   // S from its LDS staging (B1 takes V at the end of the N phases)
         if (MV >= NW || wv < MV) {
 #pragma unroll
             for (int kt = 0; kt < MK; ++kt) Sb[kt] = run4_lds<true>(sS, LDV, 16 * wv, 16 * kt + 4 * g);
