@@ -74,11 +74,13 @@ def workspace_size(B, H, L, d_k, d_v, chunk, dtype, path="auto") -> int:
 
 
 def forward(q, k, v, beta, S0=None, chunk: int = 64, path: str = "auto", workspace=None,
-            out=None, S_L=None, update: str = "exact"):
+            out=None, S_L=None, update: str = "exact", config=None):
     """Chunked EFLA forward.  q, k: [B,H,L,d_k]; v: [B,H,L,d_v]; beta: [B,H,L] fp32.
 
     Returns (o [B,H,L,d_v] in q's dtype, S_L [B,H,d_k,d_v] fp32).  ``workspace``
     (uint8, >= workspace_size bytes), ``out`` and ``S_L`` may be preallocated.
+    ``config``: a launch configuration (dict with fused_scan_waves, scan_waves,
+    bwd_scan_waves; None = the built-in one).
     """
     B, H, L, dk = k.shape
     dv = v.shape[-1]
@@ -99,10 +101,10 @@ def forward(q, k, v, beta, S0=None, chunk: int = 64, path: str = "auto", workspa
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _lib.efla_forward_update(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(out),
+    st = _lib.efla_forward_config(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(out),
                                   _ptr(S_L), B, H, L, dk, dv, chunk, dt, _ptr(workspace), ws_bytes,
-                                  p, _UPDATES[update], _stream(dev))
-    _raise(st, "efla_forward_update")
+                                  p, _UPDATES[update], config, _stream(dev))
+    _raise(st, "efla_forward_config")
     return out, S_L
 
 
@@ -206,7 +208,7 @@ def backward_workspace_size(B, H, L, d_k, d_v, chunk, dtype) -> int:
 
 
 def backward(q, k, v, beta, S0, d_o, dS_L=None, chunk: int = 64, update: str = "exact",
-             workspace=None, want_dS0: bool = True):
+             workspace=None, want_dS0: bool = True, config=None):
     """Gradients of a loss through ``forward``: given d_o = dLoss/do and
     dS_L = dLoss/dS_L (None: zero), returns (dq, dk, dv, dbeta, dS0) with dq,
     dk, dv in q's dtype, dbeta and dS0 fp32 (dS0 None if not ``want_dS0``)."""
@@ -232,11 +234,11 @@ def backward(q, k, v, beta, S0, d_o, dS_L=None, chunk: int = 64, update: str = "
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _lib.efla_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(d_o), _ptr(dS_L),
-                            _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dbeta), _ptr(dS0), B, H, L, dk,
-                            dv, chunk, dt, _UPDATES[update], _ptr(workspace), ws_bytes,
-                            _stream(dev))
-    _raise(st, "efla_backward")
+    st = _lib.efla_backward_config(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(d_o),
+                                   _ptr(dS_L), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dbeta),
+                                   _ptr(dS0), B, H, L, dk, dv, chunk, dt, _UPDATES[update], config,
+                                   _ptr(workspace), ws_bytes, _stream(dev))
+    _raise(st, "efla_backward_config")
     return dq, dkk, dvv, dbeta, dS0
 
 

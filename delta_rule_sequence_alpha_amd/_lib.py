@@ -31,6 +31,7 @@ SIGNATURES = [
     ("efla_forward_ex", _I, [_P] * 7 + [_I] * 7 + [_P, _S, _I, _P]),
     ("efla_forward_varlen", _I, [_P] * 8 + [_I] * 8 + [_P]),
     ("efla_forward_update", _I, [_P] * 7 + [_I] * 7 + [_P, _S, _I, _I, _P]),
+    ("efla_forward_config", _I, [_P] * 7 + [_I] * 7 + [_P, _S, _I, _I, _P, _P]),
     ("efla_decode_step", _I, [_P] * 6 + [_I] * 5 + [_P]),
     ("efla_decode_step_update", _I, [_P] * 6 + [_I] * 6 + [_P]),
     ("efla_coefficients", _I, [_P] * 4 + [_L, _I, _I, _P]),
@@ -39,7 +40,21 @@ SIGNATURES = [
     ("efla_chunk_scan", _I, [_P] * 8 + [_I] * 7 + [_P]),
     ("efla_backward_workspace_size", _S, [_I] * 7),
     ("efla_backward", _I, [_P] * 12 + [_I] * 8 + [_P, _S, _P]),
+    ("efla_backward_config", _I, [_P] * 12 + [_I] * 8 + [_P, _P, _S, _P]),
 ]
+
+
+class LaunchConfig(ctypes.Structure):
+    """efla_launch_config_t: 0 in a field takes the library's built-in choice."""
+    _fields_ = [("fused_scan_waves", _I), ("scan_waves", _I), ("bwd_scan_waves", _I)]
+
+
+def launch_config(cfg) -> LaunchConfig | None:
+    """A LaunchConfig from None, a LaunchConfig or a dict of its fields."""
+    if cfg is None or isinstance(cfg, LaunchConfig):
+        return cfg
+    return LaunchConfig(**cfg)
+
 
 _lib = None
 
@@ -108,6 +123,13 @@ def efla_forward_update(q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt, w
                  ws_bytes, path, update, stream)
 
 
+def efla_forward_config(q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt, ws, ws_bytes,
+                        path, update, config, stream) -> int:
+    cfg = launch_config(config)
+    return _call("efla_forward_config", q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt, ws,
+                 ws_bytes, path, update, None if cfg is None else ctypes.byref(cfg), stream)
+
+
 def efla_forward_varlen(q, k, v, beta, cu_seqlens, S0, o, S_L, N, H, T, dk, dv, chunk, dt, update,
                         stream) -> int:
     return _call("efla_forward_varlen", q, k, v, beta, cu_seqlens, S0, o, S_L, N, H, T, dk, dv,
@@ -148,3 +170,11 @@ def efla_backward(q, k, v, beta, S0, d_o, dS_L, dq, dk_, dv_, dbeta, dS0, B, H, 
                   dt, update, ws, ws_bytes, stream) -> int:
     return _call("efla_backward", q, k, v, beta, S0, d_o, dS_L, dq, dk_, dv_, dbeta, dS0, B, H, L,
                  dk, dv, chunk, dt, update, ws, ws_bytes, stream)
+
+
+def efla_backward_config(q, k, v, beta, S0, d_o, dS_L, dq, dk_, dv_, dbeta, dS0, B, H, L, dk, dv,
+                         chunk, dt, update, config, ws, ws_bytes, stream) -> int:
+    cfg = launch_config(config)
+    return _call("efla_backward_config", q, k, v, beta, S0, d_o, dS_L, dq, dk_, dv_, dbeta, dS0, B,
+                 H, L, dk, dv, chunk, dt, update, None if cfg is None else ctypes.byref(cfg), ws,
+                 ws_bytes, stream)

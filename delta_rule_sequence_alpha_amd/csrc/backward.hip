@@ -718,7 +718,7 @@ hipError_t launch_grad(const void *q, const void *k, const void *v, const void *
     static_assert(Lay::bytes <= 160 * 1024, "gradient kernel LDS");
     const int nchunks = (L + C - 1) / C;
     if (BH == 0 || nchunks == 0) return hipSuccess;
-    static const hipError_t attr = hipFuncSetAttribute(
+    const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&grad_kernel<T, DK, DV, C>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
     if (attr != hipSuccess) return attr;

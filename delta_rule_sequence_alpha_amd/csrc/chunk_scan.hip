@@ -282,7 +282,7 @@ hipError_t launch_scan(const void *q, const void *k, const void *w, const void *
     const int ntiles = DV / Lay::TV + (sg.mode == SCAN_SUMMARY ? DK / Lay::TV : 0);
     const int nchunks = (L + C - 1) / C;
     if (BH == 0) return hipSuccess;
-    static const hipError_t attr = hipFuncSetAttribute(
+    const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&scan_kernel<T, DK, DV, C, NW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
     if (attr != hipSuccess) return attr;
@@ -547,7 +547,7 @@ hipError_t launch_rscan_nw(const void *q, const void *k, const void *w, const vo
     const int ntiles = DV / Lay::TV + (sg.mode == SCAN_SUMMARY ? DK / Lay::TV : 0);
     const int nchunks = (L + C - 1) / C;
     if (BH == 0) return hipSuccess;
-    static const hipError_t attr = hipFuncSetAttribute(
+    const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&rscan_kernel<T, DK, DV, C, NW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
     if (attr != hipSuccess) return attr;
@@ -674,7 +674,7 @@ hipError_t launch_scan_pair_nw(const void *q, const void *k, const void *w, cons
     const int nchunks = (L + C - 1) / C;
     const int nfwd = BH * (DV / Lay::TV);
     if (BH == 0) return hipSuccess;
-    static const hipError_t attr = hipFuncSetAttribute(
+    const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&scan_pair_kernel<T, DK, DV, C, NW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
     if (attr != hipSuccess) return attr;

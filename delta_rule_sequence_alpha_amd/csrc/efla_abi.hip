@@ -2,7 +2,6 @@
 // HIP call before it passes), workspace sizing, and kernel launches on the
 // caller's stream.
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "efla.h"
 #include "efla_launch.h"
@@ -129,24 +128,27 @@ int plan_G(efla_path_t p, int B, int H, int L, int dk, int dv, int chunk)
     return p == EFLA_PATH_SEGMENTED ? seg_plan((long long)B * H, L, dk, dv, chunk).G : 1;
 }
 
-// Waves per workgroup of the scan / fused kernels (0 = the built-in choice).
-int waves_override(const char *name)
-{
-    const char *e = getenv(name);
-    return e ? atoi(e) : 0;
-}
-int scan_waves_override() { return waves_override("EFLA_SCAN_WAVES"); }
-
-// Waves per workgroup of the backward's two scans (64-column workgroups).
+// Launch configuration: every field 0 (or no struct) is the built-in choice.
+// The backward's two scans default to 4-wave (64-column) workgroups.
 // Unsegmented they share one launch, whose workgroups then fill the CUs
 // (lm1.3b-bf16: 270 us for both at 4 waves, 297 at 2; run one after the
 // other they took 197 + 232 us at 2 waves).  Segmented scans have
 // workgroups to spare (long-stiff-f32: 1.5 vs 2.6 ms per state-scan pass
 // at 4 vs 2 waves).
-int bwd_scan_waves()
+efla_launch_config_t config_of(const efla_launch_config_t *c)
 {
-    const int o = waves_override("EFLA_BWD_SCAN_WAVES");
-    return o > 0 ? o : 4;
+    efla_launch_config_t r{0, 0, 0};
+    if (c) r = *c;
+    if (r.bwd_scan_waves == 0) r.bwd_scan_waves = 4;
+    return r;
+}
+
+bool config_ok(const efla_launch_config_t *c)
+{
+    if (!c) return true;
+    auto w124 = [](int n) { return n == 0 || n == 1 || n == 2 || n == 4; };
+    return (c->fused_scan_waves == 0 || c->fused_scan_waves == 1 || c->fused_scan_waves == 2) &&
+           w124(c->scan_waves) && w124(c->bwd_scan_waves);
 }
 
 efla_status_t hip_status(hipError_t e) { return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP; }
@@ -188,15 +190,17 @@ size_t efla_forward_workspace_size(int B, int H, int L, int dk, int dv, int chun
     return efla_forward_workspace_size_ex(B, H, L, dk, dv, chunk, dt, EFLA_PATH_AUTO);
 }
 
-efla_status_t efla_forward_update(const void *q, const void *k, const void *v, const float *beta,
+efla_status_t efla_forward_config(const void *q, const void *k, const void *v, const float *beta,
                                   const float *S0, void *o, float *S_L, int B, int H, int L,
                                   int dk, int dv, int chunk, efla_dtype_t dt, void *workspace,
                                   size_t workspace_bytes, efla_path_t path, efla_update_t update,
-                                  void *stream)
+                                  const efla_launch_config_t *config, void *stream)
 {
     efla_status_t s = check_shape(B, H, L, dk, dv, chunk, dt);
     if (s != EFLA_OK) return s;
     if (update != EFLA_EXACT && update != EFLA_EULER) return EFLA_ERR_INVALID_ARG;
+    if (!config_ok(config)) return EFLA_ERR_INVALID_ARG;
+    const efla_launch_config_t cfg = config_of(config);
     const bool euler = update == EFLA_EULER;
     if (path != EFLA_PATH_AUTO && path != EFLA_PATH_STAGED && path != EFLA_PATH_FUSED &&
         path != EFLA_PATH_SEGMENTED)
@@ -215,8 +219,8 @@ efla_status_t efla_forward_update(const void *q, const void *k, const void *v, c
         if (!efla::fused_supported(dt == EFLA_BF16, dk, dv, chunk)) return EFLA_ERR_UNSUPPORTED;
         if (L == 0) return hip_status(efla::launch_copy_state(S0, S_L, BH * dk * dv, st));
         return hip_status(efla::dispatch_fused(dt == EFLA_BF16, dk, dv, chunk, q, k, v, beta, S0,
-                                               o, S_L, (int)BH, L,
-                                               waves_override("EFLA_FUSED_WAVES"), euler, st));
+                                               o, S_L, (int)BH, L, cfg.fused_scan_waves, euler,
+                                               st));
     }
     const SegPlan plan = path == EFLA_PATH_SEGMENTED ? seg_plan(BH, L, dk, dv, chunk) : SegPlan{1, 0};
     const StagedWs ws = staged_ws(B, H, L, dk, dv, chunk, dt, plan.G);
@@ -240,11 +244,21 @@ efla_status_t efla_forward_update(const void *q, const void *k, const void *v, c
                                           reinterpret_cast<float *>(base + ws.R),
                                           reinterpret_cast<float *>(base + ws.P),
                                           reinterpret_cast<float *>(base + ws.Sin),
-                                          scan_waves_override(), st);
+                                          cfg.scan_waves, st);
     else if (e == hipSuccess)
         e = efla::dispatch_scan(bf, dk, dv, chunk, q, k, w, u, aqk, S0, o, S_L, (int)BH, L,
-                                scan_waves_override(), st);
+                                cfg.scan_waves, st);
     return hip_status(e);
+}
+
+efla_status_t efla_forward_update(const void *q, const void *k, const void *v, const float *beta,
+                                  const float *S0, void *o, float *S_L, int B, int H, int L,
+                                  int dk, int dv, int chunk, efla_dtype_t dt, void *workspace,
+                                  size_t workspace_bytes, efla_path_t path, efla_update_t update,
+                                  void *stream)
+{
+    return efla_forward_config(q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt, workspace,
+                               workspace_bytes, path, update, nullptr, stream);
 }
 
 efla_status_t efla_forward_varlen(const void *q, const void *k, const void *v, const float *beta,
@@ -270,7 +284,7 @@ efla_status_t efla_forward_varlen(const void *q, const void *k, const void *v, c
     }
     return hip_status(efla::dispatch_fused_varlen(
         dt == EFLA_BF16, dk, dv, chunk, q, k, v, beta, S0, o, S_L, (int)NH, T, cu_seqlens, H,
-        waves_override("EFLA_FUSED_WAVES"), update == EFLA_EULER, static_cast<hipStream_t>(stream)));
+        0, update == EFLA_EULER, static_cast<hipStream_t>(stream)));
 }
 
 efla_status_t efla_forward_ex(const void *q, const void *k, const void *v, const float *beta,
@@ -370,7 +384,7 @@ efla_status_t efla_chunk_scan(const void *q, const void *k, const void *w, const
         !aligned16(o))
         return EFLA_ERR_INVALID_ARG;
     return hip_status(efla::dispatch_scan(dt == EFLA_BF16, dk, dv, chunk, q, k, w, u, a_qk, S0, o,
-                                          S_L, (int)BH, L, scan_waves_override(), st));
+                                          S_L, (int)BH, L, 0, st));
 }
 
 size_t efla_backward_workspace_size(int B, int H, int L, int dk, int dv, int chunk,
@@ -382,16 +396,18 @@ size_t efla_backward_workspace_size(int B, int H, int L, int dk, int dv, int chu
                        seg_plan((long long)B * H, L, dk, dv, chunk).G).total;
 }
 
-efla_status_t efla_backward(const void *q, const void *k, const void *v, const float *beta,
-                            const float *S0, const void *d_o, const float *dS_L, void *dq,
-                            void *dk_out, void *dv_out, float *dbeta, float *dS0, int B, int H,
-                            int L, int dk, int dv, int chunk, efla_dtype_t dt,
-                            efla_update_t update, void *workspace, size_t workspace_bytes,
-                            void *stream)
+efla_status_t efla_backward_config(const void *q, const void *k, const void *v, const float *beta,
+                                   const float *S0, const void *d_o, const float *dS_L, void *dq,
+                                   void *dk_out, void *dv_out, float *dbeta, float *dS0, int B,
+                                   int H, int L, int dk, int dv, int chunk, efla_dtype_t dt,
+                                   efla_update_t update, const efla_launch_config_t *config,
+                                   void *workspace, size_t workspace_bytes, void *stream)
 {
     efla_status_t s = check_shape(B, H, L, dk, dv, chunk, dt);
     if (s != EFLA_OK) return s;
     if (update != EFLA_EXACT && update != EFLA_EULER) return EFLA_ERR_INVALID_ARG;
+    if (!config_ok(config)) return EFLA_ERR_INVALID_ARG;
+    const efla_launch_config_t cfg = config_of(config);
     const bool euler = update == EFLA_EULER;
     const long long BH = (long long)B * H;
     if (BH == 0) return EFLA_OK;
@@ -424,7 +440,7 @@ efla_status_t efla_backward(const void *q, const void *k, const void *v, const f
     hipError_t e = efla::dispatch_coef(bf, dk, k, beta, alpha, lambda, BH * L, euler, st);
     if (e == hipSuccess)
         e = efla::dispatch_ut(bf, dk, dv, chunk, q, k, v, alpha, w, u, aqk, (int)BH, L, st);
-    const int nw = bwd_scan_waves();
+    const int nw = cfg.bwd_scan_waves;
     if (e == hipSuccess && plan.G == 1) {   // the two scans are independent: one launch
         e = efla::dispatch_scan_pair(bf, dk, dv, chunk, q, k, w, u, aqk, S0, states, d_o, dS_L,
                                      dSout, dE, dS0, (int)BH, L, nw, st);
@@ -439,6 +455,18 @@ efla_status_t efla_backward(const void *q, const void *k, const void *v, const f
         e = efla::dispatch_grad(bf, dk, dv, chunk, q, k, v, d_o, beta, alpha, lambda, states,
                                 dSout, dE, dq, dk_out, dv_out, dbeta, (int)BH, L, euler, st);
     return hip_status(e);
+}
+
+efla_status_t efla_backward(const void *q, const void *k, const void *v, const float *beta,
+                            const float *S0, const void *d_o, const float *dS_L, void *dq,
+                            void *dk_out, void *dv_out, float *dbeta, float *dS0, int B, int H,
+                            int L, int dk, int dv, int chunk, efla_dtype_t dt,
+                            efla_update_t update, void *workspace, size_t workspace_bytes,
+                            void *stream)
+{
+    return efla_backward_config(q, k, v, beta, S0, d_o, dS_L, dq, dk_out, dv_out, dbeta, dS0, B,
+                                H, L, dk, dv, chunk, dt, update, nullptr, workspace,
+                                workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -755,7 +755,7 @@ hipError_t launch_fused(const void *q, const void *k, const void *v, const float
     constexpr int NTILE = DV / Lay::TV;
     const int nchunks = (L + C - 1) / C;
     if (BH == 0 || (nchunks == 0 && !cu)) return hipSuccess;
-    static const hipError_t attr = hipFuncSetAttribute(
+    const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&fused_kernel<DK, DV, C, NS>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
     if (attr != hipSuccess) return attr;

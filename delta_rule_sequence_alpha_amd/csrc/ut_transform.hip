@@ -212,7 +212,7 @@ hipError_t launch_ut(const void *q, const void *k, const void *v, const float *a
     using Lay = UtLayout<T, DK, DV, C>;
     const int nchunks = (L + C - 1) / C;
     if (BH == 0 || nchunks == 0) return hipSuccess;
-    static const hipError_t attr = hipFuncSetAttribute(
+    const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&ut_kernel<T, DK, DV, C>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
     if (attr != hipSuccess) return attr;

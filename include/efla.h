@@ -78,6 +78,24 @@ typedef enum {
  * Any other value returns EFLA_ERR_INVALID_ARG. */
 typedef enum { EFLA_EXACT = 0, EFLA_EULER = 1 } efla_update_t;
 
+/* Launch shape of the chunked kernels, for callers that tune them.  Each
+ * field chosen as 0 takes the library's built-in choice; a NULL pointer means
+ * all zero.  The values pick other compiled instances of the same kernels
+ * (how many 16-column tiles of the state one workgroup owns); the arithmetic
+ * of every column, and so the result, does not depend on them.
+ *   fused_scan_waves  fused forward: 1 or 2 scan waves per workgroup
+ *                     (16- or 32-column state tiles)
+ *   scan_waves        staged and segmented state scans: 1, 2 or 4 waves per
+ *                     workgroup
+ *   bwd_scan_waves    the backward's two state scans: 1, 2 or 4
+ * Any other value returns EFLA_ERR_INVALID_ARG.  The library reads no
+ * environment variable and keeps no setting between calls. */
+typedef struct {
+    int fused_scan_waves;
+    int scan_waves;
+    int bwd_scan_waves;
+} efla_launch_config_t;
+
 /* The path EFLA_PATH_AUTO takes for this shape (EFLA_PATH_AUTO itself for an
  * invalid shape). */
 efla_path_t efla_forward_path(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype_t dt);
@@ -145,6 +163,15 @@ efla_status_t efla_forward_update(const void *q, const void *k, const void *v, c
                                   int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype_t dt,
                                   void *workspace, size_t workspace_bytes, efla_path_t path,
                                   efla_update_t update, void *stream);
+
+/* efla_forward_update with an explicit launch configuration (NULL = the
+ * built-in one).  Same results as efla_forward_update. */
+efla_status_t efla_forward_config(const void *q, const void *k, const void *v, const float *beta,
+                                  const float *S0, void *o, float *S_L,
+                                  int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype_t dt,
+                                  void *workspace, size_t workspace_bytes, efla_path_t path,
+                                  efla_update_t update, const efla_launch_config_t *config,
+                                  void *stream);
 
 /*
  * Single-token decode step (the recurrent form of the same update) for N
@@ -247,6 +274,16 @@ efla_status_t efla_backward(const void *q, const void *k, const void *v, const f
                             int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype_t dt,
                             efla_update_t update, void *workspace, size_t workspace_bytes,
                             void *stream);
+
+/* efla_backward with an explicit launch configuration (NULL = the built-in
+ * one).  Same results as efla_backward. */
+efla_status_t efla_backward_config(const void *q, const void *k, const void *v, const float *beta,
+                                   const float *S0, const void *d_o, const float *dS_L,
+                                   void *dq, void *dk, void *dv, float *dbeta, float *dS0,
+                                   int B, int H, int L, int d_k, int d_v, int chunk,
+                                   efla_dtype_t dt, efla_update_t update,
+                                   const efla_launch_config_t *config, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 16
+    assert len(declared) == 18
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], check=True,
                          capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (efla_[a-z_]+)\b", out))
@@ -220,3 +220,31 @@ def _bwd(lib, **over):
 ])
 def test_backward_rejects_bad_arguments(lib, over, status):
     assert _bwd(lib, **over) == status
+
+
+@pytest.mark.parametrize("cfg,status", [
+    (dict(fused_scan_waves=3), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(scan_waves=3), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(bwd_scan_waves=8), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(scan_waves=-1), _lib.EFLA_ERR_INVALID_ARG),
+    # valid values pass the check and validation goes on to the next error
+    (dict(fused_scan_waves=1, scan_waves=4, bwd_scan_waves=2), _lib.EFLA_ERR_WORKSPACE),
+    (None, _lib.EFLA_ERR_WORKSPACE),
+])
+def test_launch_config_validation(lib, cfg, status):
+    """The launch configuration is an argument: out-of-range wave counts are
+    rejected before any HIP call, on the forward and the backward entry."""
+    assert _lib.efla_forward_config(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 2, 64, 16, 16, 16,
+                                    _lib.EFLA_F32, None, 0, _lib.EFLA_PATH_STAGED, _lib.EFLA_EXACT,
+                                    cfg, None) == status
+    assert _lib.efla_backward_config(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, 1, 2, 64, 16, 16, 16, _lib.EFLA_F32,
+                                     _lib.EFLA_EXACT, cfg, None, 0, None) == status
+
+
+def test_library_reads_no_environment():
+    """No entry point depends on the process environment: the library imports
+    no getenv/secure_getenv."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", _lib.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    assert not re.search(r"\b(secure_)?getenv\b", out)

@@ -125,24 +125,43 @@ def test_state_aliasing_in_place(path):
     _check(w, (q, k, v, beta, S0), o, S_L)
 
 
-@pytest.mark.parametrize("path", PATHS)
-def test_degenerate_tokens_are_identity(path):
-    """beta = 0 or k = 0 tokens leave the state unchanged (alpha k k^T = 0)."""
-    w = wl.FORWARD_WORKLOADS["tiny-f32"].with_(H=2, L=48, dtype="bf16")
-    note(f"forward degenerate tokens {path}")
+def _segmented_splits(w):
+    """True when the segmented path's plan splits this shape (its workspace
+    then holds segment maps beyond the staged path's)."""
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    args = (w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, dt)
+    return efla.workspace_size(*args, "segmented") > efla.workspace_size(*args, "staged")
+
+
+# (path, dtype, L, beta = 0 span in head 0, k = 0 span in head 1).  The
+# segmented case is long enough to be split, and its spans cross segments.
+DEGENERATE_CASES = [("fused", "bf16", 48, (10, 30), (5, 40)),
+                    ("staged", "bf16", 48, (10, 30), (5, 40)),
+                    ("staged", "f32", 48, (10, 30), (5, 40)),
+                    ("segmented", "f32", 16 * 24, (60, 200), (100, 300))]
+
+
+@pytest.mark.parametrize("path,dtype,L,zb,zk", DEGENERATE_CASES)
+def test_degenerate_tokens_are_identity(path, dtype, L, zb, zk):
+    """beta = 0 or k = 0 tokens leave the state unchanged: alpha k k^T = 0 and
+    alpha k v^T = 0 (Methodology 3), so over a beta = 0 span o_t = S^T q_t
+    with S frozen at the state entering the span."""
+    w = wl.FORWARD_WORKLOADS["tiny-f32"].with_(H=2, L=L, dtype=dtype)
+    if path == "segmented":
+        assert _segmented_splits(w)
+    note(f"forward degenerate tokens {path} {dtype} L={L}")
     q, k, v, beta, _ = wl.forward_inputs(w, seed=4)
-    beta[:, 0, 10:30] = 0.0
-    k[:, 1, 5:40] = 0.0
+    beta[:, 0, zb[0]:zb[1]] = 0.0
+    k[:, 1, zk[0]:zk[1]] = 0.0
     inputs = (q, k, v, beta, None)
     qd, kd, vd, bd = dev(q, k, v, beta)
     o, S_L = efla.forward(qd, kd, vd, bd, None, chunk=16, path=path)
     torch.cuda.synchronize()
     _check(w, inputs, o, S_L)
-    # with S = S_9 frozen over tokens 10..29, o_t = S_9^T q_t there
-    o_r, _ = oracle.forward(q[:, :, :10], k[:, :, :10], v[:, :, :10], beta[:, :, :10])
-    _, S9 = oracle.forward(q[:, :, :10], k[:, :, :10], v[:, :, :10], beta[:, :, :10])
-    frozen = np.einsum("bhij,bhti->bhtj", S9[:, :1], q[:, :1, 10:30].double().numpy())
-    assert rel_err(o[:, :1, 10:30], frozen) <= TOL[w.dtype]
+    t0, t1 = zb
+    _, S_in = oracle.forward(q[:, :, :t0], k[:, :, :t0], v[:, :, :t0], beta[:, :, :t0])
+    frozen = np.einsum("bhij,bhti->bhtj", S_in[:, :1], q[:, :1, t0:t1].double().numpy())
+    assert rel_err(o[:, :1, t0:t1], frozen) <= TOL[w.dtype]
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -195,3 +214,36 @@ def test_split_and_resume(path, t0):
     assert rel_err(torch.cat([oa, ob], dim=2), o_r) <= tol
     assert rel_err(Sb, S_r) <= tol
     assert rel_err(S, S_r) <= tol
+
+
+# (path, L, t0): the stiff fp32 recipe, split at t0 and resumed from the
+# first part's state.  The segmented sizes are long enough that the whole
+# sequence and both parts are each split into segments.
+STIFF_SPLITS = [("staged", 64 * 6 + 9, 64 * 3), ("staged", 64 * 6 + 9, 100),
+                ("segmented", 64 * 40, 64 * 20 + 17)]
+
+
+@pytest.mark.parametrize("path,L,t0", STIFF_SPLITS)
+def test_split_and_resume_stiff_f32(path, L, t0):
+    """A sequence split at t0, the second part starting from the first part's
+    final state, equals the whole (the recurrence is sequential in S,
+    Methodology 3), on the stiff recipe (beta lambda up to 5e4) in fp32."""
+    w = wl.FORWARD_WORKLOADS["long-stiff-f32"].with_(B=1, H=2, L=L)
+    if path == "segmented":
+        for part in (w, w.with_(L=t0), w.with_(L=L - t0)):
+            assert _segmented_splits(part), part
+    note(f"forward stiff split/resume {path} L={L} t0={t0}")
+    q, k, v, beta, _ = wl.forward_inputs(w, seed=8)
+    qd, kd, vd, bd = dev(q, k, v, beta)
+    o, S = efla.forward(qd, kd, vd, bd, None, chunk=64, path=path)
+    oa, Sa = efla.forward(*[x[:, :, :t0].contiguous() for x in (qd, kd, vd, bd)], None, chunk=64,
+                          path=path)
+    ob, Sb = efla.forward(*[x[:, :, t0:].contiguous() for x in (qd, kd, vd, bd)], Sa, chunk=64,
+                          path=path)
+    torch.cuda.synchronize()
+    o_r, S_r = oracle.forward(q, k, v, beta)
+    tol = TOL["f32"]
+    e = (rel_err(torch.cat([oa, ob], dim=2), o_r), rel_err(Sb, S_r), rel_err(o, o_r),
+         rel_err(S, S_r))
+    print(f"  err split o={e[0]:.3e} S={e[1]:.3e} whole o={e[2]:.3e} S={e[3]:.3e}", flush=True)
+    assert max(e) <= tol

@@ -8,6 +8,8 @@ Solution from Continuous-Time Dynamics", Technical Summary, Methodology 3).
 The loss is Loss = <dO, o> + <dS_L, S_L>, so its gradients with respect to the
 inputs are what a training step back-propagates through the operator.
 """
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -74,7 +76,7 @@ def _rel(a, b):
                                                (2, 1, 9, 4, 3, False, True),
                                                (1, 2, 7, 2, 5, True, False)])
 def test_backward_matches_finite_differences_elementwise(update, B, H, L, dk, dv, s0, dsl):
-    rng = np.random.default_rng(hash((B, H, L, dk, dv, update)) % 2**32)
+    rng = np.random.default_rng(zlib.crc32(repr((B, H, L, dk, dv, update)).encode()))
     q, k, v, beta, S0, dO, dSL = _inputs(rng, B, H, L, dk, dv, s0=s0, dsl=dsl)
     grads = oracle.backward(q, k, v, beta, S0, dO, dSL, update=update)
     names = ["q", "k", "v", "beta", "S0"]
