@@ -110,7 +110,7 @@ struct FusedLayout {
     // one chunk of chunk-local quantities (double-buffered), A fragments
     static constexpr size_t pG = 0;                            // -G_{i,m}, m < i
     static constexpr size_t pA = pG + 1024 * g_slot(MC, 0);    // -tril(Q K^T)
-    static constexpr size_t pT = pA + 1024 * a_slot(MC, 0);    // T_ii: [i][lane] x 8 bytes
+    static constexpr size_t pT = pA + 1024 * a_slot(MC, 0);    // T_ii: [i][column][row] bf16
     static constexpr size_t prepBytes = pT + 512 * MC;
     // T-wave scratch, used within one interval: fp32 G_ii [16i + col][row]
     static constexpr size_t kGt = 0;
@@ -376,34 +376,85 @@ __device__ __forceinline__ float row_bcast(float x)
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
                                                               0x150 + I, 0xf, 0xf, false));
 }
-// acc -= (lane I's g) * t, the broadcast and the negation folded into the
-// FMA.  A DPP source needs two wait states after a VALU write; g comes
-// straight from an LDS load and no VALU instruction writes it.
-template <int I>
-__device__ __forceinline__ void fnmac_row_bcast(float &acc, float g, float t)
+// acc[m] -= (lane I's gc[m]) * t for m = M0 .. M0+N-1 (N <= 8): the
+// broadcast and the negation folded into each FMA, in one asm group.  A DPP
+// source needs two wait states after a VALU write of it, and the compiler
+// cannot see inside this asm; the s_nop at the group's head provides them
+// whatever was scheduled before it (inside, only the accumulators are
+// written, never a DPP source).
+#define EFLA_FM(d, s) "v_fmac_f32_dpp %" #d ", -%" #s ", %[t] row_newbcast:%[i] row_mask:0xf bank_mask:0xf\n\t"
+#define EFLA_A(j) "+v"(acc[M0 + j])
+#define EFLA_G(j) "v"(gc[M0 + j])
+template <int I, int M0, int N>
+__device__ __forceinline__ void fnmac_group(float (&acc)[16], const float (&gc)[16], float t)
 {
-    asm volatile("v_fmac_f32_dpp %0, -%1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-                 : "+v"(acc)
-                 : "v"(g), "v"(t), "n"(I));
+    static_assert(N >= 1 && N <= 8, "one asm group takes 1 to 8 updates");
+    if constexpr (N == 1)
+        asm volatile("s_nop 1\n\t" EFLA_FM(0, 1)
+                     : EFLA_A(0) : EFLA_G(0), [t] "v"(t), [i] "n"(I));
+    else if constexpr (N == 2)
+        asm volatile("s_nop 1\n\t" EFLA_FM(0, 2) EFLA_FM(1, 3)
+                     : EFLA_A(0), EFLA_A(1) : EFLA_G(0), EFLA_G(1), [t] "v"(t), [i] "n"(I));
+    else if constexpr (N == 3)
+        asm volatile("s_nop 1\n\t" EFLA_FM(0, 3) EFLA_FM(1, 4) EFLA_FM(2, 5)
+                     : EFLA_A(0), EFLA_A(1), EFLA_A(2)
+                     : EFLA_G(0), EFLA_G(1), EFLA_G(2), [t] "v"(t), [i] "n"(I));
+    else if constexpr (N == 4)
+        asm volatile("s_nop 1\n\t" EFLA_FM(0, 4) EFLA_FM(1, 5) EFLA_FM(2, 6) EFLA_FM(3, 7)
+                     : EFLA_A(0), EFLA_A(1), EFLA_A(2), EFLA_A(3)
+                     : EFLA_G(0), EFLA_G(1), EFLA_G(2), EFLA_G(3), [t] "v"(t), [i] "n"(I));
+    else if constexpr (N == 5)
+        asm volatile("s_nop 1\n\t" EFLA_FM(0, 5) EFLA_FM(1, 6) EFLA_FM(2, 7) EFLA_FM(3, 8)
+                         EFLA_FM(4, 9)
+                     : EFLA_A(0), EFLA_A(1), EFLA_A(2), EFLA_A(3), EFLA_A(4)
+                     : EFLA_G(0), EFLA_G(1), EFLA_G(2), EFLA_G(3), EFLA_G(4), [t] "v"(t),
+                       [i] "n"(I));
+    else if constexpr (N == 6)
+        asm volatile("s_nop 1\n\t" EFLA_FM(0, 6) EFLA_FM(1, 7) EFLA_FM(2, 8) EFLA_FM(3, 9)
+                         EFLA_FM(4, 10) EFLA_FM(5, 11)
+                     : EFLA_A(0), EFLA_A(1), EFLA_A(2), EFLA_A(3), EFLA_A(4), EFLA_A(5)
+                     : EFLA_G(0), EFLA_G(1), EFLA_G(2), EFLA_G(3), EFLA_G(4), EFLA_G(5),
+                       [t] "v"(t), [i] "n"(I));
+    else if constexpr (N == 7)
+        asm volatile("s_nop 1\n\t" EFLA_FM(0, 7) EFLA_FM(1, 8) EFLA_FM(2, 9) EFLA_FM(3, 10)
+                         EFLA_FM(4, 11) EFLA_FM(5, 12) EFLA_FM(6, 13)
+                     : EFLA_A(0), EFLA_A(1), EFLA_A(2), EFLA_A(3), EFLA_A(4), EFLA_A(5), EFLA_A(6)
+                     : EFLA_G(0), EFLA_G(1), EFLA_G(2), EFLA_G(3), EFLA_G(4), EFLA_G(5), EFLA_G(6),
+                       [t] "v"(t), [i] "n"(I));
+    else
+        asm volatile("s_nop 1\n\t" EFLA_FM(0, 8) EFLA_FM(1, 9) EFLA_FM(2, 10) EFLA_FM(3, 11)
+                         EFLA_FM(4, 12) EFLA_FM(5, 13) EFLA_FM(6, 14) EFLA_FM(7, 15)
+                     : EFLA_A(0), EFLA_A(1), EFLA_A(2), EFLA_A(3), EFLA_A(4), EFLA_A(5), EFLA_A(6),
+                       EFLA_A(7)
+                     : EFLA_G(0), EFLA_G(1), EFLA_G(2), EFLA_G(3), EFLA_G(4), EFLA_G(5), EFLA_G(6),
+                       EFLA_G(7), [t] "v"(t), [i] "n"(I));
 }
+#undef EFLA_G
+#undef EFLA_A
+#undef EFLA_FM
 
 // Step i of the right-looking substitution for column j = l16 of T_bb: T[i][j]
 // = alpha_i acc[i] (lane i holds alpha_i), then acc[m] -= G[m][i] T[i][j] for
 // m > i, G[m][i] being lane i's own gc[m].
 template <int I>
 __device__ __forceinline__ void subst_step(float (&acc)[16], const float (&gc)[16], float al,
-                                           bf *tcol)
+                                           float (&tv)[16])
 {
     const float t = row_bcast<I>(al) * acc[I];
-    tcol[4 * I] = static_cast<bf>(t);
-#pragma unroll
-    for (int m = I + 1; m < 16; ++m) fnmac_row_bcast<I>(acc[m], gc[m], t);
+    tv[I] = t;
+    constexpr int N = 15 - I;   // updates of rows I+1 .. 15
+    if constexpr (N > 8) {
+        fnmac_group<I, I + 1, 8>(acc, gc, t);
+        fnmac_group<I, I + 9, N - 8>(acc, gc, t);
+    } else if constexpr (N > 0) {
+        fnmac_group<I, I + 1, N>(acc, gc, t);
+    }
 }
 template <int... I>
-__device__ __forceinline__ void subst(float (&acc)[16], const float (&gc)[16], float al, bf *tcol,
-                                      std::integer_sequence<int, I...>)
+__device__ __forceinline__ void subst(float (&acc)[16], const float (&gc)[16], float al,
+                                      float (&tv)[16], std::integer_sequence<int, I...>)
 {
-    (subst_step<I>(acc, gc, al, tcol), ...);
+    (subst_step<I>(acc, gc, al, tv), ...);
 }
 
 // T wave, after the diagonal Gram tiles: every T_ii, lane group b (a 16-lane
@@ -412,8 +463,10 @@ __device__ __forceinline__ void subst(float (&acc)[16], const float (&gc)[16], f
 // diagonal entry, so the lane forms that token's alpha itself.  Then the 16
 // steps of the right-looking substitution (once T[i][j] is known it is
 // eliminated from every later row, so each step carries independent FMAs),
-// reading column i of G and alpha_i from lane i by row broadcast.  T[i][j]
-// is written to its place in the A fragment of T_bb: lane 16(j/4) + i, slot j%4.
+// reading column i of G and alpha_i from lane i by row broadcast.  Column j
+// of T_bb is kept in registers and stored at the end as row j of a 16 x 16
+// bf16 tile (two 16-byte writes), from which the scan takes its operand
+// fragment with one transposing read.
 template <int DK, int DV, int C, int NS>
 __device__ __forceinline__ void prep_diag(const char *in, char *prep, char *ks, int euler)
 {
@@ -435,11 +488,18 @@ __device__ __forceinline__ void prep_diag(const char *in, char *prep, char *ks, 
         }
         const float lam = grow[j];
         const float al = update_alpha(euler, sB[lane], lam);
-        float acc[16];
+        float acc[16], tv[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) acc[m] = (m == j) ? 1.f : 0.f;
-        subst(acc, gc, al, sT + (b * 64 + 16 * (j >> 2)) * 4 + (j & 3),
-              std::make_integer_sequence<int, 16>{});
+        subst(acc, gc, al, tv, std::make_integer_sequence<int, 16>{});
+        bf16x8 r0, r1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            r0[i] = static_cast<bf>(tv[i]);
+            r1[i] = static_cast<bf>(tv[8 + i]);
+        }
+        *reinterpret_cast<bf16x8 *>(sT + (16 * b + j) * 16) = r0;
+        *reinterpret_cast<bf16x8 *>(sT + (16 * b + j) * 16 + 8) = r1;
     }
 }
 
@@ -597,9 +657,11 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
             if (2 * s + 1 < i) ga[i * NKC + s] = *reinterpret_cast<const bf16x8 *>(sG + gfrag(i, 2 * s));
             else ga[i * NKC + s] = cat(*reinterpret_cast<const bf16x4 *>(sG + gfrag(i, 2 * s)), zb4());
         }
+    // T_ii, stored row j = column j of the block: one transposing read gives
+    // lane (l16, g) T_ii[l16][4g + r], the A fragment
     bf16x4 ta[MC];
 #pragma unroll
-    for (int i = 0; i < MC; ++i) ta[i] = *reinterpret_cast<const bf16x4 *>(sT + (i * 64 + lane) * 4);
+    for (int i = 0; i < MC; ++i) ta[i] = ds_read_tr(sT + 256 * i + (4 * g + (l16 >> 2)) * 16 + 4 * (l16 & 3));
     f32x4 E[MC];
     bf16x4 eb[MC];
 #pragma unroll
