@@ -18,7 +18,10 @@ the same token count is timed under "varlen", and the backward pass (dq, dk,
 dv, dbeta, dS0 given dO and dS_L) of the same workload under "backward".
 "call_ms" has per-call median/p10/p90 times, warm and cold (1 GiB written
 between calls); "decode_512" the decode step with a state twice the Infinity
-Cache; "measured_peaks" a device copy and vendor GEMMs for reference.
+Cache; "configs" the lm340m-bf16 and long-stiff-f32 forwards, each with its
+roofline, per-call times and oracle baseline; "measured_peaks" what the
+library's reference copy and MFMA-loop kernels reach (include/efla_peaks.h),
+against which every roofline also states a fraction.
 """
 from __future__ import annotations
 
@@ -313,21 +316,23 @@ def bench_decode(args, dev, n_distinct=8, n_seq=None):
         if st:
             raise RuntimeError("decode failed")
 
+    # the workload's 1000 steps; --decode-only (counter runs) takes --steps
+    n_steps = args.steps if args.decode_only else w.steps
     for i in range(10):
         step(i)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for i in range(w.steps):
+    for i in range(n_steps):
         step(i)
     e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / w.steps
+    ms = e0.elapsed_time(e1) / n_steps
     nh = w.N * w.H
     by = nh * (2 * w.d_k * w.d_v * 4 + (2 * w.d_k + 2 * w.d_v) * 4 + 4)
     return {"workload": w.name, "N": w.N, "H": w.H, "d_k": w.d_k, "d_v": w.d_v,
-            "steps": w.steps, "ms_per_step": ms, "GB_s": by / (ms * 1e-3) / 1e9,
+            "steps": n_steps, "ms_per_step": ms, "GB_s": by / (ms * 1e-3) / 1e9,
             "hbm_frac": by / (ms * 1e-3) / HBM_PEAK, "algorithmic_bytes": by,
             "note": f"{n_distinct} distinct token sets cycled over the steps; the state is "
                     f"{nh * w.d_k * w.d_v * 4} B against the 256 MiB Infinity Cache"}
@@ -367,6 +372,27 @@ def bench_varlen(args, dev, n_seq=16):
     return {"sequences": n_seq, "heads": H, "tokens_per_head": T, "longest": max(lengths),
             "shortest": min(lengths), "kernel_ms": ms, "tokens_per_s": T / (ms * 1e-3),
             "note": "lm1.3b-bf16 recipe; random lengths; the longest sequence sets the time"}
+
+
+def bench_config(args, name, dev):
+    """Another workload, timed like the headline one on the path AUTO takes
+    for it, with its roofline (fp32 workloads against the fp32 MFMA peak),
+    warm and cold per-call times, and the fp64 oracle on the host beside it."""
+    a = argparse.Namespace(**vars(args))
+    a.path, a.no_compare = "auto", True
+    w = wl.FORWARD_WORKLOADS[name]
+    res, host = bench_forward(a, w, dev)
+    out = {k: res[k] for k in ("ms_per_step", "tflops", "mfma_frac", "kernel_ms", "roofline",
+                               "call_ms", "flops_per_token_head")}
+    out["workload"] = w.name
+    out["config"] = res["config"]
+    out["dtype"] = w.dtype
+    out["value"] = res["value"]
+    out["unit"] = "tokens/s"
+    out["token_heads_per_s"] = w.B * w.H * w.L / (res["ms_per_step"] * 1e-3)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, host)
+    return out
 
 
 def backward_flops_per_token(dk, dv, C):
@@ -441,7 +467,9 @@ def bench_backward(args, w, dev):
 
 
 def cpu_baseline(w, host):
-    """The fp64 oracle on the host cores, timed on the whole workload."""
+    """The fp64 oracle on the host cores, timed on the whole workload.  It
+    runs OpenMP over the B*H independent sequences, so the threads it can
+    use are min(available threads, B*H); that is `cores`."""
     import oracle
     q, k, v, beta, S0 = host
     threads = oracle.max_threads()
@@ -450,40 +478,68 @@ def cpu_baseline(w, host):
     oracle.forward(q, k, v, beta, S0)
     t = time.perf_counter() - t0
     return {"value": w.B * w.L / t, "unit": "tokens/s", "cores": min(threads, heads),
+            "threads_available": threads, "cpu_model": cpu_model(),
             "kind": "oracle", "seconds": t,
             "sample": f"whole {w.name} workload ({heads} heads x {w.L} tokens), fp64, "
                       f"OpenMP over heads; inputs converted to fp64 before timing"}
 
 
 def measured_peaks(dev):
-    """What this GPU reaches in practice, beside the published peaks: a 1 GiB
-    device copy (bytes read + written per second) and large square GEMMs in
-    torch (the vendor BLAS) in bf16 and fp32."""
+    """What this GPU reaches in practice, beside the published peaks, from the
+    library's own reference kernels (include/efla_peaks.h): a streaming copy
+    of 1 GiB (bytes read + written per second) and loops of independent MFMAs
+    on register operands, bf16 (v_mfma_f32_16x16x32_bf16) and fp32
+    (v_mfma_f32_16x16x4_f32), eight workgroups of four waves per CU."""
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
     def time_ms(fn, n):
         fn()
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
-        a.record()
+        a.record(stream)
         for _ in range(n):
             fn()
-        b.record()
+        b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
-    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def check(st):
+        if st:
+            raise RuntimeError(f"peak kernel failed: {_lib.status_string(st)}")
+
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
-    t_copy = time_ms(lambda: dst.copy_(src), 10)
+    t_copy = time_ms(lambda: check(_lib.efla_peak_copy(src.data_ptr(), dst.data_ptr(),
+                                                       COPY_BYTES, sp)), 10)
     del src, dst
     out = {"hbm_copy_GB_s": 2 * COPY_BYTES / (t_copy * 1e-3) / 1e9}
-    for name, dtype, n in (("bf16", torch.bfloat16, 8192), ("f32", torch.float32, 4096)):
-        a = torch.randn(n, n, device=dev).to(dtype)
-        b = torch.randn(n, n, device=dev).to(dtype)
-        t = time_ms(lambda: torch.mm(a, b), 10)
-        out[f"{name}_gemm_TFLOP_s"] = 2 * n ** 3 / (t * 1e-3) / 1e12
-        del a, b
-    out["note"] = ("1 GiB device copy; torch.mm of square contiguous matrices (8192^3 bf16, "
-                   "4096^3 fp32); published peaks: 8 TB/s, 2.5 PFLOP/s bf16, 157.3 TFLOP/s fp32")
+    blocks = 256 * 8
+    sink = torch.empty(blocks * 4, dtype=torch.float32, device=dev)
+    for name, dt, iters in (("bf16", _lib.EFLA_BF16, 4000), ("f32", _lib.EFLA_F32, 2000)):
+        fl = [0.0]
+
+        def run():
+            st, fl[0] = _lib.efla_peak_mfma(sink.data_ptr(), blocks, iters, dt, sp)
+            check(st)
+        t = time_ms(run, 5)
+        out[f"{name}_mfma_TFLOP_s"] = fl[0] / (t * 1e-3) / 1e12
+    out["note"] = ("library reference kernels: 1 GiB streaming copy (16-byte loads, "
+                   "non-temporal stores); independent-MFMA loops on register operands, "
+                   f"{blocks} workgroups x 4 waves; published peaks: 8 TB/s, 2.5 PFLOP/s bf16, "
+                   "157.3 TFLOP/s fp32")
     return out
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # --- HBM traffic from rocprofv3 --pmc ----------------------------------------
@@ -529,7 +585,8 @@ def pmc_summary(args):
     w = wl.FORWARD_WORKLOADS[args.workload]
     kname, kre, src = {"fused": ("fused", r"fused_kernel", "fused_forward.hip"),
                        "scan": ("scan", r"scan_kernel", "chunk_scan.hip"),
-                       "ut": ("ut", r"ut_kernel", "ut_transform.hip")}[args.pmc_kernel]
+                       "ut": ("ut", r"ut_kernel", "ut_transform.hip"),
+                       "decode": ("decode", r"decode_kernel", "coef_decode.hip")}[args.pmc_kernel]
 
     def csv_of(sub):
         hits = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)
@@ -544,12 +601,21 @@ def pmc_summary(args):
     w_fac = COPY_BYTES / (cwk * 1024.0)
     hbm = fk * 1024.0 * f_fac + wk * 1024.0 * w_fac
     esz = 2 if w.dtype == "bf16" else 4
-    algo = (fused_work(w, esz, True)[1] if kname == "fused"
-            else stage_work(w, esz)[kname][1])
-    out = os.path.join(PROFILES, f"traffic_{kname}_{w.name}.txt")
-    bench_cmd = f"python bench.py --workload {w.name} --steps 5 --warmup 2 --no-decode --no-cpu-baseline"
+    if kname == "decode":
+        dw = wl.DECODE_WORKLOADS["decode-f32"]
+        n = args.decode_only or 512
+        algo = n * dw.H * (2 * dw.d_k * dw.d_v * 4 + (2 * dw.d_k + 2 * dw.d_v) * 4 + 4)
+        wname = f"decode-f32-N{n}"
+        bench_cmd = f"python bench.py --decode-only {n}"
+    else:
+        algo = (fused_work(w, esz, True)[1] if kname == "fused"
+                else stage_work(w, esz)[kname][1])
+        wname = w.name
+        bench_cmd = (f"python bench.py --workload {w.name} --steps 5 --warmup 2 --no-decode "
+                     "--no-cpu-baseline --no-backward --no-configs --no-peaks --no-cold")
+    out = os.path.join(PROFILES, f"traffic_{kname}_{wname}.txt")
     lines = [
-        f"HBM traffic of {kre} on {w.name} from rocprofv3 --pmc (one counter per run)",
+        f"HBM traffic of {kre} on {wname} from rocprofv3 --pmc (one counter per run)",
         f"  fetch: rocprofv3 --pmc FETCH_SIZE --kernel-include-regex {kre} --output-format csv -- {bench_cmd}",
         f"  write: rocprofv3 --pmc WRITE_SIZE --kernel-include-regex {kre} --output-format csv -- {bench_cmd}",
         "  calibration: the same two counters over python bench.py --copy-calibration --steps 5",
@@ -578,14 +644,19 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache per-call timing")
-    ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy/GEMM peaks")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured copy / MFMA peaks")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the lm340m-bf16 and long-stiff-f32 forward lines")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip timing the Euler variant of the fused kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (traffic counter calibration)")
     ap.add_argument("--pmc-summary", metavar="DIR",
                     help="write profiles/traffic_<kernel>_<workload>.txt from --pmc runs in DIR")
-    ap.add_argument("--pmc-kernel", default="fused", choices=["fused", "scan", "ut"])
+    ap.add_argument("--pmc-kernel", default="fused", choices=["fused", "scan", "ut", "decode"])
+    ap.add_argument("--decode-only", type=int, metavar="N",
+                    help="only time the decode step with N sequences (for --pmc runs)")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args)
@@ -603,6 +674,9 @@ def main():
     if args.copy_calibration:
         copy_calibration(args, dev)
         return
+    if args.decode_only:
+        print(json.dumps(bench_decode(args, dev, n_seq=args.decode_only)), flush=True)
+        return
     w = wl.FORWARD_WORKLOADS[args.workload]
     print(f"[bench] forward {w.name} path={args.path}", file=sys.stderr, flush=True)
     res, host = bench_forward(args, w, dev)
@@ -618,14 +692,35 @@ def main():
     if not args.no_backward:
         print(f"[bench] backward {w.name}", file=sys.stderr, flush=True)
         res["backward"] = bench_backward(args, w, dev)
+    if not args.no_configs:
+        res["configs"] = {}
+        for name in ("lm340m-bf16", "long-stiff-f32"):
+            if name == w.name:
+                continue
+            print(f"[bench] forward {name}", file=sys.stderr, flush=True)
+            res["configs"][name] = bench_config(args, name, dev)
     if not args.no_peaks:
         print("[bench] measured peaks", file=sys.stderr, flush=True)
         pk = measured_peaks(dev)
+        # the HBM figure: the better of the reference copy and the decode step
+        # at N = 512 (a state twice the Infinity Cache), which streams HBM too
+        hbm = pk["hbm_copy_GB_s"]
+        src = "reference copy kernel"
+        if "decode_512" in res and res["decode_512"]["GB_s"] > hbm:
+            hbm, src = res["decode_512"]["GB_s"], "decode step at N=512"
+        pk["hbm_GB_s"], pk["hbm_source"] = hbm, src
         res["measured_peaks"] = pk
-        rf = res["roofline"]
-        ref = pk["hbm_copy_GB_s"] if rf["bound"] == "hbm" else pk[f"{w.dtype}_gemm_TFLOP_s"]
-        rf["measured_peak"] = ref
-        rf["frac_of_measured_peak"] = rf["achieved"] / ref
+
+        def attach(rf, dtype):
+            ref = hbm if rf["bound"] == "hbm" else pk[f"{dtype}_mfma_TFLOP_s"]
+            rf["measured_peak"] = ref
+            rf["frac_of_measured_peak"] = rf["achieved"] / ref
+        attach(res["roofline"], w.dtype)
+        for c in res.get("configs", {}).values():
+            attach(c["roofline"], c["dtype"])
+        if "decode" in res:
+            for key in ("decode", "decode_512"):
+                res[key]["frac_of_measured_hbm"] = res[key]["GB_s"] / hbm
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, host)

@@ -1,4 +1,5 @@
-"""ctypes binding of libefla.so: the C ABI of include/efla.h, name for name.
+"""ctypes binding of libefla.so: the C ABI of include/efla.h (and the peak
+reference kernels of include/efla_peaks.h), name for name.
 
 Argument marshalling only.  Every step of the operator runs in the HIP
 kernels of libefla.so; if the library is missing this module raises instead
@@ -41,6 +42,9 @@ SIGNATURES = [
     ("efla_backward_workspace_size", _S, [_I] * 7),
     ("efla_backward", _I, [_P] * 12 + [_I] * 8 + [_P, _S, _P]),
     ("efla_backward_config", _I, [_P] * 12 + [_I] * 8 + [_P, _P, _S, _P]),
+    # include/efla_peaks.h
+    ("efla_peak_copy", _I, [_P, _P, _S, _P]),
+    ("efla_peak_mfma", _I, [_P, _I, _I, _I, _P, _P]),
 ]
 
 
@@ -178,3 +182,14 @@ def efla_backward_config(q, k, v, beta, S0, d_o, dS_L, dq, dk_, dv_, dbeta, dS0,
     return _call("efla_backward_config", q, k, v, beta, S0, d_o, dS_L, dq, dk_, dv_, dbeta, dS0, B,
                  H, L, dk, dv, chunk, dt, update, None if cfg is None else ctypes.byref(cfg), ws,
                  ws_bytes, stream)
+
+
+def efla_peak_copy(src, dst, nbytes, stream) -> int:
+    return _call("efla_peak_copy", src, dst, nbytes, stream)
+
+
+def efla_peak_mfma(sink, blocks, iters, dt, stream) -> tuple:
+    """(status, flops of one launch)."""
+    fl = ctypes.c_double(0.0)
+    st = _call("efla_peak_mfma", sink, blocks, iters, dt, ctypes.byref(fl), stream)
+    return st, fl.value

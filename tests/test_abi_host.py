@@ -11,16 +11,20 @@ import pytest
 from delta_rule_sequence_alpha_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "efla.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 FAKE = 0x10000        # a 16-byte-aligned pointer value that is never dereferenced
 MISALIGNED = 0x10008
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(efla_[a-z_]+)\s*\(", text)))
+    """Every function declared in include/*.h."""
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(efla_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +36,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 18
+    assert len(declared) == 20
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], check=True,
                          capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (efla_[a-z_]+)\b", out))
@@ -248,3 +252,16 @@ def test_library_reads_no_environment():
     out = subprocess.run(["nm", "-D", "--undefined-only", _lib.LIB_PATH], check=True,
                          capture_output=True, text=True).stdout
     assert not re.search(r"\b(secure_)?getenv\b", out)
+
+
+def test_peak_kernel_validation(lib):
+    """The peak reference kernels validate before any HIP call."""
+    assert _lib.efla_peak_copy(None, FAKE, 1024, None) == _lib.EFLA_ERR_INVALID_ARG
+    assert _lib.efla_peak_copy(FAKE, MISALIGNED, 1024, None) == _lib.EFLA_ERR_INVALID_ARG
+    assert _lib.efla_peak_copy(FAKE, FAKE + 4096, 1000, None) == _lib.EFLA_ERR_INVALID_ARG  # not x16
+    assert _lib.efla_peak_copy(FAKE, FAKE + 512, 1024, None) == _lib.EFLA_ERR_INVALID_ARG   # overlap
+    assert _lib.efla_peak_copy(FAKE, FAKE + 4096, 0, None) == _lib.EFLA_OK                 # nothing
+    assert _lib.efla_peak_mfma(None, 1, 1, _lib.EFLA_BF16, None)[0] == _lib.EFLA_ERR_INVALID_ARG
+    assert _lib.efla_peak_mfma(FAKE, 0, 1, _lib.EFLA_BF16, None)[0] == _lib.EFLA_ERR_INVALID_ARG
+    assert _lib.efla_peak_mfma(FAKE, 1, 0, _lib.EFLA_F32, None)[0] == _lib.EFLA_ERR_INVALID_ARG
+    assert _lib.efla_peak_mfma(FAKE, 1, 1, 5, None)[0] == _lib.EFLA_ERR_INVALID_ARG
