@@ -33,6 +33,7 @@ SIGNATURES = [
     ("efla_forward_varlen", _I, [_P] * 8 + [_I] * 8 + [_P]),
     ("efla_forward_update", _I, [_P] * 7 + [_I] * 7 + [_P, _S, _I, _I, _P]),
     ("efla_forward_config", _I, [_P] * 7 + [_I] * 7 + [_P, _S, _I, _I, _P, _P]),
+    ("efla_forward_noalloc", _I, [_P] * 7 + [_I] * 7 + [_I, _I, _P]),
     ("efla_decode_step", _I, [_P] * 6 + [_I] * 5 + [_P]),
     ("efla_decode_step_update", _I, [_P] * 6 + [_I] * 6 + [_P]),
     ("efla_coefficients", _I, [_P] * 4 + [_L, _I, _I, _P]),
@@ -132,6 +133,15 @@ def efla_forward_config(q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt, w
     cfg = launch_config(config)
     return _call("efla_forward_config", q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt, ws,
                  ws_bytes, path, update, None if cfg is None else ctypes.byref(cfg), stream)
+
+
+def efla_forward_noalloc(q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt, path, update,
+                         stream) -> int:
+    return _call("efla_forward_noalloc", q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt,
+                 path, update, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # EFLA_NOALLOC_SCRATCH_BYTES
 
 
 def efla_forward_varlen(q, k, v, beta, cu_seqlens, S0, o, S_L, N, H, T, dk, dv, chunk, dt, update,

@@ -3,6 +3,8 @@
 // caller's stream.
 #include <stdint.h>
 
+#include <atomic>
+
 #include "efla.h"
 #include "efla_launch.h"
 
@@ -190,11 +192,45 @@ size_t efla_forward_workspace_size(int B, int H, int L, int dk, int dv, int chun
     return efla_forward_workspace_size_ex(B, H, L, dk, dv, chunk, dt, EFLA_PATH_AUTO);
 }
 
-efla_status_t efla_forward_config(const void *q, const void *k, const void *v, const float *beta,
-                                  const float *S0, void *o, float *S_L, int B, int H, int L,
-                                  int dk, int dv, int chunk, efla_dtype_t dt, void *workspace,
-                                  size_t workspace_bytes, efla_path_t path, efla_update_t update,
-                                  const efla_launch_config_t *config, void *stream)
+}  // extern "C"
+
+namespace {
+
+// The allocation-free forward's scratch: the staged and segmented paths'
+// intermediates, in a fixed device array that the library holds on each
+// device it runs on.  Host code never uses the array's name as an address
+// (on the host it names a stand-in); the device address is looked up once
+// per device, with that device current, and kept.
+constexpr size_t kScratchBytes = EFLA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+hipError_t scratch_address(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+// The forward after the entry point's own argument: intermediates of the
+// staged and segmented paths in `workspace`, or (noalloc) in the scratch
+// array above, for shapes whose workspace fits in it.
+efla_status_t forward_impl(const void *q, const void *k, const void *v, const float *beta,
+                           const float *S0, void *o, float *S_L, int B, int H, int L, int dk,
+                           int dv, int chunk, efla_dtype_t dt, void *workspace,
+                           size_t workspace_bytes, efla_path_t path, efla_update_t update,
+                           const efla_launch_config_t *config, bool noalloc, void *stream)
 {
     efla_status_t s = check_shape(B, H, L, dk, dv, chunk, dt);
     if (s != EFLA_OK) return s;
@@ -224,6 +260,12 @@ efla_status_t efla_forward_config(const void *q, const void *k, const void *v, c
     }
     const SegPlan plan = path == EFLA_PATH_SEGMENTED ? seg_plan(BH, L, dk, dv, chunk) : SegPlan{1, 0};
     const StagedWs ws = staged_ws(B, H, L, dk, dv, chunk, dt, plan.G);
+    if (noalloc && L > 0) {
+        if (ws.total > kScratchBytes) return EFLA_ERR_WORKSPACE;
+        const hipError_t e = scratch_address(&workspace);
+        if (e != hipSuccess) return EFLA_ERR_HIP;
+        workspace_bytes = kScratchBytes;
+    }
     if (L > 0) {
         if (!workspace || workspace_bytes < ws.total) return EFLA_ERR_WORKSPACE;
         if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return EFLA_ERR_INVALID_ARG;
@@ -249,6 +291,29 @@ efla_status_t efla_forward_config(const void *q, const void *k, const void *v, c
         e = efla::dispatch_scan(bf, dk, dv, chunk, q, k, w, u, aqk, S0, o, S_L, (int)BH, L,
                                 cfg.scan_waves, st);
     return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+efla_status_t efla_forward_config(const void *q, const void *k, const void *v, const float *beta,
+                                  const float *S0, void *o, float *S_L, int B, int H, int L,
+                                  int dk, int dv, int chunk, efla_dtype_t dt, void *workspace,
+                                  size_t workspace_bytes, efla_path_t path, efla_update_t update,
+                                  const efla_launch_config_t *config, void *stream)
+{
+    return forward_impl(q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt, workspace,
+                        workspace_bytes, path, update, config, false, stream);
+}
+
+efla_status_t efla_forward_noalloc(const void *q, const void *k, const void *v, const float *beta,
+                                   const float *S0, void *o, float *S_L, int B, int H, int L,
+                                   int dk, int dv, int chunk, efla_dtype_t dt, efla_path_t path,
+                                   efla_update_t update, void *stream)
+{
+    return forward_impl(q, k, v, beta, S0, o, S_L, B, H, L, dk, dv, chunk, dt, nullptr, 0, path,
+                        update, nullptr, true, stream);
 }
 
 efla_status_t efla_forward_update(const void *q, const void *k, const void *v, const float *beta,

@@ -174,6 +174,31 @@ efla_status_t efla_forward_config(const void *q, const void *k, const void *v, c
                                   void *stream);
 
 /*
+ * Allocation-free chunked forward, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): efla_forward_update without a workspace argument.  The
+ * fused path needs no workspace; the staged and segmented paths keep their
+ * intermediates (alpha, W, U, A and the segment maps) in a device array of
+ * EFLA_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs
+ * on until the process ends.  A shape whose workspace on the path taken
+ * (efla_forward_workspace_size_ex) exceeds that size returns
+ * EFLA_ERR_WORKSPACE with nothing launched.  This entry calls no hipMalloc,
+ * hipFree or allocating routine.  Every call on one device shares the array
+ * and relies on nothing it held before (each call writes every intermediate
+ * it reads): calls that overlap in time on one device -- on different streams,
+ * or from host threads without ordering -- race, and the caller must
+ * serialize them.  The first call on a device looks up the array's device
+ * address (hipGetSymbolAddress, with that device current) and keeps it.
+ * Arguments, layouts and results as for efla_forward_update.
+ */
+#define EFLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+efla_status_t efla_forward_noalloc(const void *q, const void *k, const void *v, const float *beta,
+                                   const float *S0, void *o, float *S_L,
+                                   int B, int H, int L, int d_k, int d_v, int chunk,
+                                   efla_dtype_t dt, efla_path_t path, efla_update_t update,
+                                   void *stream);
+
+/*
  * Single-token decode step (the recurrent form of the same update) for N
  * sequences x H heads, in place:
  *   q, k [N,H,d_k]  v [N,H,d_v]  dtype dt;  beta [N,H] fp32

@@ -36,7 +36,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 20
+    assert len(declared) == 21
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], check=True,
                          capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (efla_[a-z_]+)\b", out))
@@ -265,3 +265,30 @@ def test_peak_kernel_validation(lib):
     assert _lib.efla_peak_mfma(FAKE, 0, 1, _lib.EFLA_BF16, None)[0] == _lib.EFLA_ERR_INVALID_ARG
     assert _lib.efla_peak_mfma(FAKE, 1, 0, _lib.EFLA_F32, None)[0] == _lib.EFLA_ERR_INVALID_ARG
     assert _lib.efla_peak_mfma(FAKE, 1, 1, 5, None)[0] == _lib.EFLA_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
+    """efla_forward_noalloc validates like efla_forward_update and refuses a
+    staged or segmented shape whose intermediates exceed its fixed scratch,
+    before any HIP call."""
+    def f(**o):
+        a = dict(B=1, H=2, L=64, dk=16, dv=16, chunk=16, dt=_lib.EFLA_F32, path=_lib.EFLA_PATH_STAGED,
+                 update=_lib.EFLA_EXACT, q=FAKE, S_L=FAKE)
+        a.update(o)
+        return _lib.efla_forward_noalloc(a["q"], FAKE, FAKE, FAKE, None, FAKE, a["S_L"], a["B"],
+                                         a["H"], a["L"], a["dk"], a["dv"], a["chunk"], a["dt"],
+                                         a["path"], a["update"], None)
+    big = dict(B=4, H=16, L=4096, dk=128, dv=128, chunk=64)     # 168 MB of intermediates (bf16)
+    need = _lib.efla_forward_workspace_size_ex(4, 16, 4096, 128, 128, 64, _lib.EFLA_BF16,
+                                               _lib.EFLA_PATH_STAGED)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    assert f(dt=_lib.EFLA_BF16, **big) == _lib.EFLA_ERR_WORKSPACE
+    assert f(dt=_lib.EFLA_F32, path=_lib.EFLA_PATH_SEGMENTED, B=1, H=16, L=65536, dk=128, dv=128,
+             chunk=64) == _lib.EFLA_ERR_WORKSPACE
+    assert f(dt=7) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(update=3) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(path=9) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(dk=24) == _lib.EFLA_ERR_UNSUPPORTED
+    assert f(S_L=None) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(q=MISALIGNED) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(B=0) == _lib.EFLA_OK          # nothing to do, nothing launched
