@@ -6,6 +6,7 @@ runs in the library's HIP kernels.
 
   forward(q, k, v, beta, S0=None, chunk=64, path="auto", update="exact") -> (o, S_L)
   decode_step(q, k, v, beta, S, update="exact") -> o     (S updated in place)
+  decode_step_indexed(q, k, v, beta, slots, S_pool) -> o  (pool entries slots[n] in place)
   forward_varlen(q, k, v, beta, cu_seqlens, S0=None, chunk=64) -> (o, S_L)
                                               packed sequences, [H, T, d] tensors
   coefficients(k, beta, update="exact") -> (alpha, lambda)   stage 1 of the staged path
@@ -26,8 +27,8 @@ from . import _lib
 from ._lib import (EFLA_BF16, EFLA_EULER, EFLA_EXACT, EFLA_F32, EFLA_PATH_AUTO, EFLA_PATH_FUSED,
                    EFLA_PATH_SEGMENTED, EFLA_PATH_STAGED, EflaError, LIB_PATH)
 
-__all__ = ["forward", "forward_varlen", "decode_step", "coefficients", "ut_transform", "chunk_scan",
-           "backward", "efla", "workspace_size", "backward_workspace_size", "EflaError", "LIB_PATH"]
+__all__ = ["forward", "forward_varlen", "decode_step", "decode_step_indexed", "coefficients", "ut_transform", "chunk_scan",
+           "backward", "efla", "workspace_size", "varlen_workspace_size", "backward_workspace_size", "EflaError", "LIB_PATH"]
 
 _PATHS = {"auto": EFLA_PATH_AUTO, "staged": EFLA_PATH_STAGED, "fused": EFLA_PATH_FUSED,
           "segmented": EFLA_PATH_SEGMENTED}
@@ -94,8 +95,10 @@ def forward(q, k, v, beta, S0=None, chunk: int = 64, path: str = "auto", workspa
     dev = q.device
     if out is None:
         out = torch.empty((B, H, L, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", (B, H, L, dv), q.dtype)
     if S_L is None:
         S_L = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check(S_L, "S_L", (B, H, dk, dv), torch.float32)
     p = _PATHS[path]
     need = _lib.efla_forward_workspace_size_ex(B, H, L, dk, dv, chunk, dt, p)
     if workspace is None and need > 0:
@@ -108,10 +111,17 @@ def forward(q, k, v, beta, S0=None, chunk: int = 64, path: str = "auto", workspa
     return out, S_L
 
 
+def varlen_workspace_size(N, H, T, d_k, d_v, chunk, dtype, path="auto") -> int:
+    """Bytes of device workspace forward_varlen needs on ``path``."""
+    dt = EFLA_BF16 if dtype == torch.bfloat16 else EFLA_F32
+    return _lib.efla_forward_varlen_workspace_size(N, H, T, d_k, d_v, chunk, dt, _PATHS[path])
+
+
 def forward_varlen(q, k, v, beta, cu_seqlens, S0=None, chunk: int = 64, out=None, S_L=None,
-                   update: str = "exact"):
+                   update: str = "exact", path: str = "auto", workspace=None):
     """Packed sequences: q, k [H,T,d_k], v [H,T,d_v], beta [H,T]; cu_seqlens int32
-    [N+1] on the device.  Returns (o [H,T,d_v], S_L [N,H,d_k,d_v] fp32)."""
+    [N+1] on the device.  Returns (o [H,T,d_v], S_L [N,H,d_k,d_v] fp32).
+    ``workspace`` (uint8, >= varlen_workspace_size bytes) may be preallocated."""
     H, T, dk = k.shape
     dv = v.shape[-1]
     N = cu_seqlens.numel() - 1
@@ -125,12 +135,20 @@ def forward_varlen(q, k, v, beta, cu_seqlens, S0=None, chunk: int = 64, out=None
         _check(S0, "S0", (N, H, dk, dv), torch.float32)
     if out is None:
         out = torch.empty((H, T, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", (H, T, dv), q.dtype)
     if S_L is None:
         S_L = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
-    st = _lib.efla_forward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(cu_seqlens), _ptr(S0),
-                                  _ptr(out), _ptr(S_L), N, H, T, dk, dv, chunk, dt,
-                                  _UPDATES[update], _stream(q.device))
-    _raise(st, "efla_forward_varlen")
+    _check(S_L, "S_L", (N, H, dk, dv), torch.float32)
+    p = _PATHS[path]
+    need = _lib.efla_forward_varlen_workspace_size(N, H, T, dk, dv, chunk, dt, p)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.efla_forward_varlen_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(cu_seqlens),
+                                     _ptr(S0), _ptr(out), _ptr(S_L), N, H, T, dk, dv, chunk, dt,
+                                     _UPDATES[update], p, _ptr(workspace), ws_bytes,
+                                     _stream(q.device))
+    _raise(st, "efla_forward_varlen_ex")
     return out, S_L
 
 
@@ -146,9 +164,38 @@ def decode_step(q, k, v, beta, S, out=None, update: str = "exact"):
     _check(S, "S", (N, H, dk, dv), torch.float32)
     if out is None:
         out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", (N, H, dv), q.dtype)
     st = _lib.efla_decode_step_update(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(out),
                                       N, H, dk, dv, dt, _UPDATES[update], _stream(q.device))
     _raise(st, "efla_decode_step_update")
+    return out
+
+
+def decode_step_indexed(q, k, v, beta, slots, S_pool, out=None, err=None, update: str = "exact"):
+    """One decode step for N tokens whose states are pool entries: token n
+    updates S_pool[slots[n]] ([P,H,d_k,d_v] fp32) in place.  slots: int32 [N]
+    on the device, distinct, in [0, P).  err (int32 [1] on the device, or
+    None): OR-ed with 1 / 2 for repeated / out-of-range slots, whose tokens
+    are rejected (pool untouched, o = NaN).  Returns o [N,H,d_v]."""
+    N, H, dk = k.shape
+    dv = v.shape[-1]
+    P = S_pool.shape[0]
+    dt = _dt(q)
+    _check(q, "q", (N, H, dk), q.dtype)
+    _check(k, "k", (N, H, dk), q.dtype)
+    _check(v, "v", (N, H, dv), q.dtype)
+    _check(beta, "beta", (N, H), torch.float32)
+    _check(slots, "slots", (N,), torch.int32)
+    _check(S_pool, "S_pool", (P, H, dk, dv), torch.float32)
+    if err is not None:
+        _check(err, "err", (1,), torch.int32)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", (N, H, dv), q.dtype)
+    st = _lib.efla_decode_step_indexed(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(slots),
+                                       _ptr(S_pool), _ptr(out), _ptr(err), N, H, P, dk, dv, dt,
+                                       _UPDATES[update], _stream(q.device))
+    _raise(st, "efla_decode_step_indexed")
     return out
 
 

@@ -31,11 +31,14 @@ SIGNATURES = [
     ("efla_forward", _I, [_P] * 7 + [_I] * 7 + [_P, _S, _P]),
     ("efla_forward_ex", _I, [_P] * 7 + [_I] * 7 + [_P, _S, _I, _P]),
     ("efla_forward_varlen", _I, [_P] * 8 + [_I] * 8 + [_P]),
+    ("efla_forward_varlen_workspace_size", _S, [_I] * 8),
+    ("efla_forward_varlen_ex", _I, [_P] * 8 + [_I] * 9 + [_P, _S, _P]),
     ("efla_forward_update", _I, [_P] * 7 + [_I] * 7 + [_P, _S, _I, _I, _P]),
     ("efla_forward_config", _I, [_P] * 7 + [_I] * 7 + [_P, _S, _I, _I, _P, _P]),
     ("efla_forward_noalloc", _I, [_P] * 7 + [_I] * 7 + [_I, _I, _P]),
     ("efla_decode_step", _I, [_P] * 6 + [_I] * 5 + [_P]),
     ("efla_decode_step_update", _I, [_P] * 6 + [_I] * 6 + [_P]),
+    ("efla_decode_step_indexed", _I, [_P] * 8 + [_I] * 7 + [_P]),
     ("efla_coefficients", _I, [_P] * 4 + [_L, _I, _I, _P]),
     ("efla_coefficients_update", _I, [_P] * 4 + [_L, _I, _I, _I, _P]),
     ("efla_ut_transform", _I, [_P] * 7 + [_I] * 7 + [_P]),
@@ -150,12 +153,28 @@ def efla_forward_varlen(q, k, v, beta, cu_seqlens, S0, o, S_L, N, H, T, dk, dv, 
                  chunk, dt, update, stream)
 
 
+def efla_forward_varlen_workspace_size(N, H, T, dk, dv, chunk, dt, path) -> int:
+    return int(lib().efla_forward_varlen_workspace_size(N, H, T, dk, dv, chunk, dt, path))
+
+
+def efla_forward_varlen_ex(q, k, v, beta, cu_seqlens, S0, o, S_L, N, H, T, dk, dv, chunk, dt,
+                           update, path, ws, ws_bytes, stream) -> int:
+    return _call("efla_forward_varlen_ex", q, k, v, beta, cu_seqlens, S0, o, S_L, N, H, T, dk, dv,
+                 chunk, dt, update, path, ws, ws_bytes, stream)
+
+
 def efla_decode_step(q, k, v, beta, S, o, N, H, dk, dv, dt, stream) -> int:
     return _call("efla_decode_step", q, k, v, beta, S, o, N, H, dk, dv, dt, stream)
 
 
 def efla_decode_step_update(q, k, v, beta, S, o, N, H, dk, dv, dt, update, stream) -> int:
     return _call("efla_decode_step_update", q, k, v, beta, S, o, N, H, dk, dv, dt, update, stream)
+
+
+def efla_decode_step_indexed(q, k, v, beta, slots, S_pool, o, err, N, H, P, dk, dv, dt, update,
+                             stream) -> int:
+    return _call("efla_decode_step_indexed", q, k, v, beta, slots, S_pool, o, err, N, H, P, dk, dv,
+                 dt, update, stream)
 
 
 def efla_coefficients(k, beta, alpha, lam, n_tokens, dk, dt, stream) -> int:

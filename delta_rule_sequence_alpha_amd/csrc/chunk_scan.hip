@@ -39,6 +39,14 @@ struct SegArgs {
     const float *Sin;  // REPLAY: [BH, G, DK, DV]
     void *states;      // WHOLE, optional: the entry state of every chunk [BH, nchunks, DK, DV],
                        // stored in the input dtype
+    // Packed sequences (cu != NULL): BH = N * H with bh = seq * H + h; head
+    // h's L tokens hold the N sequences back to back, sequence seq at
+    // [cu[seq], cu[seq+1]), and A is stored by token ([H, L, C], valid rows
+    // only).  Each sequence is split into G segments of ceil(chunks / G)
+    // chunks (seg_chunks is not used); a segment with no chunk maps its
+    // entry state to itself.
+    const int *cu = nullptr;
+    int H = 1;
 };
 
 template <typename T, int DK, int DV, int C, int NW>
@@ -83,7 +91,22 @@ __device__ __forceinline__ void scan_body(
     const bool ptile = tile >= NTILE;                 // a column of P (U = 0, from S = I)
     const int utile = ptile ? 0 : tile;               // U columns read (ignored for P)
     const int col = (ptile ? tile - NTILE : tile) * TV + 16 * wv + l16;   // this lane's column
-    const int c_begin = gs * sg.seg_chunks, c_end = min(nchunks, c_begin + sg.seg_chunks);
+    // this sequence's tokens and chunks
+    long tokb = (long)bh * L;
+    int Ls = L, seg_chunks = sg.seg_chunks;
+    if (sg.cu) {
+        const int seq = bh / sg.H, h = bh - seq * sg.H;
+        const int t0 = packed_begin(sg.cu, seq, L);
+        tokb = (long)h * L + t0;
+        Ls = packed_end(sg.cu, seq, L) - t0;
+        nchunks = (Ls + C - 1) / C;
+        seg_chunks = sg.G > 1 ? (nchunks + sg.G - 1) / sg.G : nchunks;
+    }
+    const int c_begin = gs * seg_chunks, c_end = min(nchunks, c_begin + seg_chunks);
+    // chunk c's A block: per chunk, or (packed) by token
+    auto a_at = [&](int c) {
+        return sg.cu ? aqk + (tokb + (long)c * C) * C : aqk + ((long)bh * nchunks + c) * C * C;
+    };
 
     f32x4 S[MK];
     const long sbase = (long)bh * DK * DV;
@@ -123,21 +146,23 @@ __device__ __forceinline__ void scan_body(
     const bool want_o = sg.mode != SCAN_SUMMARY && o;
     auto load_all = [&](int cn) {
         cn = min(cn, c_end - 1);
-        const long t0 = (long)bh * L + (long)cn * C;
-        const int vn = min(C, L - cn * C);
+        const long t0 = tokb + (long)cn * C;
+        const int vn = min(C, Ls - cn * C);
         rW.load(w + t0 * DK, DK, vn);
         rK.load(k + t0 * DK, DK, vn);
         rU.load(u + t0 * DV + utile * TV, DV, vn);
         if (want_o) {
             rQ.load(q + t0 * DK, DK, vn);
-            rA.load(aqk + ((long)bh * nchunks + cn) * C * C, C, C);
+            rA.load(a_at(cn), C, sg.cu ? vn : C);
         }
     };
-    if constexpr (PREFETCH) load_all(c_begin);
+    if constexpr (PREFETCH) {
+        if (c_begin < c_end) load_all(c_begin);
+    }
 
     for (int c = c_begin; c < c_end; ++c) {
-        const long tok0 = (long)bh * L + (long)c * C;
-        const int valid = min(C, L - c * C);
+        const long tok0 = tokb + (long)c * C;
+        const int valid = min(C, Ls - c * C);
         __syncthreads();   // the previous chunk is done with LDS (and this chunk's loads have landed)
         if constexpr (PREFETCH) {
             rW.store(sW, Lay::LDK, valid);
@@ -145,7 +170,7 @@ __device__ __forceinline__ void scan_body(
             rU.store(sU, Lay::LDU, valid);
             if (want_o) {
                 rQ.store(sQ, Lay::LDK, valid);
-                rA.store(sA, Lay::LDC, C);
+                rA.store(sA, Lay::LDC, sg.cu ? valid : C);
             }
         } else {
             RW t;
@@ -158,8 +183,9 @@ __device__ __forceinline__ void scan_body(
             if (want_o) {
                 t.load(q + tok0 * DK, DK, valid);
                 t.store(sQ, Lay::LDK, valid);
-                rA.load(aqk + ((long)bh * nchunks + c) * C * C, C, C);
-                rA.store(sA, Lay::LDC, C);
+                const int arows = sg.cu ? valid : C;
+                rA.load(a_at(c), C, arows);
+                rA.store(sA, Lay::LDC, arows);
             }
         }
         __syncthreads();
@@ -319,17 +345,17 @@ template <typename T, int DK, int DV, int C>
 hipError_t launch_scan_segmented(const void *q, const void *k, const void *w, const void *u,
                                  const void *aqk, const float *S0, void *o, float *SL, int BH,
                                  int L, int G, int seg_chunks, float *R, float *P, float *Sin,
-                                 int nw, hipStream_t st)
+                                 int nw, const int *cu, int H, hipStream_t st)
 {
     if (BH == 0) return hipSuccess;
-    SegArgs sum{SCAN_SUMMARY, G, seg_chunks, R, P, nullptr, nullptr};
+    SegArgs sum{SCAN_SUMMARY, G, seg_chunks, R, P, nullptr, nullptr, cu, H};
     hipError_t e = launch_scan_auto<T, DK, DV, C>(q, k, w, u, aqk, nullptr, o, SL, BH, L, nw, sum, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((seg_combine_kernel<DK, DV>), dim3((unsigned)(BH * (DV / 16))), dim3(256), 0,
                        st, S0, P, R, Sin, G);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    SegArgs rep{SCAN_REPLAY, G, seg_chunks, nullptr, nullptr, Sin, nullptr};
+    SegArgs rep{SCAN_REPLAY, G, seg_chunks, nullptr, nullptr, Sin, nullptr, cu, H};
     return launch_scan_auto<T, DK, DV, C>(q, k, w, u, aqk, nullptr, o, SL, BH, L, nw, rep, st);
 }
 
@@ -722,9 +748,9 @@ hipError_t dispatch_scan_pair(bool bf16, int dk, int dv, int chunk, const void *
 
 hipError_t dispatch_scan(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                          const void *w, const void *u, const void *aqk, const float *S0, void *o,
-                         float *SL, int BH, int L, int nw, hipStream_t st)
+                         float *SL, int BH, int L, int nw, hipStream_t st, const int *cu, int H)
 {
-    const SegArgs whole{SCAN_WHOLE, 1, 1 << 30, nullptr, nullptr, nullptr, nullptr};
+    const SegArgs whole{SCAN_WHOLE, 1, 1 << 30, nullptr, nullptr, nullptr, nullptr, cu, H};
 #define CASE(DKV, DVV, CC)                                                                      \
     if (dk == DKV && dv == DVV && chunk == CC)                                                  \
         return bf16 ? launch_scan_auto<__bf16, DKV, DVV, CC>(q, k, w, u, aqk, S0, o, SL, BH, L, \
@@ -740,14 +766,16 @@ hipError_t dispatch_scan_segmented(bool bf16, int dk, int dv, int chunk, const v
                                    const void *k, const void *w, const void *u, const void *aqk,
                                    const float *S0, void *o, float *SL, int BH, int L, int G,
                                    int seg_chunks, float *R, float *P, float *Sin, int nw,
-                                   hipStream_t st)
+                                   hipStream_t st, const int *cu, int H)
 {
 #define CASE(DKV, DVV, CC)                                                                      \
     if (dk == DKV && dv == DVV && chunk == CC)                                                  \
         return bf16 ? launch_scan_segmented<__bf16, DKV, DVV, CC>(                              \
-                          q, k, w, u, aqk, S0, o, SL, BH, L, G, seg_chunks, R, P, Sin, nw, st)  \
+                          q, k, w, u, aqk, S0, o, SL, BH, L, G, seg_chunks, R, P, Sin, nw, cu,  \
+                          H, st)                                                                \
                     : launch_scan_segmented<float, DKV, DVV, CC>(                               \
-                          q, k, w, u, aqk, S0, o, SL, BH, L, G, seg_chunks, R, P, Sin, nw, st);
+                          q, k, w, u, aqk, S0, o, SL, BH, L, G, seg_chunks, R, P, Sin, nw, cu,  \
+                          H, st);
     EFLA_SHAPE_CASES(CASE)
 #undef CASE
     return hipErrorInvalidValue;

@@ -70,20 +70,43 @@ struct DecodeShape {
     static constexpr int RPT = DK / RG;                                  // rows per thread
 };
 
+// Slot-indexed form (slots != NULL): token n's state is entry slots[n] of a
+// pool of P sequences, nh = n * H + h.  A slot outside [0, P), or one that
+// more than one token of the batch names, is rejected: its tokens leave the
+// pool untouched, their outputs are NaN, and err (if given) is OR-ed with 2
+// or 1.  Every thread of the workgroup takes the same decision (the slot is
+// per token, the repeat test is reduced over the workgroup).
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const float *__restrict__ beta, float *__restrict__ S, T *__restrict__ o, int euler)
+    const float *__restrict__ beta, float *__restrict__ S, T *__restrict__ o, int euler,
+    const int *__restrict__ slots, int N, int H, int P, int *__restrict__ err)
 {
     using Sh = DecodeShape<DK, DV>;
     constexpr int NT = Sh::NT, CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT;
     static_assert(RG * CG == NT && RPT * RG == DK, "decode shape");
+    static_assert(NT >= DV, "one thread per output column of a rejected token");
     __shared__ float sk[DK], sq[DK], sv[DV];
     __shared__ float4 red_k[RG][CG], red_q[RG][CG];
     __shared__ float s_alpha, s_kq;
 
     const long nh = blockIdx.x;
     const int tid = threadIdx.x;
+    long sidx = nh;   // the state this token updates
+    if (slots) {
+        const int n = (int)(nh / H), h = (int)(nh - (long)n * H);
+        const int slot = slots[n];
+        const int bad = slot < 0 || slot >= P;
+        int rep = 0;
+        for (int j = tid; j < N; j += NT) rep |= (j != n && slots[j] == slot);
+        rep = __syncthreads_or(rep);
+        if (bad || rep) {
+            if (tid < DV) o[nh * DV + tid] = from_f32<T>(__builtin_nanf(""));
+            if (tid == 0 && err) atomicOr(err, (bad ? 2 : 0) | (rep ? 1 : 0));
+            return;
+        }
+        sidx = (long)slot * H + h;
+    }
     for (int i = tid; i < DK; i += NT) {
         sk[i] = to_f32(k[nh * DK + i]);
         sq[i] = to_f32(q[nh * DK + i]);
@@ -91,7 +114,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     for (int i = tid; i < DV; i += NT) sv[i] = to_f32(v[nh * DV + i]);
 
     const int c = tid % CG, rg = tid / CG;
-    float4 *Sp = reinterpret_cast<float4 *>(S + nh * DK * DV);
+    float4 *Sp = reinterpret_cast<float4 *>(S + sidx * DK * DV);
     float4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) s[i] = Sp[(rg + i * RG) * CG + c];
@@ -163,13 +186,14 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
 
 template <typename T, int DK, int DV>
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *beta, float *S,
-                         void *o, long NH, bool euler, hipStream_t st)
+                         void *o, long NH, bool euler, const int *slots, int N, int H, int P,
+                         int *err, hipStream_t st)
 {
     if (NH == 0) return hipSuccess;
     hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3((unsigned)NH),
                        dim3(DecodeShape<DK, DV>::NT), 0, st, static_cast<const T *>(q),
                        static_cast<const T *>(k), static_cast<const T *>(v), beta, S,
-                       static_cast<T *>(o), (int)euler);
+                       static_cast<T *>(o), (int)euler, slots, N, H, P, err);
     return hipGetLastError();
 }
 
@@ -207,12 +231,14 @@ hipError_t dispatch_coef(bool bf16, int dk, const void *k, const float *beta, fl
 
 hipError_t dispatch_decode(bool bf16, int dk, int dv, const void *q, const void *k, const void *v,
                            const float *beta, float *S, void *o, long NH, bool euler,
-                           hipStream_t st)
+                           hipStream_t st, const int *slots, int N, int H, int P, int *err)
 {
 #define CASE2(DKV, DVV)                                                                      \
     if (dk == DKV && dv == DVV)                                                              \
-        return bf16 ? launch_decode<__bf16, DKV, DVV>(q, k, v, beta, S, o, NH, euler, st)    \
-                    : launch_decode<float, DKV, DVV>(q, k, v, beta, S, o, NH, euler, st);
+        return bf16 ? launch_decode<__bf16, DKV, DVV>(q, k, v, beta, S, o, NH, euler, slots,  \
+                                                      N, H, P, err, st)                      \
+                    : launch_decode<float, DKV, DVV>(q, k, v, beta, S, o, NH, euler, slots,   \
+                                                     N, H, P, err, st);
 #define CASE(D) CASE2(D, 16) CASE2(D, 32) CASE2(D, 64) CASE2(D, 128)
     EFLA_D_CASES(CASE)
 #undef CASE

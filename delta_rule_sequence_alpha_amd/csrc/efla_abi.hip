@@ -82,6 +82,67 @@ StagedWs staged_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t 
     return s;
 }
 
+// Packed-sequence (varlen) staged workspace: alpha, W, U over every token of
+// the H heads, A by token ([H, T, chunk]), the chunk offsets of the sequences
+// (int32 [N+1]) and, for G > 1 segments per sequence, the segment maps and
+// entry states (fp32).
+struct VarlenWs {
+    size_t alpha, w, u, aqk, cuc, R, P, Sin, total;
+};
+
+VarlenWs varlen_ws(int N, int H, int T, int dk, int dv, int chunk, efla_dtype_t dt, int G)
+{
+    const size_t n = (size_t)H * T;
+    const size_t segs = (size_t)N * H * G;
+    VarlenWs s;
+    s.alpha = 0;
+    s.w = s.alpha + align_up(n * sizeof(float));
+    s.u = s.w + align_up(n * dk * esize(dt));
+    s.aqk = s.u + align_up(n * dv * esize(dt));
+    s.cuc = s.aqk + align_up(n * chunk * esize(dt));
+    s.R = s.cuc + align_up(((size_t)N + 1) * sizeof(int));
+    s.total = s.P = s.Sin = s.R;
+    if (G > 1) {
+        s.P = s.R + align_up(segs * dk * dv * sizeof(float));
+        s.Sin = s.P + align_up(segs * dk * dk * sizeof(float));
+        s.total = s.Sin + align_up(segs * dk * dv * sizeof(float));
+    }
+    return s;
+}
+
+// Shape checks of the packed entry points: the tensors are [H, T, d] (one
+// "batch" of H rows of T tokens) and N * H sequences; the UT transform's grid
+// has at most ceil(T / chunk) + N chunks per head.
+efla_status_t check_varlen(int N, int H, int T, int dk, int dv, int chunk, efla_dtype_t dt)
+{
+    const efla_status_t s = check_shape(1, H, T, dk, dv, chunk, dt);
+    if (s != EFLA_OK) return s;
+    if (N < 0) return EFLA_ERR_INVALID_ARG;
+    const long long NH = (long long)N * H;
+    if (NH * 8 > INT32_MAX) return EFLA_ERR_UNSUPPORTED;
+    if ((long long)H * (((long long)T + chunk - 1) / chunk + N) > INT32_MAX)
+        return EFLA_ERR_UNSUPPORTED;
+    return EFLA_OK;
+}
+
+// The packed path: AUTO takes the fused kernel where it exists, else the
+// segmented scan when a sequence as long as the whole token axis would be
+// split, else the staged one.  G for the segmented path is planned for that
+// longest possible sequence; shorter ones leave segments empty.
+efla_path_t resolve_varlen_path(efla_path_t p, efla_dtype_t dt, int N, int H, int T, int dk,
+                                int dv, int chunk)
+{
+    if (p != EFLA_PATH_AUTO) return p;
+    if (efla::fused_supported(dt == EFLA_BF16, dk, dv, chunk)) return EFLA_PATH_FUSED;
+    return seg_plan((long long)N * H, T, dk, dv, chunk).G > 1 ? EFLA_PATH_SEGMENTED
+                                                               : EFLA_PATH_STAGED;
+}
+
+int varlen_G(efla_path_t p, int N, int H, int T, int dk, int dv, int chunk)
+{
+    return p == EFLA_PATH_SEGMENTED ? seg_plan((long long)N * H, T, dk, dv, chunk).G : 1;
+}
+
 // Backward workspace: the forward's coefficient and UT-transform outputs,
 // plus every chunk's entry state, dS_out and dE (in the input dtype), and for
 // G > 1 segments the segment maps and boundary states (fp32) that the two
@@ -326,19 +387,33 @@ efla_status_t efla_forward_update(const void *q, const void *k, const void *v, c
                                workspace_bytes, path, update, nullptr, stream);
 }
 
-efla_status_t efla_forward_varlen(const void *q, const void *k, const void *v, const float *beta,
-                                  const int *cu_seqlens, const float *S0, void *o, float *S_L,
-                                  int N, int H, int T, int dk, int dv, int chunk, efla_dtype_t dt,
-                                  efla_update_t update, void *stream)
+size_t efla_forward_varlen_workspace_size(int N, int H, int T, int dk, int dv, int chunk,
+                                          efla_dtype_t dt, efla_path_t path)
 {
-    // the tensors are [H, T, d]: one "batch" of H rows of T tokens
-    efla_status_t s = check_shape(1, H, T, dk, dv, chunk, dt);
+    if (check_varlen(N, H, T, dk, dv, chunk, dt) != EFLA_OK) return 0;
+    path = resolve_varlen_path(path, dt, N, H, T, dk, dv, chunk);
+    if (path != EFLA_PATH_STAGED && path != EFLA_PATH_SEGMENTED) return 0;
+    return varlen_ws(N, H, T, dk, dv, chunk, dt, varlen_G(path, N, H, T, dk, dv, chunk)).total;
+}
+
+efla_status_t efla_forward_varlen_ex(const void *q, const void *k, const void *v,
+                                     const float *beta, const int *cu_seqlens, const float *S0,
+                                     void *o, float *S_L, int N, int H, int T, int dk, int dv,
+                                     int chunk, efla_dtype_t dt, efla_update_t update,
+                                     efla_path_t path, void *workspace, size_t workspace_bytes,
+                                     void *stream)
+{
+    efla_status_t s = check_varlen(N, H, T, dk, dv, chunk, dt);
     if (s != EFLA_OK) return s;
-    if (N < 0) return EFLA_ERR_INVALID_ARG;
     if (update != EFLA_EXACT && update != EFLA_EULER) return EFLA_ERR_INVALID_ARG;
-    if (!efla::fused_supported(dt == EFLA_BF16, dk, dv, chunk)) return EFLA_ERR_UNSUPPORTED;
+    if (path != EFLA_PATH_AUTO && path != EFLA_PATH_STAGED && path != EFLA_PATH_FUSED &&
+        path != EFLA_PATH_SEGMENTED)
+        return EFLA_ERR_INVALID_ARG;
+    path = resolve_varlen_path(path, dt, N, H, T, dk, dv, chunk);
+    const bool bf = dt == EFLA_BF16, euler = update == EFLA_EULER;
+    if (path == EFLA_PATH_FUSED && !efla::fused_supported(bf, dk, dv, chunk))
+        return EFLA_ERR_UNSUPPORTED;
     const long long NH = (long long)N * H;
-    if (NH * 8 > INT32_MAX) return EFLA_ERR_UNSUPPORTED;
     if (NH == 0) return EFLA_OK;
     if (!cu_seqlens || !S_L || !aligned16(S_L) || (S0 && !aligned16(S0)))
         return EFLA_ERR_INVALID_ARG;
@@ -347,9 +422,46 @@ efla_status_t efla_forward_varlen(const void *q, const void *k, const void *v, c
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(o))
             return EFLA_ERR_INVALID_ARG;
     }
-    return hip_status(efla::dispatch_fused_varlen(
-        dt == EFLA_BF16, dk, dv, chunk, q, k, v, beta, S0, o, S_L, (int)NH, T, cu_seqlens, H,
-        0, update == EFLA_EULER, static_cast<hipStream_t>(stream)));
+    const int G = varlen_G(path, N, H, T, dk, dv, chunk);
+    const VarlenWs ws = varlen_ws(N, H, T, dk, dv, chunk, dt, G);
+    if (path != EFLA_PATH_FUSED && T > 0) {
+        if (!workspace || workspace_bytes < ws.total) return EFLA_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return EFLA_ERR_INVALID_ARG;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (T == 0) return hip_status(efla::launch_copy_state(S0, S_L, NH * dk * dv, st));
+    if (path == EFLA_PATH_FUSED)
+        return hip_status(efla::dispatch_fused_varlen(bf, dk, dv, chunk, q, k, v, beta, S0, o, S_L,
+                                                      (int)NH, T, cu_seqlens, H, 0, euler, st));
+
+    char *base = static_cast<char *>(workspace);
+    float *alpha = reinterpret_cast<float *>(base + ws.alpha);
+    void *w = base + ws.w, *u = base + ws.u, *aqk = base + ws.aqk;
+    int *cuc = reinterpret_cast<int *>(base + ws.cuc);
+    hipError_t e = efla::dispatch_coef(bf, dk, k, beta, alpha, nullptr, (long)H * T, euler, st);
+    if (e == hipSuccess) e = efla::dispatch_packed_chunks(cu_seqlens, N, T, chunk, cuc, st);
+    if (e == hipSuccess)
+        e = efla::dispatch_ut(bf, dk, dv, chunk, q, k, v, alpha, w, u, aqk, H, T, st, cu_seqlens,
+                              cuc, N, H);
+    if (e == hipSuccess && G > 1)
+        e = efla::dispatch_scan_segmented(bf, dk, dv, chunk, q, k, w, u, aqk, S0, o, S_L, (int)NH,
+                                          T, G, 0, reinterpret_cast<float *>(base + ws.R),
+                                          reinterpret_cast<float *>(base + ws.P),
+                                          reinterpret_cast<float *>(base + ws.Sin), 0, st,
+                                          cu_seqlens, H);
+    else if (e == hipSuccess)
+        e = efla::dispatch_scan(bf, dk, dv, chunk, q, k, w, u, aqk, S0, o, S_L, (int)NH, T, 0, st,
+                                cu_seqlens, H);
+    return hip_status(e);
+}
+
+efla_status_t efla_forward_varlen(const void *q, const void *k, const void *v, const float *beta,
+                                  const int *cu_seqlens, const float *S0, void *o, float *S_L,
+                                  int N, int H, int T, int dk, int dv, int chunk, efla_dtype_t dt,
+                                  efla_update_t update, void *stream)
+{
+    return efla_forward_varlen_ex(q, k, v, beta, cu_seqlens, S0, o, S_L, N, H, T, dk, dv, chunk,
+                                  dt, update, EFLA_PATH_FUSED, nullptr, 0, stream);
 }
 
 efla_status_t efla_forward_ex(const void *q, const void *k, const void *v, const float *beta,
@@ -387,6 +499,27 @@ efla_status_t efla_decode_step_update(const void *q, const void *k, const void *
         return EFLA_ERR_INVALID_ARG;
     return hip_status(efla::dispatch_decode(dt == EFLA_BF16, dk, dv, q, k, v, beta, S, o, NH,
                                             update == EFLA_EULER, static_cast<hipStream_t>(stream)));
+}
+
+efla_status_t efla_decode_step_indexed(const void *q, const void *k, const void *v,
+                                       const float *beta, const int *slots, float *S_pool, void *o,
+                                       int *err, int N, int H, int P, int dk, int dv,
+                                       efla_dtype_t dt, efla_update_t update, void *stream)
+{
+    if (dt != EFLA_F32 && dt != EFLA_BF16) return EFLA_ERR_INVALID_ARG;
+    if (update != EFLA_EXACT && update != EFLA_EULER) return EFLA_ERR_INVALID_ARG;
+    if (N < 0 || H < 0 || P < 0 || dk <= 0 || dv <= 0) return EFLA_ERR_INVALID_ARG;
+    if (!dim_ok(dk) || !dim_ok(dv)) return EFLA_ERR_UNSUPPORTED;
+    const long long NH = (long long)N * H;
+    if (NH > INT32_MAX || (long long)P * H > INT32_MAX) return EFLA_ERR_UNSUPPORTED;
+    if (NH == 0) return EFLA_OK;
+    if (!q || !k || !v || !beta || !slots || !S_pool || !o) return EFLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) ||
+        !aligned16(S_pool) || !aligned16(o))
+        return EFLA_ERR_INVALID_ARG;
+    return hip_status(efla::dispatch_decode(dt == EFLA_BF16, dk, dv, q, k, v, beta, S_pool, o, NH,
+                                            update == EFLA_EULER, static_cast<hipStream_t>(stream),
+                                            slots, N, H, P, err));
 }
 
 efla_status_t efla_decode_step(const void *q, const void *k, const void *v, const float *beta,

@@ -312,6 +312,19 @@ __device__ __forceinline__ float update_alpha(int euler, float beta, float lambd
     return euler ? beta : efla_alpha(beta, lambda);
 }
 
+// Packed sequences: sequence n of a head spans tokens [packed_begin,
+// packed_end) of its L-token axis; offsets out of [0, L] (or a decreasing
+// pair) are clamped, so a bad offset shortens or empties a sequence but never
+// reaches past the tensor.
+__device__ __forceinline__ int packed_begin(const int *cu, int n, int L)
+{
+    return min(max(cu[n], 0), L);
+}
+__device__ __forceinline__ int packed_end(const int *cu, int n, int L)
+{
+    return min(max(cu[n + 1], packed_begin(cu, n, L)), L);
+}
+
 // Workgroup -> (sequence, tile) map that keeps the NTILE tiles of one
 // sequence on one XCD.  Consecutive workgroup ids are dispatched round-robin
 // over the 8 XCDs, so ids x, x+8, x+16, ... share an XCD and its L2.

@@ -18,27 +18,46 @@ namespace efla {
 hipError_t dispatch_coef(bool bf16, int dk, const void *k, const float *beta, float *alpha,
                          float *lambda, long n, bool euler, hipStream_t st);
 
+// slots != NULL: token n = nh / H updates pool entry slots[n] of P (see
+// decode_kernel for the rejection of repeated or out-of-range slots).
 hipError_t dispatch_decode(bool bf16, int dk, int dv, const void *q, const void *k, const void *v,
                            const float *beta, float *S, void *o, long NH, bool euler,
-                           hipStream_t st);
+                           hipStream_t st, const int *slots = nullptr, int N = 0, int H = 1,
+                           int P = 0, int *err = nullptr);
 
+// Packed sequences (the chunked kernels' varlen form).  Head h's L-token
+// axis holds N sequences back to back, sequence n at [cu[n], cu[n+1]) (cu:
+// device int32 [N+1], offsets clamped into [0, L]); chunks restart at each
+// sequence's first token.  dispatch_packed_chunks writes cu_chunks[n] (n = 0
+// .. N), the chunks of the sequences before n (capped at ceil(L/C) + N, the
+// most that sequences that do not overlap can have); the UT transform then
+// runs on H heads with one workgroup per chunk (A stored by token, [H, L,
+// C]), and the scans on BH = N * H sequences (bh = seq * H + h).
+hipError_t dispatch_packed_chunks(const int *cu, int N, int L, int chunk, int *cu_chunks,
+                                  hipStream_t st);
+
+// cu_chunks != NULL: the packed form above, with BH = H.
 hipError_t dispatch_ut(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                        const void *v, const float *alpha, void *w, void *u, void *aqk, int BH,
-                       int L, hipStream_t st);
+                       int L, hipStream_t st, const int *cu = nullptr,
+                       const int *cu_chunks = nullptr, int N = 0, int H = 1);
 
+// cu != NULL: the packed form above.
 hipError_t dispatch_scan(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                          const void *w, const void *u, const void *aqk, const float *S0, void *o,
-                         float *SL, int BH, int L, int nw, hipStream_t st);
+                         float *SL, int BH, int L, int nw, hipStream_t st,
+                         const int *cu = nullptr, int H = 1);
 
 // The same scan split over L into G segments of seg_chunks chunks (the last
 // may be shorter): segment maps (R [BH,G,dk,dv], P [BH,G,dk,dk]), their
 // composition into entry states (Sin [BH,G,dk,dv]) and the segments replayed
-// from them; o and S_L as from dispatch_scan.
+// from them; o and S_L as from dispatch_scan.  Packed (cu != NULL): every
+// sequence in G segments of ceil(its chunks / G) chunks (seg_chunks unused).
 hipError_t dispatch_scan_segmented(bool bf16, int dk, int dv, int chunk, const void *q,
                                    const void *k, const void *w, const void *u, const void *aqk,
                                    const float *S0, void *o, float *SL, int BH, int L, int G,
                                    int seg_chunks, float *R, float *P, float *Sin, int nw,
-                                   hipStream_t st);
+                                   hipStream_t st, const int *cu = nullptr, int H = 1);
 
 // Backward building blocks.  dispatch_scan_states runs the state scan for
 // the entry state of every chunk only (states [BH, nchunks, dk, dv]; no o,

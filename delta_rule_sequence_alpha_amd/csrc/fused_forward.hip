@@ -751,8 +751,7 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
     long tokb = (long)bh * L;
     if (cu_seqlens) {
         const int seq = bh / H, h = bh - seq * H;
-        const int t0 = min(max(cu_seqlens[seq], 0), L);
-        const int t1 = min(max(cu_seqlens[seq + 1], t0), L);
+        const int t0 = packed_begin(cu_seqlens, seq, L), t1 = packed_end(cu_seqlens, seq, L);
         tokb = (long)h * L + t0;
         L = t1 - t0;
         nchunks = (L + C - 1) / C;

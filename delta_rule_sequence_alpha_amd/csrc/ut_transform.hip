@@ -40,12 +40,23 @@ struct UtLayout {
     static constexpr size_t bytes = offA + sizeof(float) * C;
 };
 
+// Fixed length: workgroup bh * nchunks + c is chunk c of sequence bh, whose L
+// tokens start at bh * L; A is stored per chunk, [BH][nchunks][C][C].
+// Packed (cu_chunks != NULL): the tensors are [H, L, d] with N sequences per
+// head back to back, sequence n at tokens [cu[n], cu[n+1]) of its head, and
+// chunks restart at each sequence's first token.  cu_chunks[n] counts the
+// chunks of the sequences before n; workgroup h * nchunks + i is chunk
+// i - cu_chunks[n] of the sequence n holding the i-th chunk (workgroups past
+// the last chunk do nothing).  A is then stored by token, row r of a chunk at
+// token row tok0 + r of [H, L, C], and only the chunk's valid rows.
 template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                  const T *__restrict__ v,
                                                  const float *__restrict__ alpha,
                                                  T *__restrict__ w, T *__restrict__ u,
-                                                 T *__restrict__ aqk, int L, int nchunks)
+                                                 T *__restrict__ aqk, int L, int nchunks,
+                                                 const int *__restrict__ cu,
+                                                 const int *__restrict__ cu_chunks, int N)
 {
     using Lay = UtLayout<T, DK, DV, C>;
     constexpr int MC = C / 16;
@@ -60,9 +71,29 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
     float *sAl = reinterpret_cast<float *>(smem + Lay::offA);
 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
-    const int bh = blockIdx.x / nchunks, c = blockIdx.x - bh * nchunks;
-    const long tok0 = (long)bh * L + (long)c * C;
-    const int valid = min(C, L - c * C);
+    const bool packed = cu_chunks != nullptr;
+    long tok0;
+    int valid;
+    T *aq;
+    if (!packed) {
+        const int bh = blockIdx.x / nchunks, c = blockIdx.x - bh * nchunks;
+        tok0 = (long)bh * L + (long)c * C;
+        valid = min(C, L - c * C);
+        aq = aqk + ((long)bh * nchunks + c) * C * C;
+    } else {
+        const int h = blockIdx.x / nchunks, i = blockIdx.x - h * nchunks;
+        if (i >= cu_chunks[N]) return;          // past the last chunk (uniform)
+        int lo = 0, hi = N;                     // last n with cu_chunks[n] <= i
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (cu_chunks[mid] <= i) lo = mid; else hi = mid;
+        }
+        const int t0 = packed_begin(cu, lo, L), t1 = packed_end(cu, lo, L);
+        const int c = i - cu_chunks[lo];
+        tok0 = (long)h * L + t0 + (long)c * C;
+        valid = min(C, t1 - t0 - c * C);
+        aq = aqk + tok0 * C;
+    }
 
     // every load of the chunk in flight before the first LDS store
     TileRegs<T, C, DK, 256> tk, tq;
@@ -78,7 +109,6 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
 
     // Gram tiles G = K K^T (lower incl. diagonal, fp32 into LDS) and A = tril(Q K^T)
     // (written to global; tiles above the diagonal are written as zeros).
-    T *aq = aqk + ((long)bh * nchunks + c) * C * C;
     for (int t = wv; t < 2 * MC * MC; t += 4) {
         const bool gram = t < MC * MC;
         const int tt = gram ? t : t - MC * MC;
@@ -97,7 +127,8 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * it + 4 * g + r, col = 16 * jt + l16;
-                aq[row * C + col] = from_f32<T>(col <= row ? acc[r] : 0.f);
+                if (!packed || row < valid)
+                    aq[row * C + col] = from_f32<T>(col <= row ? acc[r] : 0.f);
             }
         }
     }
@@ -205,9 +236,50 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
     store_rows_t<T, C, DV, 256>(u + tok0 * DV, DV, sV, Lay::LDV, valid);
 }
 
+// cu_chunks[n] = chunks of packed sequences 0 .. n-1 (n = 0 .. N), capped
+// at cap.  One workgroup: each thread sums a run of sequences, the 256 run
+// totals are scanned in LDS, and each thread writes its run's offsets.
+__global__ __launch_bounds__(256) void packed_chunks_kernel(const int *__restrict__ cu, int N,
+                                                            int L, int C, int cap,
+                                                            int *__restrict__ cu_chunks)
+{
+    __shared__ long long part[256];
+    const int t = threadIdx.x, per = (N + 255) / 256;
+    const int n0 = min(N, t * per), n1 = min(N, n0 + per);
+    auto chunks = [&](int n) {
+        return (long long)(packed_end(cu, n, L) - packed_begin(cu, n, L) + C - 1) / C;
+    };
+    long long sum = 0;
+    for (int n = n0; n < n1; ++n) sum += chunks(n);
+    part[t] = sum;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const long long x = t >= off ? part[t - off] : 0;
+        __syncthreads();
+        part[t] += x;
+        __syncthreads();
+    }
+    long long run = t ? part[t - 1] : 0;
+    for (int n = n0; n < n1; ++n) {
+        cu_chunks[n] = (int)min(run, (long long)cap);
+        run += chunks(n);
+    }
+    if (t == 255) cu_chunks[N] = (int)min(part[255], (long long)cap);
+}
+
+hipError_t dispatch_packed_chunks(const int *cu, int N, int L, int chunk, int *cu_chunks,
+                                  hipStream_t st)
+{
+    const int cap = (L + chunk - 1) / chunk + N;
+    hipLaunchKernelGGL(packed_chunks_kernel, dim3(1), dim3(256), 0, st, cu, N, L, chunk, cap,
+                       cu_chunks);
+    return hipGetLastError();
+}
+
 template <typename T, int DK, int DV, int C>
 hipError_t launch_ut(const void *q, const void *k, const void *v, const float *alpha, void *w,
-                     void *u, void *aqk, int BH, int L, hipStream_t st)
+                     void *u, void *aqk, int BH, int L, const int *cu, const int *cu_chunks, int N,
+                     int H, hipStream_t st)
 {
     using Lay = UtLayout<T, DK, DV, C>;
     const int nchunks = (L + C - 1) / C;
@@ -216,21 +288,26 @@ hipError_t launch_ut(const void *q, const void *k, const void *v, const float *a
         reinterpret_cast<const void *>(&ut_kernel<T, DK, DV, C>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((ut_kernel<T, DK, DV, C>), dim3((unsigned)(BH * nchunks)), dim3(256),
-                       Lay::bytes, st, static_cast<const T *>(q), static_cast<const T *>(k),
+    // packed: per head, at most one chunk more per sequence than whole chunks
+    const int per = cu_chunks ? nchunks + N : nchunks;
+    const long grid = (long)(cu_chunks ? H : BH) * per;
+    hipLaunchKernelGGL((ut_kernel<T, DK, DV, C>), dim3((unsigned)grid), dim3(256), Lay::bytes, st,
+                       static_cast<const T *>(q), static_cast<const T *>(k),
                        static_cast<const T *>(v), alpha, static_cast<T *>(w),
-                       static_cast<T *>(u), static_cast<T *>(aqk), L, nchunks);
+                       static_cast<T *>(u), static_cast<T *>(aqk), L, per, cu, cu_chunks, N);
     return hipGetLastError();
 }
 
 hipError_t dispatch_ut(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                        const void *v, const float *alpha, void *w, void *u, void *aqk, int BH,
-                       int L, hipStream_t st)
+                       int L, hipStream_t st, const int *cu, const int *cu_chunks, int N, int H)
 {
 #define CASE(DKV, DVV, CC)                                                                      \
     if (dk == DKV && dv == DVV && chunk == CC)                                                  \
-        return bf16 ? launch_ut<__bf16, DKV, DVV, CC>(q, k, v, alpha, w, u, aqk, BH, L, st)     \
-                    : launch_ut<float, DKV, DVV, CC>(q, k, v, alpha, w, u, aqk, BH, L, st);
+        return bf16 ? launch_ut<__bf16, DKV, DVV, CC>(q, k, v, alpha, w, u, aqk, BH, L, cu,     \
+                                                      cu_chunks, N, H, st)                     \
+                    : launch_ut<float, DKV, DVV, CC>(q, k, v, alpha, w, u, aqk, BH, L, cu,      \
+                                                     cu_chunks, N, H, st);
     EFLA_SHAPE_CASES(CASE)
 #undef CASE
     return hipErrorInvalidValue;

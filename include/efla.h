@@ -149,13 +149,45 @@ efla_status_t efla_forward_ex(const void *q, const void *k, const void *v, const
  *   S0   [N,H,d_k,d_v] fp32 or NULL (zero state); S_L [N,H,d_k,d_v] fp32 out,
  *        may alias S0 exactly
  *   o    [H,T,d_v] dtype dt; tokens outside every sequence are left untouched
- * Needs no workspace.  Only the fused path exists for it: dt must be
- * EFLA_BF16, else EFLA_ERR_UNSUPPORTED.
+ * Runs the fused kernel and needs no workspace: dt must be EFLA_BF16, else
+ * EFLA_ERR_UNSUPPORTED (efla_forward_varlen_ex takes fp32 and the other
+ * paths).
  */
 efla_status_t efla_forward_varlen(const void *q, const void *k, const void *v, const float *beta,
                                   const int *cu_seqlens, const float *S0, void *o, float *S_L,
                                   int N, int H, int T, int d_k, int d_v, int chunk,
                                   efla_dtype_t dt, efla_update_t update, void *stream);
+
+/* Workspace bytes efla_forward_varlen_ex needs on `path` for these sizes (0
+ * for the fused path, or for invalid arguments).  It depends on N, H, T and
+ * the shape only, not on the offsets. */
+size_t efla_forward_varlen_workspace_size(int N, int H, int T, int d_k, int d_v, int chunk,
+                                          efla_dtype_t dt, efla_path_t path);
+
+/*
+ * efla_forward_varlen on any evaluation path, for fp32 and bf16 inputs
+ * (Methodology 3; each packed sequence is its own recurrence).  Arguments,
+ * layouts, clamping of offsets and results as for efla_forward_varlen, plus:
+ *   path  EFLA_PATH_FUSED (bf16 only, no workspace), EFLA_PATH_STAGED (alpha,
+ *         UT transform, state scan; one scan per (sequence, head)),
+ *         EFLA_PATH_SEGMENTED (the scan split into segment maps, their
+ *         composition and a replay: for few long sequences), or
+ *         EFLA_PATH_AUTO (fused where it exists, else segmented when
+ *         efla_forward_varlen_workspace_size plans more than one segment,
+ *         else staged)
+ *   workspace  device buffer of efla_forward_varlen_workspace_size(...)
+ *         bytes, 256-byte aligned, owned by the caller (NULL allowed when
+ *         that size is 0 or T = 0); too small: EFLA_ERR_WORKSPACE
+ * The staged and segmented paths compute the coefficients of every token of
+ * the T-token axes, inside a sequence or not; beta outside every sequence is
+ * read and its result discarded.
+ */
+efla_status_t efla_forward_varlen_ex(const void *q, const void *k, const void *v,
+                                     const float *beta, const int *cu_seqlens, const float *S0,
+                                     void *o, float *S_L, int N, int H, int T, int d_k, int d_v,
+                                     int chunk, efla_dtype_t dt, efla_update_t update,
+                                     efla_path_t path, void *workspace, size_t workspace_bytes,
+                                     void *stream);
 
 /* efla_forward_ex with an explicit update (EFLA_EXACT or EFLA_EULER). */
 efla_status_t efla_forward_update(const void *q, const void *k, const void *v, const float *beta,
@@ -215,6 +247,28 @@ efla_status_t efla_decode_step_update(const void *q, const void *k, const void *
                                       const float *beta, float *S, void *o, int N, int H,
                                       int d_k, int d_v, efla_dtype_t dt, efla_update_t update,
                                       void *stream);
+
+/*
+ * Single-token decode step for a ragged serving batch whose states live in a
+ * pool (Methodology 3, the recurrent form): token n of the batch belongs to
+ * the sequence whose state is pool entry slots[n], and updates it in place.
+ * No gather or scatter of states: each token's workgroup reads and writes its
+ * pool entry directly.
+ *   q, k [N,H,d_k], v [N,H,d_v] dtype dt; beta [N,H] fp32; o [N,H,d_v] dtype dt
+ *   slots   device int32 [N]; entries must be distinct and in [0, P)
+ *   S_pool  [P,H,d_k,d_v] fp32: entries slots[n] read and overwritten (each
+ *           read completely before any of it is written), all others untouched
+ *   err     device int32 or NULL.  A slot outside [0, P) or named by more than
+ *           one token is rejected on the device: the tokens naming it leave
+ *           the pool untouched, get o = NaN, and OR 2 (out of range) or 1
+ *           (repeated) into *err.  The library never clears *err.
+ * N = 0 is valid and launches nothing.  Other arguments as for
+ * efla_decode_step_update.
+ */
+efla_status_t efla_decode_step_indexed(const void *q, const void *k, const void *v,
+                                       const float *beta, const int *slots, float *S_pool,
+                                       void *o, int *err, int N, int H, int P, int d_k, int d_v,
+                                       efla_dtype_t dt, efla_update_t update, void *stream);
 
 /*
  * Stage 1 of the staged path: per-token coefficients (Methodology 2-3).

@@ -36,7 +36,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 21
+    assert len(declared) == 24
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], check=True,
                          capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (efla_[a-z_]+)\b", out))
@@ -171,6 +171,61 @@ def test_varlen_validation(lib):
     assert f(N=0, cu=None) == _lib.EFLA_OK     # nothing to do
 
 
+def _varlen_ex(**o):
+    a = dict(q=FAKE, cu=FAKE, S_L=FAKE, N=3, H=2, T=1000, dk=64, dv=64, chunk=64,
+             dt=_lib.EFLA_F32, update=0, path=_lib.EFLA_PATH_STAGED, ws=FAKE, ws_bytes=1 << 30)
+    a.update(o)
+    return _lib.efla_forward_varlen_ex(a["q"], FAKE, FAKE, FAKE, a["cu"], None, FAKE, a["S_L"],
+                                       a["N"], a["H"], a["T"], a["dk"], a["dv"], a["chunk"],
+                                       a["dt"], a["update"], a["path"], a["ws"], a["ws_bytes"],
+                                       None)
+
+
+def test_varlen_ex_validation(lib):
+    f = _varlen_ex
+    need = _lib.efla_forward_varlen_workspace_size(3, 2, 1000, 64, 64, 64, _lib.EFLA_F32,
+                                                   _lib.EFLA_PATH_STAGED)
+    assert f(ws=None) == _lib.EFLA_ERR_WORKSPACE
+    assert f(ws_bytes=need - 1) == _lib.EFLA_ERR_WORKSPACE
+    assert f(ws=MISALIGNED) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(path=9) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(path=_lib.EFLA_PATH_FUSED) == _lib.EFLA_ERR_UNSUPPORTED   # no fp32 fused kernel
+    assert f(N=-1) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(dk=24) == _lib.EFLA_ERR_UNSUPPORTED
+    assert f(update=5) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(cu=None) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(S_L=MISALIGNED) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(q=None) == _lib.EFLA_ERR_INVALID_ARG
+    assert f(N=0, cu=None, ws=None) == _lib.EFLA_OK    # nothing to do
+    # grid bound: H * (ceil(T / C) + N) workgroups must fit an int
+    assert f(N=1 << 24, H=64, T=1 << 20) == _lib.EFLA_ERR_UNSUPPORTED
+
+
+def test_varlen_workspace_size(lib):
+    # alpha fp32, W, U, A by token (dtype) over H*T tokens, chunk offsets int32 [N+1]
+    N, H, T, dk, dv, C = 5, 3, 1000, 64, 32, 32
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for dt, e in ((_lib.EFLA_F32, 4), (_lib.EFLA_BF16, 2)):
+        want = up(H * T * 4) + up(H * T * dk * e) + up(H * T * dv * e) + up(H * T * C * e) + \
+            up((N + 1) * 4)
+        assert _lib.efla_forward_varlen_workspace_size(N, H, T, dk, dv, C, dt,
+                                                       _lib.EFLA_PATH_STAGED) == want
+    assert _lib.efla_forward_varlen_workspace_size(N, H, T, dk, dv, C, _lib.EFLA_BF16,
+                                                   _lib.EFLA_PATH_FUSED) == 0
+    assert _lib.efla_forward_varlen_workspace_size(N, H, T, 24, dv, C, _lib.EFLA_F32,
+                                                   _lib.EFLA_PATH_STAGED) == 0
+    # few long sequences: AUTO takes the segmented scan (maps and entry states on top)
+    seg = _lib.efla_forward_varlen_workspace_size(1, 16, 65536, 128, 128, 64, _lib.EFLA_F32,
+                                                  _lib.EFLA_PATH_AUTO)
+    stg = _lib.efla_forward_varlen_workspace_size(1, 16, 65536, 128, 128, 64, _lib.EFLA_F32,
+                                                  _lib.EFLA_PATH_STAGED)
+    assert seg > stg > 0
+    assert _lib.efla_forward_varlen_workspace_size(64, 16, 65536, 128, 128, 64, _lib.EFLA_F32,
+                                                   _lib.EFLA_PATH_AUTO) == \
+        _lib.efla_forward_varlen_workspace_size(64, 16, 65536, 128, 128, 64, _lib.EFLA_F32,
+                                                _lib.EFLA_PATH_STAGED)
+
+
 def test_auto_path_choice(lib):
     # bf16: the fused kernel; fp32: segmented scan for few long sequences, else staged
     assert _lib.efla_forward_path(4, 16, 4096, 128, 128, 64, _lib.EFLA_BF16) == _lib.EFLA_PATH_FUSED
@@ -292,3 +347,25 @@ def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
     assert f(S_L=None) == _lib.EFLA_ERR_INVALID_ARG
     assert f(q=MISALIGNED) == _lib.EFLA_ERR_INVALID_ARG
     assert f(B=0) == _lib.EFLA_OK          # nothing to do, nothing launched
+
+
+def test_indexed_decode_validation(lib):
+    """efla_decode_step_indexed validates before any HIP call; N = 0 is a
+    no-op that needs no pointers."""
+    def d(**o):
+        a = dict(q=FAKE, slots=FAKE, S=FAKE, N=4, H=2, P=8, dk=128, dv=128, dt=_lib.EFLA_F32,
+                 update=_lib.EFLA_EXACT)
+        a.update(o)
+        return _lib.efla_decode_step_indexed(a["q"], FAKE, FAKE, FAKE, a["slots"], a["S"], FAKE,
+                                             None, a["N"], a["H"], a["P"], a["dk"], a["dv"],
+                                             a["dt"], a["update"], None)
+    assert d(dt=4) == _lib.EFLA_ERR_INVALID_ARG
+    assert d(update=2) == _lib.EFLA_ERR_INVALID_ARG
+    assert d(N=-1) == _lib.EFLA_ERR_INVALID_ARG
+    assert d(P=-1) == _lib.EFLA_ERR_INVALID_ARG
+    assert d(dk=48) == _lib.EFLA_ERR_UNSUPPORTED
+    assert d(slots=None) == _lib.EFLA_ERR_INVALID_ARG
+    assert d(S=None) == _lib.EFLA_ERR_INVALID_ARG
+    assert d(S=MISALIGNED) == _lib.EFLA_ERR_INVALID_ARG
+    assert d(q=None) == _lib.EFLA_ERR_INVALID_ARG
+    assert d(N=0, q=None, slots=None, S=None) == _lib.EFLA_OK
