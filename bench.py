@@ -14,7 +14,8 @@ timed in the same run and reported under "decode".
 
 The fused path is also timed with the Euler update (alpha = beta) and both
 kernel times are reported under "update_compare"; a packed (varlen) batch of
-the same token count is timed under "varlen", and the backward pass (dq, dk,
+the same token count is timed under "varlen" (and one of the long-stiff-f32
+token count, on the segmented path, under "varlen_f32"), and the backward pass (dq, dk,
 dv, dbeta, dS0 given dO and dS_L) of the same workload under "backward".
 "call_ms" has per-call median/p10/p90 times, warm and cold (1 GiB written
 between calls); "decode_512" the decode step with a state twice the Infinity
@@ -338,24 +339,30 @@ def bench_decode(args, dev, n_distinct=8, n_seq=None):
                     f"{nh * w.d_k * w.d_v * 4} B against the 256 MiB Infinity Cache"}
 
 
-def bench_varlen(args, dev, n_seq=16):
-    """Packed sequences: the lm1.3b-bf16 token count per head (4 x 4096)
-    split at random into n_seq sequences, 16 heads, fused kernel."""
-    w = wl.FORWARD_WORKLOADS["lm1.3b-bf16"]
+def bench_varlen(args, dev, name="lm1.3b-bf16", n_seq=16):
+    """Packed sequences: the workload's token count per head (B x L) split at
+    random into n_seq sequences, its H heads, on the path AUTO takes (the
+    fused kernel for bf16, the segmented scan for the long fp32 case)."""
+    w = wl.FORWARD_WORKLOADS[name]
     lengths = wl.varlen_lengths(n_seq, w.B * w.L, seed=0)
     q, k, v, beta, cu, S0 = wl.varlen_inputs(w, lengths, seed=0)
-    qd, kd, vd, bd, cud, s0d = (x.to(dev) for x in (q, k, v, beta, cu, S0))
+    qd, kd, vd, bd, cud = (x.to(dev) for x in (q, k, v, beta, cu))
+    s0d = None if S0 is None else S0.to(dev)
     H, T = w.H, q.shape[1]
-    o = torch.empty((H, T, w.d_v), dtype=torch.bfloat16, device=dev)
+    dt = _lib.EFLA_BF16 if w.dtype == "bf16" else _lib.EFLA_F32
+    o = torch.empty((H, T, w.d_v), dtype=q.dtype, device=dev)
     S_L = torch.empty((n_seq, H, w.d_k, w.d_v), dtype=torch.float32, device=dev)
+    need = _lib.efla_forward_varlen_workspace_size(n_seq, H, T, w.d_k, w.d_v, w.chunk, dt,
+                                                   _lib.EFLA_PATH_AUTO)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
-    p = lambda x: x.data_ptr()  # noqa: E731
+    p = lambda x: None if x is None else x.data_ptr()  # noqa: E731
 
     def step():
-        st = _lib.efla_forward_varlen(p(qd), p(kd), p(vd), p(bd), p(cud), p(s0d), p(o), p(S_L),
-                                      n_seq, H, T, w.d_k, w.d_v, w.chunk, _lib.EFLA_BF16,
-                                      _lib.EFLA_EXACT, sp)
+        st = _lib.efla_forward_varlen_ex(p(qd), p(kd), p(vd), p(bd), p(cud), p(s0d), p(o),
+                                         p(S_L), n_seq, H, T, w.d_k, w.d_v, w.chunk, dt,
+                                         _lib.EFLA_EXACT, _lib.EFLA_PATH_AUTO, p(ws), need, sp)
         if st:
             raise RuntimeError(f"varlen forward failed: {_lib.status_string(st)}")
     for _ in range(args.warmup):
@@ -369,9 +376,12 @@ def bench_varlen(args, dev, n_seq=16):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    return {"sequences": n_seq, "heads": H, "tokens_per_head": T, "longest": max(lengths),
-            "shortest": min(lengths), "kernel_ms": ms, "tokens_per_s": T / (ms * 1e-3),
-            "note": "lm1.3b-bf16 recipe; random lengths; the longest sequence sets the time"}
+    path = "fused" if need == 0 else ("segmented" if need > _lib.efla_forward_varlen_workspace_size(
+        n_seq, H, T, w.d_k, w.d_v, w.chunk, dt, _lib.EFLA_PATH_STAGED) else "staged")
+    return {"workload": name, "dtype": w.dtype, "path": path, "sequences": n_seq, "heads": H,
+            "tokens_per_head": T, "longest": max(lengths), "shortest": min(lengths),
+            "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+            "note": f"{name} recipe; random lengths; region of {args.steps} calls"}
 
 
 def bench_config(args, name, dev):
@@ -689,6 +699,8 @@ def main():
     if not args.no_compare and w.dtype == "bf16":
         print("[bench] varlen", file=sys.stderr, flush=True)
         res["varlen"] = bench_varlen(args, dev)
+        print("[bench] varlen long-stiff-f32", file=sys.stderr, flush=True)
+        res["varlen_f32"] = bench_varlen(args, dev, "long-stiff-f32", n_seq=4)
     if not args.no_backward:
         print(f"[bench] backward {w.name}", file=sys.stderr, flush=True)
         res["backward"] = bench_backward(args, w, dev)
