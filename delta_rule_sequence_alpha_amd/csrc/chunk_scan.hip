@@ -330,10 +330,18 @@ hipError_t launch_scan_auto(const void *q, const void *k, const void *w, const v
 {
     // Every wave owns 16 columns whatever NW is (the number of waves, hence of
     // busy SIMDs, is BH * DV / 16); wider tiles share each chunk's loads
-    // between more waves.
+    // between more waves.  By default 4 waves; the fp32 segment passes at
+    // d_k = d_v = 128 take 8 (128 columns): their 153 KB workgroup is alone
+    // on its CU either way, and 8 waves give each SIMD two to alternate
+    // between while one waits on LDS.
     constexpr int DMIN = DK < DV ? DK : DV;
     const int wmax = sg.mode == SCAN_SUMMARY ? DMIN : DV;
-    if (nw <= 0) nw = 4;
+    constexpr bool WIDE = !is_bf16<T> && DMIN >= 128;
+    if (nw <= 0) nw = (WIDE && sg.mode != SCAN_WHOLE) ? 8 : 4;
+    if constexpr (WIDE) {
+        if (nw >= 8 && wmax >= 128)
+            return launch_scan<T, DK, DV, C, 8>(q, k, w, u, aqk, S0, o, SL, BH, L, sg, st);
+    }
     if (nw >= 4 && wmax >= 64)
         return launch_scan<T, DK, DV, C, 4>(q, k, w, u, aqk, S0, o, SL, BH, L, sg, st);
     if (nw >= 2 && wmax >= 32)

@@ -35,16 +35,18 @@ efla_status_t check_shape(int B, int H, int L, int dk, int dv, int chunk, efla_d
 
 // Segments of the segmented scan: enough (sequence, segment, column tile)
 // workgroups in its summary pass for ~2 per CU of the 256, with at least 4
-// chunks per segment.  G = 1 means splitting does not pay.
+// chunks per segment.  G = 1 means splitting does not pay.  wide: the
+// forward's fp32 passes at d_k = d_v = 128, whose workgroups take 128
+// columns (8 waves) instead of 64.
 struct SegPlan {
     int G, seg_chunks;
 };
 
-SegPlan seg_plan(long long BH, int L, int dk, int dv, int chunk)
+SegPlan seg_plan(long long BH, int L, int dk, int dv, int chunk, bool wide = false)
 {
     const int nchunks = (L + chunk - 1) / chunk;
     const int dmin = dk < dv ? dk : dv;
-    const int tv = dmin >= 64 ? 64 : dmin;               // columns per summary workgroup
+    const int tv = wide && dmin >= 128 ? 128 : dmin >= 64 ? 64 : dmin;   // columns per summary workgroup
     const long long tiles = BH * ((dk + dv) / tv);
     long long G = (512 + tiles - 1) / (tiles > 0 ? tiles : 1);
     if (G > nchunks / 4) G = nchunks / 4;
@@ -134,13 +136,13 @@ efla_path_t resolve_varlen_path(efla_path_t p, efla_dtype_t dt, int N, int H, in
 {
     if (p != EFLA_PATH_AUTO) return p;
     if (efla::fused_supported(dt == EFLA_BF16, dk, dv, chunk)) return EFLA_PATH_FUSED;
-    return seg_plan((long long)N * H, T, dk, dv, chunk).G > 1 ? EFLA_PATH_SEGMENTED
+    return seg_plan((long long)N * H, T, dk, dv, chunk, dt == EFLA_F32).G > 1 ? EFLA_PATH_SEGMENTED
                                                                : EFLA_PATH_STAGED;
 }
 
-int varlen_G(efla_path_t p, int N, int H, int T, int dk, int dv, int chunk)
+int varlen_G(efla_path_t p, int N, int H, int T, int dk, int dv, int chunk, bool wide)
 {
-    return p == EFLA_PATH_SEGMENTED ? seg_plan((long long)N * H, T, dk, dv, chunk).G : 1;
+    return p == EFLA_PATH_SEGMENTED ? seg_plan((long long)N * H, T, dk, dv, chunk, wide).G : 1;
 }
 
 // Backward workspace: the forward's coefficient and UT-transform outputs,
@@ -182,13 +184,13 @@ efla_path_t resolve_path(efla_path_t p, efla_dtype_t dt, int B, int H, int L, in
 {
     if (p != EFLA_PATH_AUTO) return p;
     if (efla::fused_supported(dt == EFLA_BF16, dk, dv, chunk)) return EFLA_PATH_FUSED;
-    return seg_plan((long long)B * H, L, dk, dv, chunk).G > 1 ? EFLA_PATH_SEGMENTED
+    return seg_plan((long long)B * H, L, dk, dv, chunk, dt == EFLA_F32).G > 1 ? EFLA_PATH_SEGMENTED
                                                                : EFLA_PATH_STAGED;
 }
 
-int plan_G(efla_path_t p, int B, int H, int L, int dk, int dv, int chunk)
+int plan_G(efla_path_t p, int B, int H, int L, int dk, int dv, int chunk, bool wide)
 {
-    return p == EFLA_PATH_SEGMENTED ? seg_plan((long long)B * H, L, dk, dv, chunk).G : 1;
+    return p == EFLA_PATH_SEGMENTED ? seg_plan((long long)B * H, L, dk, dv, chunk, wide).G : 1;
 }
 
 // Launch configuration: every field 0 (or no struct) is the built-in choice.
@@ -211,7 +213,7 @@ bool config_ok(const efla_launch_config_t *c)
     if (!c) return true;
     auto w124 = [](int n) { return n == 0 || n == 1 || n == 2 || n == 4; };
     return (c->fused_scan_waves == 0 || c->fused_scan_waves == 1 || c->fused_scan_waves == 2) &&
-           w124(c->scan_waves) && w124(c->bwd_scan_waves);
+           (w124(c->scan_waves) || c->scan_waves == 8) && w124(c->bwd_scan_waves);
 }
 
 efla_status_t hip_status(hipError_t e) { return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP; }
@@ -244,7 +246,7 @@ size_t efla_forward_workspace_size_ex(int B, int H, int L, int dk, int dv, int c
     if (check_shape(B, H, L, dk, dv, chunk, dt) != EFLA_OK) return 0;
     path = resolve_path(path, dt, B, H, L, dk, dv, chunk);
     if (path == EFLA_PATH_STAGED || path == EFLA_PATH_SEGMENTED)
-        return staged_ws(B, H, L, dk, dv, chunk, dt, plan_G(path, B, H, L, dk, dv, chunk)).total;
+        return staged_ws(B, H, L, dk, dv, chunk, dt, plan_G(path, B, H, L, dk, dv, chunk, dt == EFLA_F32)).total;
     return 0;
 }
 
@@ -319,7 +321,8 @@ efla_status_t forward_impl(const void *q, const void *k, const void *v, const fl
                                                o, S_L, (int)BH, L, cfg.fused_scan_waves, euler,
                                                st));
     }
-    const SegPlan plan = path == EFLA_PATH_SEGMENTED ? seg_plan(BH, L, dk, dv, chunk) : SegPlan{1, 0};
+    const SegPlan plan = path == EFLA_PATH_SEGMENTED ? seg_plan(BH, L, dk, dv, chunk, dt == EFLA_F32)
+                                                     : SegPlan{1, 0};
     const StagedWs ws = staged_ws(B, H, L, dk, dv, chunk, dt, plan.G);
     if (noalloc && L > 0) {
         if (ws.total > kScratchBytes) return EFLA_ERR_WORKSPACE;
@@ -393,7 +396,7 @@ size_t efla_forward_varlen_workspace_size(int N, int H, int T, int dk, int dv, i
     if (check_varlen(N, H, T, dk, dv, chunk, dt) != EFLA_OK) return 0;
     path = resolve_varlen_path(path, dt, N, H, T, dk, dv, chunk);
     if (path != EFLA_PATH_STAGED && path != EFLA_PATH_SEGMENTED) return 0;
-    return varlen_ws(N, H, T, dk, dv, chunk, dt, varlen_G(path, N, H, T, dk, dv, chunk)).total;
+    return varlen_ws(N, H, T, dk, dv, chunk, dt, varlen_G(path, N, H, T, dk, dv, chunk, dt == EFLA_F32)).total;
 }
 
 efla_status_t efla_forward_varlen_ex(const void *q, const void *k, const void *v,
@@ -422,7 +425,7 @@ efla_status_t efla_forward_varlen_ex(const void *q, const void *k, const void *v
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(o))
             return EFLA_ERR_INVALID_ARG;
     }
-    const int G = varlen_G(path, N, H, T, dk, dv, chunk);
+    const int G = varlen_G(path, N, H, T, dk, dv, chunk, dt == EFLA_F32);
     const VarlenWs ws = varlen_ws(N, H, T, dk, dv, chunk, dt, G);
     if (path != EFLA_PATH_FUSED && T > 0) {
         if (!workspace || workspace_bytes < ws.total) return EFLA_ERR_WORKSPACE;

@@ -120,7 +120,8 @@ __device__ __forceinline__ void mm_acc_b(f32x4 (&out)[MT], const T *A, int lda,
                 out[mt] = mma(cat(a1, a2), b, out[mt]);
             }
         }
-    } else {
+    } else if constexpr (!A_STRIDED) {
+        // each lane's four k values of a tile are one 16-byte read
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
@@ -132,6 +133,32 @@ __device__ __forceinline__ void mm_acc_b(f32x4 (&out)[MT], const T *A, int lda,
                     out[mt] = mma(a, Bacc[kt][r], out[mt]);
                 }
             }
+        }
+    } else {
+        // A^T-shaped operand: a lane's values for one k sit in one row, 16
+        // floats apart across the MT output tiles, one scalar read each.  The
+        // reads of step s + 1 (one k for every tile) are issued before the
+        // MFMAs of step s, so their latency is covered by MFMAs; left to
+        // itself, a compiler short of registers waits on every read.
+        constexpr int NSTEP = 4 * KT;
+        float a[2][MT];
+        auto load = [&](int st, float (&d)[MT]) {
+            const int kt = st >> 2, r = st & 3;
+            const float *row = A + (16 * kt + 4 * g + r) * lda + l16;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                if (!(LOWER && kt > mt)) d[mt] = row[16 * mt];
+        };
+        load(0, a[0]);
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+            if (st + 1 < NSTEP) load(st + 1, a[(st + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            const int kt = st >> 2, r = st & 3;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                if (!(LOWER && kt > mt)) out[mt] = mma(a[st & 1][mt], Bacc[kt][r], out[mt]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }

@@ -85,8 +85,10 @@ typedef enum { EFLA_EXACT = 0, EFLA_EULER = 1 } efla_update_t;
  * of every column, and so the result, does not depend on them.
  *   fused_scan_waves  fused forward: 1 or 2 scan waves per workgroup
  *                     (16- or 32-column state tiles)
- *   scan_waves        staged and segmented state scans: 1, 2 or 4 waves per
- *                     workgroup
+ *   scan_waves        staged and segmented state scans: 1, 2, 4 or 8 waves per
+ *                     workgroup (8 only for fp32 inputs at d_k = d_v = 128, the
+ *                     built-in choice of the segmented passes there; elsewhere
+ *                     it acts as 4)
  *   bwd_scan_waves    the backward's two state scans: 1, 2 or 4
  * Any other value returns EFLA_ERR_INVALID_ARG.  The library reads no
  * environment variable and keeps no setting between calls. */

@@ -285,6 +285,7 @@ def test_backward_rejects_bad_arguments(lib, over, status):
     (dict(fused_scan_waves=3), _lib.EFLA_ERR_INVALID_ARG),
     (dict(scan_waves=3), _lib.EFLA_ERR_INVALID_ARG),
     (dict(bwd_scan_waves=8), _lib.EFLA_ERR_INVALID_ARG),
+    (dict(scan_waves=8), _lib.EFLA_ERR_WORKSPACE),   # valid: fails on the workspace after
     (dict(scan_waves=-1), _lib.EFLA_ERR_INVALID_ARG),
     # valid values pass the check and validation goes on to the next error
     (dict(fused_scan_waves=1, scan_waves=4, bwd_scan_waves=2), _lib.EFLA_ERR_WORKSPACE),

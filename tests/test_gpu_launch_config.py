@@ -3,7 +3,8 @@
 efla_forward_config and efla_backward_config take an explicit
 efla_launch_config_t: fused_scan_waves (scan waves of the fused kernel: 2
 runs 32-column tiles, 1 runs 16-column tiles), scan_waves (waves per
-workgroup of the staged and segmented state scans) and bwd_scan_waves (the
+workgroup of the staged and segmented state scans; 8 exists for fp32 at
+d_k = d_v = 128 and acts as 4 elsewhere) and bwd_scan_waves (the
 backward's two scans).  Each value selects other compiled instances than the
 defaults, so each is checked against the fp64 oracle here: a ragged bf16
 forward on the fused and staged paths, an fp32 staged forward, a segmented
@@ -20,7 +21,7 @@ from tests._parity import TOL, dev, note, rel_err
 pytestmark = pytest.mark.gpu
 
 OVERRIDES = [("fused_scan_waves", 1), ("fused_scan_waves", 2),
-             ("scan_waves", 1), ("scan_waves", 2), ("scan_waves", 4),
+             ("scan_waves", 1), ("scan_waves", 2), ("scan_waves", 4), ("scan_waves", 8),
              ("bwd_scan_waves", 1), ("bwd_scan_waves", 2), ("bwd_scan_waves", 4)]
 
 
