@@ -166,8 +166,9 @@ __device__ __forceinline__ void mm_acc_b(f32x4 (&out)[MT], const T *A, int lda,
 // acc (+)= A[i0:i0+16, 0:K] * B[0:K, j0:j0+16] with both operands in LDS.
 // A element (i,k): A[i*lda+k] or, A_STRIDED, A[k*lda+i].
 // B element (k,j): B[j*ldb+k] or, B_STRIDED, B[k*ldb+j].
-// K must be a multiple of 16.  KLIM > 0 caps the k range (block-triangular
-// operands): only k < KLIM is multiplied.
+// K must be a multiple of 16.  klim caps the k range (block-triangular
+// operands): only k < klim is multiplied; it is a multiple of 16 (bf16: 32,
+// or the whole of K).
 template <typename T, int K, bool A_STRIDED, bool B_STRIDED>
 __device__ __forceinline__ f32x4 mm_lds(f32x4 acc, const T *A, int lda, int i0, const T *B,
                                         int ldb, int j0, int klim = K)
@@ -192,12 +193,33 @@ __device__ __forceinline__ f32x4 mm_lds(f32x4 acc, const T *A, int lda, int i0, 
             acc = mma(a, b, acc);
         }
     } else {
+        // k in 16-wide blocks (klim a multiple of 16).  In block kb the MFMA
+        // of step r contracts k = 16 kb + 4 g + r over the lane groups g: a
+        // permutation of the block's k, the same for both operands, which
+        // puts a lane's four values of a row-major operand side by side.
+        // The reads of block kb + 2 are issued before the MFMAs of block kb,
+        // so LDS latency is covered by MFMAs instead of stalling each one.
+        constexpr int NB = K / 16;
+        const int nb = (klim < K ? klim : K) / 16;
+        float a[3][4], b[3][4];
+        auto load = [&](int kb, float (&av)[4], float (&bv)[4]) {
+            const int k0 = 16 * kb + 4 * g;
 #pragma unroll
-        for (int s = 0; s < K / 4; ++s) {
-            if (4 * s >= klim) break;
-            const float a = one<A_STRIDED>(A, lda, i0 + l16, 4 * s + g);
-            const float b = one<B_STRIDED>(B, ldb, j0 + l16, 4 * s + g);
-            acc = mma(a, b, acc);
+            for (int r = 0; r < 4; ++r) {
+                av[r] = one<A_STRIDED>(A, lda, i0 + l16, k0 + r);
+                bv[r] = one<B_STRIDED>(B, ldb, j0 + l16, k0 + r);
+            }
+        };
+        if (nb > 0) load(0, a[0], b[0]);
+        if (nb > 1) load(1, a[1], b[1]);
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+            if (kb >= nb) break;
+            if (kb + 2 < nb) load(kb + 2, a[(kb + 2) % 3], b[(kb + 2) % 3]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc = mma(a[kb % 3][r], b[kb % 3][r], acc);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     return acc;
