@@ -40,15 +40,65 @@ struct UtLayout {
     static constexpr size_t bytes = offA + sizeof(float) * C;
 };
 
-// Fixed length: workgroup bh * nchunks + c is chunk c of sequence bh, whose L
-// tokens start at bh * L; A is stored per chunk, [BH][nchunks][C][C].
-// Packed (cu_chunks != NULL): the tensors are [H, L, d] with N sequences per
-// head back to back, sequence n at tokens [cu[n], cu[n+1]) of its head, and
-// chunks restart at each sequence's first token.  cu_chunks[n] counts the
-// chunks of the sequences before n; workgroup h * nchunks + i is chunk
-// i - cu_chunks[n] of the sequence n holding the i-th chunk (workgroups past
-// the last chunk do nothing).  A is then stored by token, row r of a chunk at
-// token row tok0 + r of [H, L, C], and only the chunk's valid rows.
+// Chunk `id` of the launch.  Fixed length: id = bh * nchunks + c is chunk c
+// of sequence bh, whose L tokens start at bh * L; A is stored per chunk,
+// [BH][nchunks][C][C].  Packed (cu_chunks != NULL): the tensors are [H, L, d]
+// with N sequences per head back to back, sequence n at tokens [cu[n],
+// cu[n+1]) of its head, and chunks restart at each sequence's first token.
+// cu_chunks[n] counts the chunks of the sequences before n; id = h * nchunks
+// + i is chunk i - cu_chunks[n] of the sequence n holding the i-th chunk, and
+// ids past the last chunk of a head are not chunks (false).  A is then stored
+// by token, row r of a chunk at token row tok0 + r of [H, L, C], and only the
+// chunk's valid rows.
+template <typename T, int C>
+struct UtChunk {
+    long tok0;
+    int valid;
+    T *aq;
+};
+
+template <typename T, int C>
+__device__ __forceinline__ bool ut_locate(int id, int L, int nchunks, const int *cu,
+                                          const int *cu_chunks, int N, T *aqk, UtChunk<T, C> &x)
+{
+    if (!cu_chunks) {
+        const int bh = id / nchunks, c = id - bh * nchunks;
+        x.tok0 = (long)bh * L + (long)c * C;
+        x.valid = min(C, L - c * C);
+        x.aq = aqk + ((long)bh * nchunks + c) * C * C;
+        return true;
+    }
+    const int h = id / nchunks, i = id - h * nchunks;
+    if (i >= cu_chunks[N]) return false;
+    int lo = 0, hi = N;   // last n with cu_chunks[n] <= i
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cu_chunks[mid] <= i) lo = mid; else hi = mid;
+    }
+    const int t0 = packed_begin(cu, lo, L), t1 = packed_end(cu, lo, L);
+    const int c = i - cu_chunks[lo];
+    x.tok0 = (long)h * L + t0 + (long)c * C;
+    x.valid = min(C, t1 - t0 - c * C);
+    x.aq = aqk + x.tok0 * C;
+    return true;
+}
+
+// The first chunk id >= id (stepping by `stride`) that is a chunk, or an id
+// >= total.
+template <typename T, int C>
+__device__ __forceinline__ long ut_next(long id, int stride, int total, int L, int nchunks,
+                                       const int *cu, const int *cu_chunks, int N, T *aqk,
+                                       UtChunk<T, C> &x)
+{
+    while (id < total && !ut_locate<T, C>((int)id, L, nchunks, cu, cu_chunks, N, aqk, x))
+        id += stride;
+    return id;
+}
+
+// Persistent: workgroup b takes chunks b, b + gridDim.x, ... of the `total`
+// ids, and the next chunk's K and Q tiles (and, once this chunk has staged
+// its V tile, the next V tile) are loaded into registers while this chunk is
+// computed, so the loads' latency is not exposed once per chunk.
 template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                  const T *__restrict__ v,
@@ -56,7 +106,8 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
                                                  T *__restrict__ w, T *__restrict__ u,
                                                  T *__restrict__ aqk, int L, int nchunks,
                                                  const int *__restrict__ cu,
-                                                 const int *__restrict__ cu_chunks, int N)
+                                                 const int *__restrict__ cu_chunks, int N,
+                                                 int total)
 {
     using Lay = UtLayout<T, DK, DV, C>;
     constexpr int MC = C / 16;
@@ -72,168 +123,168 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
     const bool packed = cu_chunks != nullptr;
-    long tok0;
-    int valid;
-    T *aq;
-    if (!packed) {
-        const int bh = blockIdx.x / nchunks, c = blockIdx.x - bh * nchunks;
-        tok0 = (long)bh * L + (long)c * C;
-        valid = min(C, L - c * C);
-        aq = aqk + ((long)bh * nchunks + c) * C * C;
-    } else {
-        const int h = blockIdx.x / nchunks, i = blockIdx.x - h * nchunks;
-        if (i >= cu_chunks[N]) return;          // past the last chunk (uniform)
-        int lo = 0, hi = N;                     // last n with cu_chunks[n] <= i
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (cu_chunks[mid] <= i) lo = mid; else hi = mid;
-        }
-        const int t0 = packed_begin(cu, lo, L), t1 = packed_end(cu, lo, L);
-        const int c = i - cu_chunks[lo];
-        tok0 = (long)h * L + t0 + (long)c * C;
-        valid = min(C, t1 - t0 - c * C);
-        aq = aqk + tok0 * C;
-    }
+    const int stride = gridDim.x;
 
-    // every load of the chunk in flight before the first LDS store
+    UtChunk<T, C> cur, nxt;
+    long id = ut_next<T, C>(blockIdx.x, stride, total, L, nchunks, cu, cu_chunks, N, aqk, cur);
     TileRegs<T, C, DK, 256> tk, tq;
     TileRegs<T, C, DV, 256> tv;
-    tk.load(k + tok0 * DK, DK, valid);
-    tq.load(q + tok0 * DK, DK, valid);
-    tv.load(v + tok0 * DV, DV, valid);
-    tk.store(sK, Lay::LDK, valid);
-    tq.store(sQ, Lay::LDK, valid);
-    for (int i = threadIdx.x; i < C * Lay::LDG; i += 256) sT[i] = 0.f;
-    for (int i = threadIdx.x; i < C; i += 256) sAl[i] = (i < valid) ? alpha[tok0 + i] : 0.f;
-    __syncthreads();
-
-    // Gram tiles G = K K^T (lower incl. diagonal, fp32 into LDS) and A = tril(Q K^T)
-    // (written to global; tiles above the diagonal are written as zeros).
-    for (int t = wv; t < 2 * MC * MC; t += 4) {
-        const bool gram = t < MC * MC;
-        const int tt = gram ? t : t - MC * MC;
-        const int it = tt / MC, jt = tt - it * MC;
-        if (gram) {
-            if (jt > it) continue;
-            const f32x4 acc = mm_lds<T, DK, false, false>(zero4(), sK, Lay::LDK, 16 * it, sK,
-                                                          Lay::LDK, 16 * jt);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sG[(16 * it + 4 * g + r) * Lay::LDG + 16 * jt + l16] = acc[r];
-        } else {
-            f32x4 acc = zero4();
-            if (jt <= it)
-                acc = mm_lds<T, DK, false, false>(zero4(), sQ, Lay::LDK, 16 * it, sK, Lay::LDK,
-                                                  16 * jt);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * it + 4 * g + r, col = 16 * jt + l16;
-                if (!packed || row < valid)
-                    aq[row * C + col] = from_f32<T>(col <= row ? acc[r] : 0.f);
-            }
-        }
+    if (id < total) {
+        tk.load(k + cur.tok0 * DK, DK, cur.valid);
+        tq.load(q + cur.tok0 * DK, DK, cur.valid);
+        tv.load(v + cur.tok0 * DV, DV, cur.valid);
     }
-    __syncthreads();
+    while (id < total) {   // uniform over the workgroup
+        const long tok0 = cur.tok0;
+        const int valid = cur.valid;
+        T *const aq = cur.aq;
+        const long nid =
+            ut_next<T, C>(id + stride, stride, total, L, nchunks, cu, cu_chunks, N, aqk, nxt);
 
-    // Diagonal 16x16 blocks of T by forward substitution: wave 0, lane group b
-    // handles block b, lane l16 owns column l16 of it.
-    if (wv == 0 && g < MC) {
-        const int b0 = 16 * g, j = l16;
-        float t[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float acc = (i == j) ? 1.f : 0.f;
-            const float *grow = sG + (b0 + i) * Lay::LDG + b0;
-#pragma unroll
-            for (int m = 0; m < i; ++m) acc = fmaf(-grow[m], t[m], acc);
-            t[i] = sAl[b0 + i] * acc;
+        tk.store(sK, Lay::LDK, valid);
+        tq.store(sQ, Lay::LDK, valid);
+        for (int i = threadIdx.x; i < C * Lay::LDG; i += 256) sT[i] = 0.f;
+        for (int i = threadIdx.x; i < C; i += 256) sAl[i] = (i < valid) ? alpha[tok0 + i] : 0.f;
+        __syncthreads();
+        if (nid < total) {   // the next chunk's K and Q fly while this one is computed
+            tk.load(k + nxt.tok0 * DK, DK, nxt.valid);
+            tq.load(q + nxt.tok0 * DK, DK, nxt.valid);
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sT[(b0 + i) * Lay::LDG + b0 + j] = t[i];
-    }
-    __syncthreads();
 
-    // Blocks below the diagonal, one block distance at a time (fp32 MFMA).
-    for (int dist = 1; dist < MC; ++dist) {
-        if (wv < MC - dist) {
-            const int bi = dist + wv, bj = wv;
-            f32x4 p = zero4();
-            for (int m = bj; m < bi; ++m) {
+        // Gram tiles G = K K^T (lower incl. diagonal, fp32 into LDS) and A = tril(Q K^T)
+        // (written to global; tiles above the diagonal are written as zeros).
+        for (int t = wv; t < 2 * MC * MC; t += 4) {
+            const bool gram = t < MC * MC;
+            const int tt = gram ? t : t - MC * MC;
+            const int it = tt / MC, jt = tt - it * MC;
+            if (gram) {
+                if (jt > it) continue;
+                const f32x4 acc = mm_lds<T, DK, false, false>(zero4(), sK, Lay::LDK, 16 * it, sK,
+                                                              Lay::LDK, 16 * jt);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const float a = sG[(16 * bi + l16) * Lay::LDG + 16 * m + 4 * s + g];
-                    const float b = sT[(16 * m + 4 * s + g) * Lay::LDG + 16 * bj + l16];
-                    p = mma(a, b, p);
+                for (int r = 0; r < 4; ++r)
+                    sG[(16 * it + 4 * g + r) * Lay::LDG + 16 * jt + l16] = acc[r];
+            } else {
+                f32x4 acc = zero4();
+                if (jt <= it)
+                    acc = mm_lds<T, DK, false, false>(zero4(), sQ, Lay::LDK, 16 * it, sK, Lay::LDK,
+                                                      16 * jt);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * it + 4 * g + r, col = 16 * jt + l16;
+                    if (!packed || row < valid)
+                        aq[row * C + col] = from_f32<T>(col <= row ? acc[r] : 0.f);
                 }
             }
-            f32x4 x = zero4();
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float a = sT[(16 * bi + l16) * Lay::LDG + 16 * bi + 4 * g + r];
-                x = mma(a, p[r], x);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sT[(16 * bi + 4 * g + r) * Lay::LDG + 16 * bj + l16] = -x[r];
         }
         __syncthreads();
-    }
 
-    const T *sTop = nullptr;   // T as the MFMA A operand
-    int ldTop = 0;
-    if constexpr (BF) {
-        for (int i = threadIdx.x; i < C * C; i += 256) {
-            const int r = i / C, cc = i - r * C;
-            sTb[r * Lay::LDTB + cc] = from_f32<T>(sT[r * Lay::LDG + cc]);
+        // Diagonal 16x16 blocks of T by forward substitution: wave 0, lane group b
+        // handles block b, lane l16 owns column l16 of it.
+        if (wv == 0 && g < MC) {
+            const int b0 = 16 * g, j = l16;
+            float t[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float acc = (i == j) ? 1.f : 0.f;
+                const float *grow = sG + (b0 + i) * Lay::LDG + b0;
+#pragma unroll
+                for (int m = 0; m < i; ++m) acc = fmaf(-grow[m], t[m], acc);
+                t[i] = sAl[b0 + i] * acc;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sT[(b0 + i) * Lay::LDG + b0 + j] = t[i];
         }
-        sTop = sTb;
-        ldTop = Lay::LDTB;
-    } else {
-        sTop = reinterpret_cast<const T *>(sT);
-        ldTop = Lay::LDG;
-    }
-    tv.store(sV, Lay::LDV, valid);   // A = tril(Q K^T) is done with Q
-    __syncthreads();
+        __syncthreads();
 
-    // W = T K and U = T V (T lower triangular: k range of row tile mt is
-    // [0, 16mt+16)).  Each product is staged in LDS over the operand it no
-    // longer needs (W over K, U over V) and written with 16-byte stores.
-    constexpr int NTK = DK / 16, NTV = DV / 16;
-    constexpr int WPW = (MC * NTK + 3) / 4, UPW = (MC * NTV + 3) / 4;   // tiles per wave
-    f32x4 acc[WPW > UPW ? WPW : UPW];
+        // Blocks below the diagonal, one block distance at a time (fp32 MFMA).
+        for (int dist = 1; dist < MC; ++dist) {
+            if (wv < MC - dist) {
+                const int bi = dist + wv, bj = wv;
+                f32x4 p = zero4();
+                for (int m = bj; m < bi; ++m) {
 #pragma unroll
-    for (int j = 0; j < WPW; ++j) {
-        const int t = wv + 4 * j, mt = t / NTK, nt = t - mt * NTK;
-        if (t < MC * NTK)
-            acc[j] = mm_lds<T, C, false, true>(zero4(), sTop, ldTop, 16 * mt, sK, Lay::LDK, 16 * nt,
-                                               16 * mt + 16);
+                    for (int s = 0; s < 4; ++s) {
+                        const float a = sG[(16 * bi + l16) * Lay::LDG + 16 * m + 4 * s + g];
+                        const float b = sT[(16 * m + 4 * s + g) * Lay::LDG + 16 * bj + l16];
+                        p = mma(a, b, p);
+                    }
+                }
+                f32x4 x = zero4();
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float a = sT[(16 * bi + l16) * Lay::LDG + 16 * bi + 4 * g + r];
+                    x = mma(a, p[r], x);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sT[(16 * bi + 4 * g + r) * Lay::LDG + 16 * bj + l16] = -x[r];
+            }
+            __syncthreads();
+        }
+
+        const T *sTop = nullptr;   // T as the MFMA A operand
+        int ldTop = 0;
+        if constexpr (BF) {
+            for (int i = threadIdx.x; i < C * C; i += 256) {
+                const int r = i / C, cc = i - r * C;
+                sTb[r * Lay::LDTB + cc] = from_f32<T>(sT[r * Lay::LDG + cc]);
+            }
+            sTop = sTb;
+            ldTop = Lay::LDTB;
+        } else {
+            sTop = reinterpret_cast<const T *>(sT);
+            ldTop = Lay::LDG;
+        }
+        tv.store(sV, Lay::LDV, valid);   // A = tril(Q K^T) is done with Q
+        __syncthreads();
+        if (nid < total) tv.load(v + nxt.tok0 * DV, DV, nxt.valid);
+
+        // W = T K and U = T V (T lower triangular: k range of row tile mt is
+        // [0, 16mt+16)).  Each product is staged in LDS over the operand it no
+        // longer needs (W over K, U over V) and written with 16-byte stores.
+        constexpr int NTK = DK / 16, NTV = DV / 16;
+        constexpr int WPW = (MC * NTK + 3) / 4, UPW = (MC * NTV + 3) / 4;   // tiles per wave
+        f32x4 acc[WPW > UPW ? WPW : UPW];
+#pragma unroll
+        for (int j = 0; j < WPW; ++j) {
+            const int t = wv + 4 * j, mt = t / NTK, nt = t - mt * NTK;
+            if (t < MC * NTK)
+                acc[j] = mm_lds<T, C, false, true>(zero4(), sTop, ldTop, 16 * mt, sK, Lay::LDK,
+                                                   16 * nt, 16 * mt + 16);
+        }
+        __syncthreads();   // every read of K is done
+#pragma unroll
+        for (int j = 0; j < WPW; ++j) {
+            const int t = wv + 4 * j, mt = t / NTK, nt = t - mt * NTK;
+            if (t < MC * NTK)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sK[(16 * mt + 4 * g + r) * Lay::LDK + 16 * nt + l16] = from_f32<T>(acc[j][r]);
+        }
+#pragma unroll
+        for (int j = 0; j < UPW; ++j) {
+            const int t = wv + 4 * j, mt = t / NTV, nt = t - mt * NTV;
+            if (t < MC * NTV)
+                acc[j] = mm_lds<T, C, false, true>(zero4(), sTop, ldTop, 16 * mt, sV, Lay::LDV,
+                                                   16 * nt, 16 * mt + 16);
+        }
+        __syncthreads();   // every read of V is done; W is staged
+#pragma unroll
+        for (int j = 0; j < UPW; ++j) {
+            const int t = wv + 4 * j, mt = t / NTV, nt = t - mt * NTV;
+            if (t < MC * NTV)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sV[(16 * mt + 4 * g + r) * Lay::LDV + 16 * nt + l16] = from_f32<T>(acc[j][r]);
+        }
+        __syncthreads();
+        store_rows_t<T, C, DK, 256>(w + tok0 * DK, DK, sK, Lay::LDK, valid);
+        store_rows_t<T, C, DV, 256>(u + tok0 * DV, DV, sV, Lay::LDV, valid);
+        __syncthreads();   // the staged W and U are read before the next chunk's tiles land
+        id = nid;
+        cur = nxt;
     }
-    __syncthreads();   // every read of K is done
-#pragma unroll
-    for (int j = 0; j < WPW; ++j) {
-        const int t = wv + 4 * j, mt = t / NTK, nt = t - mt * NTK;
-        if (t < MC * NTK)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sK[(16 * mt + 4 * g + r) * Lay::LDK + 16 * nt + l16] = from_f32<T>(acc[j][r]);
-    }
-#pragma unroll
-    for (int j = 0; j < UPW; ++j) {
-        const int t = wv + 4 * j, mt = t / NTV, nt = t - mt * NTV;
-        if (t < MC * NTV)
-            acc[j] = mm_lds<T, C, false, true>(zero4(), sTop, ldTop, 16 * mt, sV, Lay::LDV, 16 * nt,
-                                               16 * mt + 16);
-    }
-    __syncthreads();   // every read of V is done; W is staged
-#pragma unroll
-    for (int j = 0; j < UPW; ++j) {
-        const int t = wv + 4 * j, mt = t / NTV, nt = t - mt * NTV;
-        if (t < MC * NTV)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sV[(16 * mt + 4 * g + r) * Lay::LDV + 16 * nt + l16] = from_f32<T>(acc[j][r]);
-    }
-    __syncthreads();
-    store_rows_t<T, C, DK, 256>(w + tok0 * DK, DK, sK, Lay::LDK, valid);
-    store_rows_t<T, C, DV, 256>(u + tok0 * DV, DV, sV, Lay::LDV, valid);
 }
 
 // cu_chunks[n] = chunks of packed sequences 0 .. n-1 (n = 0 .. N), capped
@@ -276,6 +327,8 @@ hipError_t dispatch_packed_chunks(const int *cu, int N, int L, int chunk, int *c
     return hipGetLastError();
 }
 
+constexpr size_t kLdsPerCu = 160 * 1024;   // gfx950
+
 template <typename T, int DK, int DV, int C>
 hipError_t launch_ut(const void *q, const void *k, const void *v, const float *alpha, void *w,
                      void *u, void *aqk, int BH, int L, const int *cu, const int *cu_chunks, int N,
@@ -290,11 +343,16 @@ hipError_t launch_ut(const void *q, const void *k, const void *v, const float *a
     if (attr != hipSuccess) return attr;
     // packed: per head, at most one chunk more per sequence than whole chunks
     const int per = cu_chunks ? nchunks + N : nchunks;
-    const long grid = (long)(cu_chunks ? H : BH) * per;
+    const long total = (long)(cu_chunks ? H : BH) * per;
+    // as many workgroups as the CUs hold at once (LDS-bound), each looping
+    // over chunks
+    const long resident = 256L * (long)(kLdsPerCu / Lay::bytes > 0 ? kLdsPerCu / Lay::bytes : 1);
+    const long grid = total < resident ? total : resident;
     hipLaunchKernelGGL((ut_kernel<T, DK, DV, C>), dim3((unsigned)grid), dim3(256), Lay::bytes, st,
                        static_cast<const T *>(q), static_cast<const T *>(k),
                        static_cast<const T *>(v), alpha, static_cast<T *>(w),
-                       static_cast<T *>(u), static_cast<T *>(aqk), L, per, cu, cu_chunks, N);
+                       static_cast<T *>(u), static_cast<T *>(aqk), L, per, cu, cu_chunks, N,
+                       (int)total);
     return hipGetLastError();
 }
 
