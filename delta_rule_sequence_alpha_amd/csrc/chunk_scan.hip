@@ -150,7 +150,7 @@ __device__ __forceinline__ void scan_body(
         const int vn = min(C, Ls - cn * C);
         rW.load(w + t0 * DK, DK, vn);
         rK.load(k + t0 * DK, DK, vn);
-        rU.load(u + t0 * DV + utile * TV, DV, vn);
+        if (!ptile) rU.load(u + t0 * DV + utile * TV, DV, vn);   // (a map's matrix: U = 0)
         if (want_o) {
             rQ.load(q + t0 * DK, DK, vn);
             rA.load(a_at(cn), C, sg.cu ? vn : C);
@@ -167,7 +167,7 @@ __device__ __forceinline__ void scan_body(
         if constexpr (PREFETCH) {
             rW.store(sW, Lay::LDK, valid);
             rK.store(sK, Lay::LDK, valid);
-            rU.store(sU, Lay::LDU, valid);
+            if (!ptile) rU.store(sU, Lay::LDU, valid);
             if (want_o) {
                 rQ.store(sQ, Lay::LDK, valid);
                 rA.store(sA, Lay::LDC, sg.cu ? valid : C);
@@ -178,8 +178,10 @@ __device__ __forceinline__ void scan_body(
             t.store(sW, Lay::LDK, valid);
             t.load(k + tok0 * DK, DK, valid);
             t.store(sK, Lay::LDK, valid);
-            rU.load(u + tok0 * DV + utile * TV, DV, valid);
-            rU.store(sU, Lay::LDU, valid);
+            if (!ptile) {
+                rU.load(u + tok0 * DV + utile * TV, DV, valid);
+                rU.store(sU, Lay::LDU, valid);
+            }
             if (want_o) {
                 t.load(q + tok0 * DK, DK, valid);
                 t.store(sQ, Lay::LDK, valid);
@@ -259,44 +261,94 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
 }
 
 // S_in(0) = S0 (or 0); S_in(g) = P_{g-1} S_in(g-1) + R_{g-1} for g = 1 .. G-1.
-// One workgroup per (sequence, 16 columns); S_in(g-1)'s columns stay in LDS,
-// P rows are read from L2; fp32 FMAs (G - 1 small products per sequence).
+// One workgroup of four waves per (sequence, 16 columns).  The 16 columns of
+// S_in(g-1) stay in LDS; P_{g-1} is staged in LDS from registers, into which
+// P_g (and the R tiles of step g) are loaded meanwhile; each wave forms
+// DK / 64 row tiles of the product on fp32 MFMA.
+template <int DK, int DV>
+struct CombineLayout {
+    static constexpr int LDP = DK + 4;    // P rows: 16-byte aligned, conflict-free row reads
+    static constexpr int LDS_ = 17;       // the state's 16 columns, read by rows 4 apart
+    static constexpr size_t offP = 0;
+    static constexpr size_t offS = offP + sizeof(float) * DK * LDP;
+    static constexpr size_t bytes = offS + sizeof(float) * DK * LDS_;
+};
+
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void seg_combine_kernel(const float *__restrict__ S0,
                                                           const float *__restrict__ P,
                                                           const float *__restrict__ R,
                                                           float *__restrict__ Sin, int G)
 {
-    constexpr int NCB = DV / 16, PER = DK * 16 / 256;   // outputs per thread
-    __shared__ float cur[DK][17];
+    using Lay = CombineLayout<DK, DV>;
+    constexpr int NCB = DV / 16, MK = DK / 16, TPW = (MK + 3) / 4;   // row tiles per wave
+    extern __shared__ __align__(16) char smem[];
+    float *sP = reinterpret_cast<float *>(smem + Lay::offP);
+    float *sS = reinterpret_cast<float *>(smem + Lay::offS);
     const int bh = blockIdx.x / NCB, cb = blockIdx.x - bh * NCB;
-    const int t = threadIdx.x, j = t & 15, i0 = t >> 4;   // rows i0, i0 + 16, ...
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6, l16 = lane & 15, g = lane >> 4;
     for (int e = t; e < DK * 16; e += 256) {
         const int i = e >> 4, jj = e & 15;
         const float x = S0 ? S0[((long)bh * DK + i) * DV + cb * 16 + jj] : 0.f;
-        cur[i][jj] = x;
+        sS[i * Lay::LDS_ + jj] = x;
         Sin[(((long)bh * G) * DK + i) * DV + cb * 16 + jj] = x;
     }
-    __syncthreads();
+    TileRegs<float, DK, DK, 256> rP;
+    f32x4 rR[TPW];
+    auto load_step = [&](int gs) {   // P_{gs-1} and this wave's tiles of R_{gs-1}
+        rP.load(P + ((long)bh * G + gs - 1) * DK * DK, DK, DK);
+        const float *Rg = R + ((long)bh * G + gs - 1) * DK * DV + cb * 16 + l16;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int mt = wv + 4 * u;
+            if (mt < MK)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) rR[u][r] = Rg[(long)(16 * mt + 4 * g + r) * DV];
+        }
+    };
+    if (G > 1) load_step(1);
     for (int gs = 1; gs < G; ++gs) {
-        const float *Pg = P + ((long)bh * G + gs - 1) * DK * DK;
-        const float *Rg = R + ((long)bh * G + gs - 1) * DK * DV;
-        float acc[PER];
+        rP.store(sP, Lay::LDP, DK);
+        f32x4 acc[TPW];
 #pragma unroll
-        for (int p = 0; p < PER; ++p) acc[p] = Rg[(long)(i0 + 16 * p) * DV + cb * 16 + j];
-        for (int m = 0; m < DK; ++m) {
-            const float s = cur[m][j];
+        for (int u = 0; u < TPW; ++u) acc[u] = rR[u];
+        __syncthreads();   // P_{gs-1} and S_in(gs-1) in LDS
+        if (gs + 1 < G) load_step(gs + 1);
 #pragma unroll
-            for (int p = 0; p < PER; ++p) acc[p] = fmaf(Pg[(long)(i0 + 16 * p) * DK + m], s, acc[p]);
+        for (int u = 0; u < TPW; ++u) {
+            const int mt = wv + 4 * u;
+            if (mt < MK)
+                acc[u] = mm_lds<float, DK, false, true>(acc[u], sP, Lay::LDP, 16 * mt, sS,
+                                                        Lay::LDS_, 0);
         }
-        __syncthreads();
+        __syncthreads();   // every read of S_in(gs-1) and P_{gs-1} is done
+        float *dst = Sin + (((long)bh * G + gs) * DK) * DV + cb * 16 + l16;
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            cur[i0 + 16 * p][j] = acc[p];
-            Sin[(((long)bh * G + gs) * DK + i0 + 16 * p) * DV + cb * 16 + j] = acc[p];
+        for (int u = 0; u < TPW; ++u) {
+            const int mt = wv + 4 * u;
+            if (mt < MK)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * mt + 4 * g + r;
+                    sS[row * Lay::LDS_ + l16] = acc[u][r];
+                    dst[(long)row * DV] = acc[u][r];
+                }
         }
-        __syncthreads();
     }
+}
+
+template <int DK, int DV>
+hipError_t launch_combine(const float *S0, const float *P, const float *R, float *Sin, int BH,
+                          int G, hipStream_t st)
+{
+    using Lay = CombineLayout<DK, DV>;
+    const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&seg_combine_kernel<DK, DV>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((seg_combine_kernel<DK, DV>), dim3((unsigned)(BH * (DV / 16))), dim3(256),
+                       Lay::bytes, st, S0, P, R, Sin, G);
+    return hipGetLastError();
 }
 
 template <typename T, int DK, int DV, int C, int NW>
@@ -359,9 +411,7 @@ hipError_t launch_scan_segmented(const void *q, const void *k, const void *w, co
     SegArgs sum{SCAN_SUMMARY, G, seg_chunks, R, P, nullptr, nullptr, cu, H};
     hipError_t e = launch_scan_auto<T, DK, DV, C>(q, k, w, u, aqk, nullptr, o, SL, BH, L, nw, sum, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((seg_combine_kernel<DK, DV>), dim3((unsigned)(BH * (DV / 16))), dim3(256), 0,
-                       st, S0, P, R, Sin, G);
-    e = hipGetLastError();
+    e = launch_combine<DK, DV>(S0, P, R, Sin, BH, G, st);
     if (e != hipSuccess) return e;
     SegArgs rep{SCAN_REPLAY, G, seg_chunks, nullptr, nullptr, Sin, nullptr, cu, H};
     return launch_scan_auto<T, DK, DV, C>(q, k, w, u, aqk, nullptr, o, SL, BH, L, nw, rep, st);
@@ -631,9 +681,7 @@ hipError_t launch_rscan(const void *q, const void *k, const void *w, const void 
     hipError_t e = launch_rscan_mode<T, DK, DV, C>(q, k, w, aqk, dout, nullptr, dSout, dE, nullptr,
                                                    BH, L, nw, sum, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((seg_combine_kernel<DK, DV>), dim3((unsigned)(BH * (DV / 16))), dim3(256), 0,
-                       st, dSL, P, R, Sin, G);
-    e = hipGetLastError();
+    e = launch_combine<DK, DV>(dSL, P, R, Sin, BH, G, st);
     if (e != hipSuccess) return e;
     const SegArgs rep{SCAN_REPLAY, G, seg_chunks, nullptr, nullptr, Sin, nullptr};
     return launch_rscan_mode<T, DK, DV, C>(q, k, w, aqk, dout, nullptr, dSout, dE, dS0, BH, L, nw,
@@ -673,9 +721,7 @@ hipError_t dispatch_scan_states(bool bf16, int dk, int dv, int chunk, const void
                                 : launch_scan_auto<float, DKV, DVV, CC>(q, k, w, u, aqk, nullptr, \
                                       nullptr, nullptr, BH, L, nw, sum, st);                    \
             if (e != hipSuccess) return e;                                                      \
-            hipLaunchKernelGGL((seg_combine_kernel<DKV, DVV>), dim3((unsigned)(BH * (DVV / 16))), \
-                               dim3(256), 0, st, S0, P, R, Sin, G);                             \
-            e = hipGetLastError();                                                              \
+            e = launch_combine<DKV, DVV>(S0, P, R, Sin, BH, G, st);                             \
             if (e != hipSuccess) return e;                                                      \
             return bf16 ? launch_scan_auto<__bf16, DKV, DVV, CC>(q, k, w, u, aqk, nullptr,      \
                                                                  nullptr, nullptr, BH, L, nw, rep, st) \

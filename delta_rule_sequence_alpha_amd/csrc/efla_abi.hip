@@ -59,8 +59,11 @@ SegPlan seg_plan(long long BH, int L, int dk, int dv, int chunk, bool wide = fal
     return p;
 }
 
+// Staged / segmented forward workspace: W, U and A (input dtype; the UT
+// transform forms alpha itself), and for G > 1 segments the segment maps and
+// entry states (fp32).
 struct StagedWs {
-    size_t alpha, w, u, aqk, R, P, Sin, total;
+    size_t w, u, aqk, R, P, Sin, total;
 };
 
 StagedWs staged_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t dt, int G)
@@ -69,8 +72,7 @@ StagedWs staged_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t 
     const size_t nch = (size_t)B * H * ((L + chunk - 1) / chunk);
     const size_t segs = (size_t)B * H * G;
     StagedWs s;
-    s.alpha = 0;
-    s.w = s.alpha + align_up(n * sizeof(float));
+    s.w = 0;
     s.u = s.w + align_up(n * dk * esize(dt));
     s.aqk = s.u + align_up(n * dv * esize(dt));
     s.R = s.aqk + align_up(nch * chunk * chunk * esize(dt));
@@ -84,12 +86,12 @@ StagedWs staged_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtype_t 
     return s;
 }
 
-// Packed-sequence (varlen) staged workspace: alpha, W, U over every token of
-// the H heads, A by token ([H, T, chunk]), the chunk offsets of the sequences
+// Packed-sequence (varlen) staged workspace: W, U over every token of the H
+// heads, A by token ([H, T, chunk]), the chunk offsets of the sequences
 // (int32 [N+1]) and, for G > 1 segments per sequence, the segment maps and
 // entry states (fp32).
 struct VarlenWs {
-    size_t alpha, w, u, aqk, cuc, R, P, Sin, total;
+    size_t w, u, aqk, cuc, R, P, Sin, total;
 };
 
 VarlenWs varlen_ws(int N, int H, int T, int dk, int dv, int chunk, efla_dtype_t dt, int G)
@@ -97,8 +99,7 @@ VarlenWs varlen_ws(int N, int H, int T, int dk, int dv, int chunk, efla_dtype_t 
     const size_t n = (size_t)H * T;
     const size_t segs = (size_t)N * H * G;
     VarlenWs s;
-    s.alpha = 0;
-    s.w = s.alpha + align_up(n * sizeof(float));
+    s.w = 0;
     s.u = s.w + align_up(n * dk * esize(dt));
     s.aqk = s.u + align_up(n * dv * esize(dt));
     s.cuc = s.aqk + align_up(n * chunk * esize(dt));
@@ -339,11 +340,9 @@ efla_status_t forward_impl(const void *q, const void *k, const void *v, const fl
 
     const bool bf = dt == EFLA_BF16;
     char *base = static_cast<char *>(workspace);
-    float *alpha = reinterpret_cast<float *>(base + ws.alpha);
     void *w = base + ws.w, *u = base + ws.u, *aqk = base + ws.aqk;
-    hipError_t e = efla::dispatch_coef(bf, dk, k, beta, alpha, nullptr, BH * L, euler, st);
-    if (e == hipSuccess)
-        e = efla::dispatch_ut(bf, dk, dv, chunk, q, k, v, alpha, w, u, aqk, (int)BH, L, st);
+    hipError_t e = efla::dispatch_ut(bf, dk, dv, chunk, q, k, v, nullptr, w, u, aqk, (int)BH, L,
+                                     st, nullptr, nullptr, 0, 1, beta, euler);
     if (e == hipSuccess && plan.G > 1)
         e = efla::dispatch_scan_segmented(bf, dk, dv, chunk, q, k, w, u, aqk, S0, o, S_L, (int)BH, L,
                                           plan.G, plan.seg_chunks,
@@ -438,14 +437,12 @@ efla_status_t efla_forward_varlen_ex(const void *q, const void *k, const void *v
                                                       (int)NH, T, cu_seqlens, H, 0, euler, st));
 
     char *base = static_cast<char *>(workspace);
-    float *alpha = reinterpret_cast<float *>(base + ws.alpha);
     void *w = base + ws.w, *u = base + ws.u, *aqk = base + ws.aqk;
     int *cuc = reinterpret_cast<int *>(base + ws.cuc);
-    hipError_t e = efla::dispatch_coef(bf, dk, k, beta, alpha, nullptr, (long)H * T, euler, st);
-    if (e == hipSuccess) e = efla::dispatch_packed_chunks(cu_seqlens, N, T, chunk, cuc, st);
+    hipError_t e = efla::dispatch_packed_chunks(cu_seqlens, N, T, chunk, cuc, st);
     if (e == hipSuccess)
-        e = efla::dispatch_ut(bf, dk, dv, chunk, q, k, v, alpha, w, u, aqk, H, T, st, cu_seqlens,
-                              cuc, N, H);
+        e = efla::dispatch_ut(bf, dk, dv, chunk, q, k, v, nullptr, w, u, aqk, H, T, st, cu_seqlens,
+                              cuc, N, H, beta, euler);
     if (e == hipSuccess && G > 1)
         e = efla::dispatch_scan_segmented(bf, dk, dv, chunk, q, k, w, u, aqk, S0, o, S_L, (int)NH,
                                           T, G, 0, reinterpret_cast<float *>(base + ws.R),

@@ -99,6 +99,8 @@ __device__ __forceinline__ long ut_next(long id, int stride, int total, int L, i
 // ids, and the next chunk's K and Q tiles (and, once this chunk has staged
 // its V tile, the next V tile) are loaded into registers while this chunk is
 // computed, so the loads' latency is not exposed once per chunk.
+// alpha == NULL: the coefficients are formed here from beta (and euler), with
+// lambda_r = k_r . k_r the diagonal of the chunk's Gram matrix.
 template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                  const T *__restrict__ v,
@@ -107,7 +109,8 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
                                                  T *__restrict__ aqk, int L, int nchunks,
                                                  const int *__restrict__ cu,
                                                  const int *__restrict__ cu_chunks, int N,
-                                                 int total)
+                                                 int total, const float *__restrict__ beta,
+                                                 int euler)
 {
     using Lay = UtLayout<T, DK, DV, C>;
     constexpr int MC = C / 16;
@@ -144,7 +147,12 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
         tk.store(sK, Lay::LDK, valid);
         tq.store(sQ, Lay::LDK, valid);
         for (int i = threadIdx.x; i < C * Lay::LDG; i += 256) sT[i] = 0.f;
-        for (int i = threadIdx.x; i < C; i += 256) sAl[i] = (i < valid) ? alpha[tok0 + i] : 0.f;
+        float be = 0.f;   // alpha from beta: token `lane` of the chunk, wave 0
+        if (alpha) {
+            for (int i = threadIdx.x; i < C; i += 256) sAl[i] = (i < valid) ? alpha[tok0 + i] : 0.f;
+        } else if (wv == 0 && lane < valid) {
+            be = beta[tok0 + lane];
+        }
         __syncthreads();
         if (nid < total) {   // the next chunk's K and Q fly while this one is computed
             tk.load(k + nxt.tok0 * DK, DK, nxt.valid);
@@ -180,7 +188,10 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
         __syncthreads();
 
         // Diagonal 16x16 blocks of T by forward substitution: wave 0, lane group b
-        // handles block b, lane l16 owns column l16 of it.
+        // handles block b, lane l16 owns column l16 of it (after writing, from
+        // beta, the alpha of token `lane`; LDS keeps one wave's accesses in order).
+        if (!alpha && wv == 0 && lane < C)
+            sAl[lane] = lane < valid ? update_alpha(euler, be, sG[lane * Lay::LDG + lane]) : 0.f;
         if (wv == 0 && g < MC) {
             const int b0 = 16 * g, j = l16;
             float t[16];
@@ -332,7 +343,7 @@ constexpr size_t kLdsPerCu = 160 * 1024;   // gfx950
 template <typename T, int DK, int DV, int C>
 hipError_t launch_ut(const void *q, const void *k, const void *v, const float *alpha, void *w,
                      void *u, void *aqk, int BH, int L, const int *cu, const int *cu_chunks, int N,
-                     int H, hipStream_t st)
+                     int H, const float *beta, bool euler, hipStream_t st)
 {
     using Lay = UtLayout<T, DK, DV, C>;
     const int nchunks = (L + C - 1) / C;
@@ -352,20 +363,21 @@ hipError_t launch_ut(const void *q, const void *k, const void *v, const float *a
                        static_cast<const T *>(q), static_cast<const T *>(k),
                        static_cast<const T *>(v), alpha, static_cast<T *>(w),
                        static_cast<T *>(u), static_cast<T *>(aqk), L, per, cu, cu_chunks, N,
-                       (int)total);
+                       (int)total, beta, (int)euler);
     return hipGetLastError();
 }
 
 hipError_t dispatch_ut(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                        const void *v, const float *alpha, void *w, void *u, void *aqk, int BH,
-                       int L, hipStream_t st, const int *cu, const int *cu_chunks, int N, int H)
+                       int L, hipStream_t st, const int *cu, const int *cu_chunks, int N, int H,
+                       const float *beta, bool euler)
 {
 #define CASE(DKV, DVV, CC)                                                                      \
     if (dk == DKV && dv == DVV && chunk == CC)                                                  \
         return bf16 ? launch_ut<__bf16, DKV, DVV, CC>(q, k, v, alpha, w, u, aqk, BH, L, cu,     \
-                                                      cu_chunks, N, H, st)                     \
+                                                      cu_chunks, N, H, beta, euler, st)        \
                     : launch_ut<float, DKV, DVV, CC>(q, k, v, alpha, w, u, aqk, BH, L, cu,      \
-                                                     cu_chunks, N, H, st);
+                                                     cu_chunks, N, H, beta, euler, st);
     EFLA_SHAPE_CASES(CASE)
 #undef CASE
     return hipErrorInvalidValue;

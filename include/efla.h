@@ -58,7 +58,9 @@ typedef enum {
  * enough to split, else STAGED. */
 typedef enum {
     EFLA_PATH_AUTO = 0,    /* the fastest path available for the shape         */
-    EFLA_PATH_STAGED = 1,  /* coefficient -> UT-transform -> state-scan kernels */
+    EFLA_PATH_STAGED = 1,  /* UT transform (with the coefficients) -> state
+                              scan: the stages below, with W, U and A in the
+                              workspace                                      */
     EFLA_PATH_FUSED = 2,   /* one kernel; no intermediate HBM traffic           */
     EFLA_PATH_SEGMENTED = 3 /* staged, with the state scan split over L into
                                segments: each segment's affine map S -> P S + R
@@ -170,8 +172,8 @@ size_t efla_forward_varlen_workspace_size(int N, int H, int T, int d_k, int d_v,
  * efla_forward_varlen on any evaluation path, for fp32 and bf16 inputs
  * (Methodology 3; each packed sequence is its own recurrence).  Arguments,
  * layouts, clamping of offsets and results as for efla_forward_varlen, plus:
- *   path  EFLA_PATH_FUSED (bf16 only, no workspace), EFLA_PATH_STAGED (alpha,
- *         UT transform, state scan; one scan per (sequence, head)),
+ *   path  EFLA_PATH_FUSED (bf16 only, no workspace), EFLA_PATH_STAGED (UT
+ *         transform, state scan; one scan per (sequence, head)),
  *         EFLA_PATH_SEGMENTED (the scan split into segment maps, their
  *         composition and a replay: for few long sequences), or
  *         EFLA_PATH_AUTO (fused where it exists, else segmented when
@@ -180,9 +182,8 @@ size_t efla_forward_varlen_workspace_size(int N, int H, int T, int d_k, int d_v,
  *   workspace  device buffer of efla_forward_varlen_workspace_size(...)
  *         bytes, 256-byte aligned, owned by the caller (NULL allowed when
  *         that size is 0 or T = 0); too small: EFLA_ERR_WORKSPACE
- * The staged and segmented paths compute the coefficients of every token of
- * the T-token axes, inside a sequence or not; beta outside every sequence is
- * read and its result discarded.
+ * Tokens outside every sequence are not read on the staged and segmented
+ * paths.
  */
 efla_status_t efla_forward_varlen_ex(const void *q, const void *k, const void *v,
                                      const float *beta, const int *cu_seqlens, const float *S0,
@@ -212,7 +213,7 @@ efla_status_t efla_forward_config(const void *q, const void *k, const void *v, c
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): efla_forward_update without a workspace argument.  The
  * fused path needs no workspace; the staged and segmented paths keep their
- * intermediates (alpha, W, U, A and the segment maps) in a device array of
+ * intermediates (W, U, A and the segment maps) in a device array of
  * EFLA_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs
  * on until the process ends.  A shape whose workspace on the path taken
  * (efla_forward_workspace_size_ex) exceeds that size returns
@@ -273,7 +274,9 @@ efla_status_t efla_decode_step_indexed(const void *q, const void *k, const void 
                                        efla_dtype_t dt, efla_update_t update, void *stream);
 
 /*
- * Stage 1 of the staged path: per-token coefficients (Methodology 2-3).
+ * Per-token coefficients (Methodology 2-3): the first stage of the chunked
+ * form, exported on its own.  (The forward entry points form them inside
+ * their UT transform or fused kernel, from the same formula.)
  *   k [n_tokens, d_k] dtype dt; beta [n_tokens] fp32
  *   alpha [n_tokens] fp32 out; lambda [n_tokens] fp32 out, or NULL to skip.
  * lambda_t = |k_t|^2 accumulated in fp32 from the stored k; with

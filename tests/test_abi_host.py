@@ -55,11 +55,12 @@ def test_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    # staged path: alpha fp32 + W + U (dtype) + A (dtype), each 256-byte aligned
+    # staged path: W + U (dtype) + A (dtype), each 256-byte aligned (the UT
+    # transform forms alpha itself)
     B, H, L, d, C = 4, 16, 4096, 128, 64
     n = B * H * L
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    want = up(n * 4) + up(n * d * 2) + up(n * d * 2) + up(B * H * (L // C) * C * C * 2)
+    want = up(n * d * 2) + up(n * d * 2) + up(B * H * (L // C) * C * C * 2)
     assert _lib.efla_forward_workspace_size_ex(B, H, L, d, d, C, _lib.EFLA_BF16,
                                                _lib.EFLA_PATH_STAGED) == want
     assert _lib.efla_forward_workspace_size(1, 1, 64, 48, 16, 16, _lib.EFLA_F32) == 0  # unsupported
@@ -67,7 +68,7 @@ def test_workspace_size(lib):
     # ragged L rounds the chunk count up
     assert _lib.efla_forward_workspace_size_ex(1, 1, 65, 16, 16, 64, _lib.EFLA_F32,
                                                _lib.EFLA_PATH_STAGED) == \
-        up(65 * 4) + up(65 * 16 * 4) * 2 + up(2 * 64 * 64 * 4)
+        up(65 * 16 * 4) * 2 + up(2 * 64 * 64 * 4)
 
 
 def _fwd(lib, **over):
@@ -202,12 +203,11 @@ def test_varlen_ex_validation(lib):
 
 
 def test_varlen_workspace_size(lib):
-    # alpha fp32, W, U, A by token (dtype) over H*T tokens, chunk offsets int32 [N+1]
+    # W, U, A by token (dtype) over H*T tokens, chunk offsets int32 [N+1]
     N, H, T, dk, dv, C = 5, 3, 1000, 64, 32, 32
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     for dt, e in ((_lib.EFLA_F32, 4), (_lib.EFLA_BF16, 2)):
-        want = up(H * T * 4) + up(H * T * dk * e) + up(H * T * dv * e) + up(H * T * C * e) + \
-            up((N + 1) * 4)
+        want = up(H * T * dk * e) + up(H * T * dv * e) + up(H * T * C * e) + up((N + 1) * 4)
         assert _lib.efla_forward_varlen_workspace_size(N, H, T, dk, dv, C, dt,
                                                        _lib.EFLA_PATH_STAGED) == want
     assert _lib.efla_forward_varlen_workspace_size(N, H, T, dk, dv, C, _lib.EFLA_BF16,
