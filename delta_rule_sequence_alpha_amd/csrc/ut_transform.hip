@@ -21,6 +21,9 @@ namespace efla {
 
 template <typename T, int DK, int DV, int C>
 struct UtLayout {
+    // waves per workgroup: the fp32 workgroup is alone on its CU (LDS), so it
+    // brings eight waves, two per SIMD; bf16 workgroups fit two per CU at four
+    static constexpr int NW = is_bf16<T> ? 4 : 8, NT = 64 * NW;
     static constexpr int PADE = is_bf16<T> ? 8 : 4;   // 16 bytes of row padding
     static constexpr int LDK = DK + PADE, LDV = DV + PADE;
     static constexpr int LDG = C + 1;                  // fp32, scalar access only
@@ -102,18 +105,14 @@ __device__ __forceinline__ long ut_next(long id, int stride, int total, int L, i
 // alpha == NULL: the coefficients are formed here from beta (and euler), with
 // lambda_r = k_r . k_r the diagonal of the chunk's Gram matrix.
 template <typename T, int DK, int DV, int C>
-__global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                 const T *__restrict__ v,
-                                                 const float *__restrict__ alpha,
-                                                 T *__restrict__ w, T *__restrict__ u,
-                                                 T *__restrict__ aqk, int L, int nchunks,
-                                                 const int *__restrict__ cu,
-                                                 const int *__restrict__ cu_chunks, int N,
-                                                 int total, const float *__restrict__ beta,
-                                                 int euler)
+__global__ __launch_bounds__((UtLayout<T, DK, DV, C>::NT)) void ut_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const float *__restrict__ alpha, T *__restrict__ w, T *__restrict__ u, T *__restrict__ aqk,
+    int L, int nchunks, const int *__restrict__ cu, const int *__restrict__ cu_chunks, int N,
+    int total, const float *__restrict__ beta, int euler)
 {
     using Lay = UtLayout<T, DK, DV, C>;
-    constexpr int MC = C / 16;
+    constexpr int NW = Lay::NW, NT = 64 * NW, MC = C / 16;
     constexpr bool BF = is_bf16<T>;
     extern __shared__ __align__(16) char smem[];
     T *sK = reinterpret_cast<T *>(smem + Lay::offK);
@@ -130,8 +129,8 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
 
     UtChunk<T, C> cur, nxt;
     long id = ut_next<T, C>(blockIdx.x, stride, total, L, nchunks, cu, cu_chunks, N, aqk, cur);
-    TileRegs<T, C, DK, 256> tk, tq;
-    TileRegs<T, C, DV, 256> tv;
+    TileRegs<T, C, DK, NT> tk, tq;
+    TileRegs<T, C, DV, NT> tv;
     if (id < total) {
         tk.load(k + cur.tok0 * DK, DK, cur.valid);
         tq.load(q + cur.tok0 * DK, DK, cur.valid);
@@ -146,10 +145,10 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
 
         tk.store(sK, Lay::LDK, valid);
         tq.store(sQ, Lay::LDK, valid);
-        for (int i = threadIdx.x; i < C * Lay::LDG; i += 256) sT[i] = 0.f;
+        for (int i = threadIdx.x; i < C * Lay::LDG; i += NT) sT[i] = 0.f;
         float be = 0.f;   // alpha from beta: token `lane` of the chunk, wave 0
         if (alpha) {
-            for (int i = threadIdx.x; i < C; i += 256) sAl[i] = (i < valid) ? alpha[tok0 + i] : 0.f;
+            for (int i = threadIdx.x; i < C; i += NT) sAl[i] = (i < valid) ? alpha[tok0 + i] : 0.f;
         } else if (wv == 0 && lane < valid) {
             be = beta[tok0 + lane];
         }
@@ -161,7 +160,7 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
 
         // Gram tiles G = K K^T (lower incl. diagonal, fp32 into LDS) and A = tril(Q K^T)
         // (written to global; tiles above the diagonal are written as zeros).
-        for (int t = wv; t < 2 * MC * MC; t += 4) {
+        for (int t = wv; t < 2 * MC * MC; t += NW) {
             const bool gram = t < MC * MC;
             const int tt = gram ? t : t - MC * MC;
             const int it = tt / MC, jt = tt - it * MC;
@@ -237,7 +236,7 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
         const T *sTop = nullptr;   // T as the MFMA A operand
         int ldTop = 0;
         if constexpr (BF) {
-            for (int i = threadIdx.x; i < C * C; i += 256) {
+            for (int i = threadIdx.x; i < C * C; i += NT) {
                 const int r = i / C, cc = i - r * C;
                 sTb[r * Lay::LDTB + cc] = from_f32<T>(sT[r * Lay::LDG + cc]);
             }
@@ -255,11 +254,11 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
         // [0, 16mt+16)).  Each product is staged in LDS over the operand it no
         // longer needs (W over K, U over V) and written with 16-byte stores.
         constexpr int NTK = DK / 16, NTV = DV / 16;
-        constexpr int WPW = (MC * NTK + 3) / 4, UPW = (MC * NTV + 3) / 4;   // tiles per wave
+        constexpr int WPW = (MC * NTK + NW - 1) / NW, UPW = (MC * NTV + NW - 1) / NW;   // per wave
         f32x4 acc[WPW > UPW ? WPW : UPW];
 #pragma unroll
         for (int j = 0; j < WPW; ++j) {
-            const int t = wv + 4 * j, mt = t / NTK, nt = t - mt * NTK;
+            const int t = wv + NW * j, mt = t / NTK, nt = t - mt * NTK;
             if (t < MC * NTK)
                 acc[j] = mm_lds<T, C, false, true>(zero4(), sTop, ldTop, 16 * mt, sK, Lay::LDK,
                                                    16 * nt, 16 * mt + 16);
@@ -267,7 +266,7 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
         __syncthreads();   // every read of K is done
 #pragma unroll
         for (int j = 0; j < WPW; ++j) {
-            const int t = wv + 4 * j, mt = t / NTK, nt = t - mt * NTK;
+            const int t = wv + NW * j, mt = t / NTK, nt = t - mt * NTK;
             if (t < MC * NTK)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -275,7 +274,7 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
         }
 #pragma unroll
         for (int j = 0; j < UPW; ++j) {
-            const int t = wv + 4 * j, mt = t / NTV, nt = t - mt * NTV;
+            const int t = wv + NW * j, mt = t / NTV, nt = t - mt * NTV;
             if (t < MC * NTV)
                 acc[j] = mm_lds<T, C, false, true>(zero4(), sTop, ldTop, 16 * mt, sV, Lay::LDV,
                                                    16 * nt, 16 * mt + 16);
@@ -283,15 +282,15 @@ __global__ __launch_bounds__(256) void ut_kernel(const T *__restrict__ q, const 
         __syncthreads();   // every read of V is done; W is staged
 #pragma unroll
         for (int j = 0; j < UPW; ++j) {
-            const int t = wv + 4 * j, mt = t / NTV, nt = t - mt * NTV;
+            const int t = wv + NW * j, mt = t / NTV, nt = t - mt * NTV;
             if (t < MC * NTV)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     sV[(16 * mt + 4 * g + r) * Lay::LDV + 16 * nt + l16] = from_f32<T>(acc[j][r]);
         }
         __syncthreads();
-        store_rows_t<T, C, DK, 256>(w + tok0 * DK, DK, sK, Lay::LDK, valid);
-        store_rows_t<T, C, DV, 256>(u + tok0 * DV, DV, sV, Lay::LDV, valid);
+        store_rows_t<T, C, DK, NT>(w + tok0 * DK, DK, sK, Lay::LDK, valid);
+        store_rows_t<T, C, DV, NT>(u + tok0 * DV, DV, sV, Lay::LDV, valid);
         __syncthreads();   // the staged W and U are read before the next chunk's tiles land
         id = nid;
         cur = nxt;
@@ -359,8 +358,8 @@ hipError_t launch_ut(const void *q, const void *k, const void *v, const float *a
     // over chunks
     const long resident = 256L * (long)(kLdsPerCu / Lay::bytes > 0 ? kLdsPerCu / Lay::bytes : 1);
     const long grid = total < resident ? total : resident;
-    hipLaunchKernelGGL((ut_kernel<T, DK, DV, C>), dim3((unsigned)grid), dim3(256), Lay::bytes, st,
-                       static_cast<const T *>(q), static_cast<const T *>(k),
+    hipLaunchKernelGGL((ut_kernel<T, DK, DV, C>), dim3((unsigned)grid), dim3(Lay::NT), Lay::bytes,
+                       st, static_cast<const T *>(q), static_cast<const T *>(k),
                        static_cast<const T *>(v), alpha, static_cast<T *>(w),
                        static_cast<T *>(u), static_cast<T *>(aqk), L, per, cu, cu_chunks, N,
                        (int)total, beta, (int)euler);
