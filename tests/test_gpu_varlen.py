@@ -194,3 +194,44 @@ def test_varlen_segmented_long_stiff_sampled():
         if t1 > t0:
             assert rel_err(o[h:h + 1, t0:t1][None], o_r) <= TOL["f32"]
         assert rel_err(S_L[n, h][None, None], S_r) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("path", ["staged", "segmented", "fused"])
+def test_varlen_offsets_are_clamped(path):
+    """Offsets outside [0, T] are clamped into it (the first below 0, the last
+    past T): the sequences become [0, 40), [40, 40), [40, 90), [90, T), each
+    equal to the oracle run on that range."""
+    dtype = "bf16" if path == "fused" else "f32"
+    w = wl.FORWARD_WORKLOADS["long-stiff-f32"].with_(H=2, d_k=64, d_v=64, chunk=32, dtype=dtype)
+    lengths = [40, 0, 50, 130]
+    note(f"varlen clamped offsets {path} {dtype}")
+    q, k, v, beta, cu, S0 = wl.varlen_inputs(w, lengths, seed=37)
+    T = q.shape[1]
+    bad = torch.tensor([-7, 40, 40, 90, T + 1000], dtype=torch.int32)
+    o, S_L = efla.forward_varlen(*dev(q, k, v, beta, bad), dev(S0) if S0 is not None else None,
+                                 chunk=32, path=path)
+    torch.cuda.synchronize()
+    _check_each(w, lengths, q, k, v, beta, cu, S0, o, S_L)
+
+
+@pytest.mark.parametrize("path", ["staged", "segmented"])
+def test_varlen_many_short_sequences_f32(path):
+    """1000 packed sequences (many empty or shorter than a chunk) of one head
+    pair: the chunk-offset prefix over a long offset array, checked on a
+    sample of sequences."""
+    w = wl.FORWARD_WORKLOADS["long-stiff-f32"].with_(H=2, d_k=32, d_v=32, chunk=16)
+    lengths = wl.varlen_lengths(1000, 20000, seed=41)
+    note(f"varlen 1000 sequences f32 {path}")
+    q, k, v, beta, cu, S0 = wl.varlen_inputs(w, lengths, seed=41)
+    o, S_L = efla.forward_varlen(*dev(q, k, v, beta, cu), None, chunk=16, path=path)
+    torch.cuda.synchronize()
+    c = cu.tolist()
+    picks = [0, 1, 2, 499, 500, 998, 999] + [i for i, n in enumerate(lengths) if n == 0][:2] + \
+        [max(range(1000), key=lambda i: lengths[i])]
+    for n in picks:
+        t0, t1 = c[n], c[n + 1]
+        o_r, S_r = oracle.forward(q[:, t0:t1][None], k[:, t0:t1][None], v[:, t0:t1][None],
+                                  beta[:, t0:t1][None], None)
+        if t1 > t0:
+            assert rel_err(o[:, t0:t1][None], o_r) <= TOL["f32"], n
+        assert rel_err(S_L[n][None], S_r) <= TOL["f32"], n
