@@ -402,7 +402,34 @@ def bench_config(args, name, dev):
     out["token_heads_per_s"] = w.B * w.H * w.L / (res["ms_per_step"] * 1e-3)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, host)
+    if w.recipe == "stiff":
+        out["stiff_exact_vs_euler"] = stiff_compare(w, host, dev)
     return out
+
+
+def stiff_compare(w, host, dev):
+    """The stiff workload under both updates on the same kernels: the exact
+    flow's state stays bounded, the explicit Euler step's (transition
+    eigenvalue 1 - beta lambda, far below -1) overflows.  Kernel time of each
+    and the size of the resulting state."""
+    q, k, v, beta, S0 = host
+    qd, kd, vd, bd = (x.to(dev) for x in (q, k, v, beta))
+    s0d = None if S0 is None else S0.to(dev)
+    res = {}
+    for upd in ("exact", "euler"):
+        efla.forward(qd, kd, vd, bd, s0d, chunk=w.chunk, update=upd)   # warm
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        o, S_L = efla.forward(qd, kd, vd, bd, s0d, chunk=w.chunk, update=upd)
+        e1.record()
+        torch.cuda.synchronize()
+        fin = torch.isfinite(S_L)
+        res[upd] = {"ms": e0.elapsed_time(e1),
+                    "S_L_nonfinite_fraction": float((~fin).float().mean()),
+                    "S_L_max_abs_finite": float(S_L[fin].abs().max()) if bool(fin.any()) else None}
+    return res
 
 
 def backward_flops_per_token(dk, dv, C):

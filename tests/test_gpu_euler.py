@@ -3,8 +3,9 @@ with the fp64 oracle's Euler recurrence, on every path that takes it: the
 fused and staged forward, the decode step and the coefficient stage.
 
 Inputs follow the lm1.3b recipe (lambda ~ 1, beta < 1), where the explicit
-Euler step is stable; in the stiff regime it is not (see the oracle pins), so
-there is nothing finite to compare."""
+Euler step is stable.  In the stiff regime it is not (see the oracle pins):
+the last test shows the GPU kernels' Euler state diverging there while the
+exact flow's stays bounded and equal to the oracle's."""
 import pytest
 import torch
 
@@ -72,3 +73,39 @@ def test_coefficients_euler_is_beta():
     assert torch.equal(a.cpu(), beta)
     _, lam_r = oracle.coefficients(k, beta)
     assert rel_err(lam, lam_r) <= 1e-6
+
+
+@pytest.mark.parametrize("path", ["staged", "segmented"])
+def test_stiff_recipe_euler_diverges_exact_stays_bounded(path):
+    """The stiff regime the exact flow is for (Technical Summary, Problem
+    Statement): with beta lambda up to ~5e4 the Euler transition
+    I - beta k k^T has an eigenvalue 1 - beta lambda far below -1 along k, so
+    the Euler state blows up within a few such tokens, while the exact
+    transition's eigenvalue e^{-beta lambda} stays in (0, 1] and the state
+    stays bounded.  Same kernels, same inputs, only alpha differs."""
+    w = wl.FORWARD_WORKLOADS["long-stiff-f32"].with_(B=1, H=2, L=64 * 40)
+    note(f"stiff exact vs euler {path}")
+    q, k, v, beta, S0 = wl.forward_inputs(w, seed=43)
+    args = dev(q, k, v, beta, S0)
+    o_x, S_x = efla.forward(*args, chunk=w.chunk, path=path)
+    o_e, S_e = efla.forward(*args, chunk=w.chunk, path=path, update="euler")
+    torch.cuda.synchronize()
+    # exact: finite, and (each transition a contraction, ||I - alpha k k^T|| <= 1)
+    # |S_L|_F at most |S0|_F plus the tokens' injections |alpha k v^T|_F =
+    # alpha |k| |v| <= min(|v| / |k|, beta |k| |v|)  (alpha <= 1/lambda, alpha <= beta)
+    assert torch.isfinite(o_x).all() and torch.isfinite(S_x).all()
+    kn = k.double().norm(dim=-1)
+    vn = v.double().norm(dim=-1)
+    inj = torch.minimum(vn / kn.clamp_min(1e-300), beta.double() * kn * vn)
+    bound = inj.sum(dim=-1)
+    if S0 is not None:
+        bound = bound + S0.double().norm(dim=(-2, -1))
+    assert bool((S_x.double().cpu().norm(dim=(-2, -1)) <= bound * (1 + 1e-6)).all())
+    # Euler: overflowed (non-finite) or astronomically large
+    big = (~torch.isfinite(S_e)).any() or float(S_e.abs().max()) > 1e30
+    print(f"  exact |S_L| {float(S_x.abs().max()):.3e}; euler non-finite "
+          f"{float((~torch.isfinite(S_e)).float().mean()):.2f}", flush=True)
+    assert big
+    # the exact result is the oracle's
+    o_r, S_r = oracle.forward(q, k, v, beta, S0)
+    assert rel_err(o_x, o_r) <= TOL["f32"] and rel_err(S_x, S_r) <= TOL["f32"]
