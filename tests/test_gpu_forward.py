@@ -247,3 +247,32 @@ def test_split_and_resume_stiff_f32(path, L, t0):
          rel_err(S, S_r))
     print(f"  err split o={e[0]:.3e} S={e[1]:.3e} whole o={e[2]:.3e} S={e[3]:.3e}", flush=True)
     assert max(e) <= tol
+
+
+@pytest.mark.parametrize("path,dtype", [("fused", "bf16"), ("staged", "bf16"), ("staged", "f32"),
+                                        ("segmented", "f32")])
+def test_affine_in_state_and_values(path, dtype):
+    """With q, k, beta fixed the outputs are linear in (S0, V) jointly (the
+    update and readout are linear in S and v).  Scaling both by 2 is exact in
+    binary floating point, so o(2 S0, 2 V) = 2 o(S0, V) bit for bit; and for
+    fp32 inputs o(S0 + S0', V + V') = o(S0, V) + o(S0', V') within fp32
+    rounding."""
+    L = 64 * 24 + 9 if path == "segmented" else 64 * 3 + 29
+    w = wl.FORWARD_WORKLOADS["long-stiff-f32"].with_(B=1, H=2, L=L, dtype=dtype)
+    note(f"forward affinity {path} {dtype} L={L}")
+    q, k, v, beta, _ = wl.forward_inputs(w, seed=47)
+    g = torch.Generator().manual_seed(47)
+    S0 = torch.randn(1, 2, w.d_k, w.d_v, generator=g) * 0.1
+    v2 = (torch.randn(v.shape, generator=g)).to(v.dtype)
+    S02 = torch.randn(1, 2, w.d_k, w.d_v, generator=g) * 0.1
+    run = lambda vv, ss: efla.forward(*dev(q, k, vv, beta, ss), chunk=w.chunk, path=path)  # noqa: E731
+    o1, s1 = run(v, S0)
+    o2, s2 = run((2 * v.float()).to(v.dtype), 2 * S0)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, 2 * o1) and torch.equal(s2, 2 * s1)
+    if dtype == "f32":
+        o3, s3 = run(v2, S02)
+        o4, s4 = run(v + v2, S0 + S02)
+        torch.cuda.synchronize()
+        assert rel_err(o4, (o1 + o3).double().cpu().numpy()) <= 1e-5
+        assert rel_err(s4, (s1 + s3).double().cpu().numpy()) <= 1e-5
