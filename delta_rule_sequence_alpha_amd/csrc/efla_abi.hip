@@ -128,17 +128,16 @@ efla_status_t check_varlen(int N, int H, int T, int dk, int dv, int chunk, efla_
     return EFLA_OK;
 }
 
-// The packed path: AUTO takes the fused kernel where it exists, else the
-// segmented scan when a sequence as long as the whole token axis would be
-// split, else the staged one.  G for the segmented path is planned for that
-// longest possible sequence; shorter ones leave segments empty.
+efla_path_t auto_path(efla_dtype_t dt, long long BH, int L, int dk, int dv, int chunk);
+
+// The packed path: AUTO as for fixed lengths (auto_path), with the segment
+// plan made for a sequence as long as the whole token axis; shorter ones
+// leave segments empty.
 efla_path_t resolve_varlen_path(efla_path_t p, efla_dtype_t dt, int N, int H, int T, int dk,
                                 int dv, int chunk)
 {
     if (p != EFLA_PATH_AUTO) return p;
-    if (efla::fused_supported(dt == EFLA_BF16, dk, dv, chunk)) return EFLA_PATH_FUSED;
-    return seg_plan((long long)N * H, T, dk, dv, chunk, dt == EFLA_F32).G > 1 ? EFLA_PATH_SEGMENTED
-                                                               : EFLA_PATH_STAGED;
+    return auto_path(dt, (long long)N * H, T, dk, dv, chunk);
 }
 
 int varlen_G(efla_path_t p, int N, int H, int T, int dk, int dv, int chunk, bool wide)
@@ -178,15 +177,30 @@ BackwardWs backward_ws(int B, int H, int L, int dk, int dv, int chunk, efla_dtyp
     return s;
 }
 
-// AUTO: the fused kernel where it exists (bf16 inputs); else the segmented
-// scan when it has more than one segment per sequence, else the staged one.
+// AUTO: the fused kernel where it exists (bf16 inputs), unless it would run
+// so few workgroups (one per sequence and 32 state columns) that most CUs
+// idle while the segmented scan splits the sequences: at d = 128, C = 64 the
+// fused kernel took 0.66 ms and the segmented path 0.41 ms for 1 x 8 heads x
+// 32768 tokens (32 workgroups), against 1.32 and 1.52 ms for 1 x 16 x 65536
+// (64 workgroups).  Otherwise (fp32) the segmented scan when it has more
+// than one segment per sequence, else the staged one.
+constexpr long long kFusedFewWorkgroups = 32;
+
+efla_path_t auto_path(efla_dtype_t dt, long long BH, int L, int dk, int dv, int chunk)
+{
+    const int G = seg_plan(BH, L, dk, dv, chunk, dt == EFLA_F32).G;
+    if (efla::fused_supported(dt == EFLA_BF16, dk, dv, chunk)) {
+        const long long fused_wgs = BH * ((dv + 31) / 32);
+        return fused_wgs <= kFusedFewWorkgroups && G > 1 ? EFLA_PATH_SEGMENTED : EFLA_PATH_FUSED;
+    }
+    return G > 1 ? EFLA_PATH_SEGMENTED : EFLA_PATH_STAGED;
+}
+
 efla_path_t resolve_path(efla_path_t p, efla_dtype_t dt, int B, int H, int L, int dk, int dv,
                          int chunk)
 {
     if (p != EFLA_PATH_AUTO) return p;
-    if (efla::fused_supported(dt == EFLA_BF16, dk, dv, chunk)) return EFLA_PATH_FUSED;
-    return seg_plan((long long)B * H, L, dk, dv, chunk, dt == EFLA_F32).G > 1 ? EFLA_PATH_SEGMENTED
-                                                               : EFLA_PATH_STAGED;
+    return auto_path(dt, (long long)B * H, L, dk, dv, chunk);
 }
 
 int plan_G(efla_path_t p, int B, int H, int L, int dk, int dv, int chunk, bool wide)
@@ -305,7 +319,15 @@ efla_status_t forward_impl(const void *q, const void *k, const void *v, const fl
     if (path != EFLA_PATH_AUTO && path != EFLA_PATH_STAGED && path != EFLA_PATH_FUSED &&
         path != EFLA_PATH_SEGMENTED)
         return EFLA_ERR_INVALID_ARG;
+    const bool auto_chosen = path == EFLA_PATH_AUTO;
     path = resolve_path(path, dt, B, H, L, dk, dv, chunk);
+    // allocation-free: AUTO keeps to the fused kernel (no intermediates) when
+    // the path it would take does not fit in the scratch array
+    if (noalloc && auto_chosen && path != EFLA_PATH_FUSED &&
+        efla::fused_supported(dt == EFLA_BF16, dk, dv, chunk) &&
+        staged_ws(B, H, L, dk, dv, chunk, dt, plan_G(path, B, H, L, dk, dv, chunk, dt == EFLA_F32))
+                .total > kScratchBytes)
+        path = EFLA_PATH_FUSED;
     const long long BH = (long long)B * H;
     if (BH == 0) return EFLA_OK;
     if (!S_L || !aligned16(S_L) || (S0 && !aligned16(S0))) return EFLA_ERR_INVALID_ARG;

@@ -53,9 +53,11 @@ typedef enum {
     EFLA_ERR_HIP = 4           /* a HIP launch reported an error                   */
 } efla_status_t;
 
-/* Evaluation strategy of efla_forward_ex.  AUTO takes FUSED for bf16 inputs;
- * for fp32, SEGMENTED when the sequences are too few to fill the GPU and long
- * enough to split, else STAGED. */
+/* Evaluation strategy of efla_forward_ex.  AUTO takes FUSED for bf16 inputs
+ * unless the fused kernel would run at most 32 workgroups (one per sequence
+ * and 32 state columns) and the sequences are long enough to split, then
+ * SEGMENTED; for fp32, SEGMENTED when the sequences are too few to fill the
+ * GPU and long enough to split, else STAGED. */
 typedef enum {
     EFLA_PATH_AUTO = 0,    /* the fastest path available for the shape         */
     EFLA_PATH_STAGED = 1,  /* UT transform (with the coefficients) -> state
@@ -176,9 +178,8 @@ size_t efla_forward_varlen_workspace_size(int N, int H, int T, int d_k, int d_v,
  *         transform, state scan; one scan per (sequence, head)),
  *         EFLA_PATH_SEGMENTED (the scan split into segment maps, their
  *         composition and a replay: for few long sequences), or
- *         EFLA_PATH_AUTO (fused where it exists, else segmented when
- *         efla_forward_varlen_workspace_size plans more than one segment,
- *         else staged)
+ *         EFLA_PATH_AUTO (as for efla_forward_ex, the segment plan made for
+ *         a sequence as long as the whole token axis)
  *   workspace  device buffer of efla_forward_varlen_workspace_size(...)
  *         bytes, 256-byte aligned, owned by the caller (NULL allowed when
  *         that size is 0 or T = 0); too small: EFLA_ERR_WORKSPACE
@@ -217,7 +218,8 @@ efla_status_t efla_forward_config(const void *q, const void *k, const void *v, c
  * EFLA_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs
  * on until the process ends.  A shape whose workspace on the path taken
  * (efla_forward_workspace_size_ex) exceeds that size returns
- * EFLA_ERR_WORKSPACE with nothing launched.  This entry calls no hipMalloc,
+ * EFLA_ERR_WORKSPACE with nothing launched; with EFLA_PATH_AUTO, bf16 inputs
+ * then take the fused kernel instead (which needs none).  This entry calls no hipMalloc,
  * hipFree or allocating routine.  Every call on one device shares the array
  * and relies on nothing it held before (each call writes every intermediate
  * it reads): calls that overlap in time on one device -- on different streams,

@@ -227,8 +227,17 @@ def test_varlen_workspace_size(lib):
 
 
 def test_auto_path_choice(lib):
-    # bf16: the fused kernel; fp32: segmented scan for few long sequences, else staged
+    # bf16: the fused kernel, unless it would run <= 32 workgroups (sequences x
+    # 32-column tiles) on sequences long enough to split; fp32: segmented scan
+    # for few long sequences, else staged
     assert _lib.efla_forward_path(4, 16, 4096, 128, 128, 64, _lib.EFLA_BF16) == _lib.EFLA_PATH_FUSED
+    assert _lib.efla_forward_path(1, 16, 65536, 128, 128, 64, _lib.EFLA_BF16) == _lib.EFLA_PATH_FUSED
+    assert _lib.efla_forward_path(1, 8, 32768, 128, 128, 64, _lib.EFLA_BF16) == \
+        _lib.EFLA_PATH_SEGMENTED
+    assert _lib.efla_forward_path(1, 8, 256, 128, 128, 64, _lib.EFLA_BF16) == _lib.EFLA_PATH_FUSED
+    assert _lib.efla_forward_workspace_size(1, 8, 32768, 128, 128, 64, _lib.EFLA_BF16) > 0
+    assert _lib.efla_forward_varlen_workspace_size(2, 4, 32768, 128, 128, 64, _lib.EFLA_BF16,
+                                                   _lib.EFLA_PATH_AUTO) > 0
     assert _lib.efla_forward_path(1, 16, 65536, 128, 128, 64, _lib.EFLA_F32) == _lib.EFLA_PATH_SEGMENTED
     assert _lib.efla_forward_path(1, 1, 64, 16, 16, 16, _lib.EFLA_F32) == _lib.EFLA_PATH_STAGED
     assert _lib.efla_forward_path(8, 16, 4096, 128, 128, 64, _lib.EFLA_F32) == _lib.EFLA_PATH_STAGED

@@ -68,3 +68,38 @@ def test_noalloc_matches_workspace_entry(path, recipe, first, second):
         eo, es = rel_err(o_n, o_r), rel_err(S_n, S_r)
         print(f"  err o={eo:.3e} S_L={es:.3e}", flush=True)
         assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
+
+
+def test_noalloc_auto_keeps_fused_when_scratch_too_small():
+    """bf16, few long sequences: AUTO would take the segmented scan, whose
+    intermediates (168 MB here) exceed the scratch array; the allocation-free
+    entry then runs the fused kernel, bit for bit as the workspace entry does
+    on that path."""
+    w = wl.FORWARD_WORKLOADS["lm1.3b-bf16"].with_(B=1, H=8, L=32768)
+    need = _lib.efla_forward_workspace_size_ex(1, 8, 32768, 128, 128, 64, _lib.EFLA_BF16,
+                                               _lib.EFLA_PATH_AUTO)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    note("noalloc auto fallback to fused, B=1 H=8 L=32768 bf16")
+    q, k, v, beta, S0 = wl.forward_inputs(w, seed=45)
+    qd, kd, vd, bd, s0d = dev(q, k, v, beta, S0)
+    p = lambda x: x.data_ptr()  # noqa: E731
+    sp = torch.cuda.current_stream().cuda_stream
+    outs = []
+    for fused in (False, True):
+        o = torch.empty((1, 8, 32768, 128), dtype=torch.bfloat16, device="cuda")
+        S_L = torch.empty((1, 8, 128, 128), dtype=torch.float32, device="cuda")
+        if fused:
+            st = _lib.efla_forward_update(p(qd), p(kd), p(vd), p(bd), p(s0d), p(o), p(S_L), 1, 8,
+                                          32768, 128, 128, 64, _lib.EFLA_BF16, None, 0,
+                                          _lib.EFLA_PATH_FUSED, _lib.EFLA_EXACT, sp)
+        else:
+            st = _lib.efla_forward_noalloc(p(qd), p(kd), p(vd), p(bd), p(s0d), p(o), p(S_L), 1, 8,
+                                           32768, 128, 128, 64, _lib.EFLA_BF16,
+                                           _lib.EFLA_PATH_AUTO, _lib.EFLA_EXACT, sp)
+        assert st == _lib.EFLA_OK, _lib.status_string(st)
+        outs.append((o, S_L))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    sl = (slice(0, 1), slice(5, 6))
+    o_r, S_r = oracle.forward(q[sl], k[sl], v[sl], beta[sl], S0[sl])
+    assert rel_err(outs[0][0][sl], o_r) <= TOL["bf16"] and rel_err(outs[0][1][sl], S_r) <= TOL["bf16"]
