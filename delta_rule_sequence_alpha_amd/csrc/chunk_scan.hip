@@ -85,7 +85,7 @@ __device__ __forceinline__ void scan_body(
     // DK / TV tiles of P after the NTILE tiles of R
     const int ntiles = NTILE + (sg.mode == SCAN_SUMMARY ? DK / TV : 0);
     int bhs, tile;
-    xcd_map(bid, nblocks, ntiles, bhs, tile);
+    xcd_map_rr(bid, nblocks, ntiles, bhs, tile);
     const int bh = bhs / sg.G, gs = bhs - bh * sg.G;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
     const bool ptile = tile >= NTILE;                 // a column of P (U = 0, from S = I)

@@ -130,19 +130,37 @@ efla_status_t check_varlen(int N, int H, int T, int dk, int dv, int chunk, efla_
 
 efla_path_t auto_path(efla_dtype_t dt, long long BH, int L, int dk, int dv, int chunk);
 
-// The packed path: AUTO as for fixed lengths (auto_path), with the segment
-// plan made for a sequence as long as the whole token axis; shorter ones
-// leave segments empty.
+int varlen_G(efla_path_t p, int N, int H, int T, int dk, int dv, int chunk, bool wide);
+
+// The packed path.  AUTO for bf16 as for fixed lengths (auto_path).  For
+// fp32 the host knows no lengths and the longest sequence bounds the plain
+// scan, so it takes the segmented scan whenever the plain scan's workgroups
+// (N H d_v / 64) are fewer than the CUs and a sequence as long as the whole
+// token axis would be split.
 efla_path_t resolve_varlen_path(efla_path_t p, efla_dtype_t dt, int N, int H, int T, int dk,
                                 int dv, int chunk)
 {
     if (p != EFLA_PATH_AUTO) return p;
-    return auto_path(dt, (long long)N * H, T, dk, dv, chunk);
+    const long long NH = (long long)N * H;
+    if (efla::fused_supported(dt == EFLA_BF16, dk, dv, chunk))
+        return auto_path(dt, NH, T, dk, dv, chunk);
+    const bool few = NH * ((dv + 63) / 64) < 256;
+    return few && varlen_G(EFLA_PATH_SEGMENTED, N, H, T, dk, dv, chunk, dt == EFLA_F32) > 1
+               ? EFLA_PATH_SEGMENTED
+               : EFLA_PATH_STAGED;
 }
 
+// Segments per packed sequence: planned for one sequence per head holding the
+// whole token axis (the longest a sequence can be; shorter ones leave
+// segments empty), capped at 4096 (sequence, head, segment) units in all so
+// the maps stay modest (each unit's are 2 d_k d_v + d_k^2 floats).
 int varlen_G(efla_path_t p, int N, int H, int T, int dk, int dv, int chunk, bool wide)
 {
-    return p == EFLA_PATH_SEGMENTED ? seg_plan((long long)N * H, T, dk, dv, chunk, wide).G : 1;
+    if (p != EFLA_PATH_SEGMENTED) return 1;
+    const long long units = (long long)N * H > 0 ? (long long)N * H : 1;
+    long long G = seg_plan(H, T, dk, dv, chunk, wide).G;
+    if (G * units > 4096) G = 4096 / units > 1 ? 4096 / units : 1;
+    return (int)G;
 }
 
 // Backward workspace: the forward's coefficient and UT-transform outputs,

@@ -388,4 +388,21 @@ __device__ __forceinline__ void xcd_map(int bid, int nblocks, int ntile, int &se
     tile = lin - seq * ntile;
 }
 
+// The same with consecutive units on consecutive XCDs (each unit's ntile
+// workgroups still on one XCD): when units carry uneven work (packed
+// sequences of varying length), a run of long ones spreads over all XCDs
+// instead of landing on one.
+__device__ __forceinline__ void xcd_map_rr(int bid, int nblocks, int ntile, int &unit, int &tile)
+{
+    const int units = nblocks / ntile;
+    if (units * ntile == nblocks && (units & 7) == 0) {
+        const int x = bid & 7, m = bid >> 3;   // XCD, and the workgroup's place on it
+        unit = 8 * (m / ntile) + x;
+        tile = m - (m / ntile) * ntile;
+    } else {
+        unit = bid / ntile;
+        tile = bid - unit * ntile;
+    }
+}
+
 }  // namespace efla

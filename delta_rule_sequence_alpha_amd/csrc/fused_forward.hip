@@ -750,7 +750,37 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
     // read past the tensor.
     long tokb = (long)bh * L;
     if (cu_seqlens) {
-        const int seq = bh / H, h = bh - seq * H;
+        int seq = bh / H, h = bh - seq * H;
+        // Longest sequences first.  Workgroups start in launch order and the
+        // longest sequence bounds the launch, so with up to one sequence per
+        // thread the workgroup takes the sequence of the right length rank:
+        // unit r = rank * H + head in the order workgroups start (round-robin
+        // over the XCDs, as xcd_map lays the units out), ties by index.
+        constexpr int NT = 64 * Lay::NW;
+        __shared__ int s_len[NT];
+        __shared__ int s_pick;
+        const int NH = (int)(gridDim.x / NTILE), N = NH / H;
+        if (N > 1 && N <= NT) {
+            int r = bh;
+            if ((gridDim.x & 7) == 0 && NH % 8 == 0) r = 8 * (bh % (NH / 8)) + bh / (NH / 8);
+            const int want = r / H;
+            h = r - want * H;
+            const int t = threadIdx.x;
+            if (t < N) s_len[t] = packed_end(cu_seqlens, t, L) - packed_begin(cu_seqlens, t, L);
+            __syncthreads();
+            if (t < N) {
+                const int lt = s_len[t];
+                int rank = 0;
+                for (int u = 0; u < N; ++u) {
+                    const int lu = s_len[u];
+                    rank += (lu > lt) | ((lu == lt) & (u < t));
+                }
+                if (rank == want) s_pick = t;
+            }
+            __syncthreads();
+            seq = s_pick;
+            bh = seq * H + h;
+        }
         const int t0 = packed_begin(cu_seqlens, seq, L), t1 = packed_end(cu_seqlens, seq, L);
         tokb = (long)h * L + t0;
         L = t1 - t0;

@@ -178,8 +178,10 @@ size_t efla_forward_varlen_workspace_size(int N, int H, int T, int d_k, int d_v,
  *         transform, state scan; one scan per (sequence, head)),
  *         EFLA_PATH_SEGMENTED (the scan split into segment maps, their
  *         composition and a replay: for few long sequences), or
- *         EFLA_PATH_AUTO (as for efla_forward_ex, the segment plan made for
- *         a sequence as long as the whole token axis)
+ *         EFLA_PATH_AUTO (bf16 as for efla_forward_ex; fp32: segmented
+ *         when N * H * ceil(d_v / 64) < 256 and a sequence as long as the
+ *         whole token axis would be split, else staged; the segment plan is
+ *         made for such a sequence)
  *   workspace  device buffer of efla_forward_varlen_workspace_size(...)
  *         bytes, 256-byte aligned, owned by the caller (NULL allowed when
  *         that size is 0 or T = 0); too small: EFLA_ERR_WORKSPACE

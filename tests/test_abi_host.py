@@ -220,6 +220,13 @@ def test_varlen_workspace_size(lib):
     stg = _lib.efla_forward_varlen_workspace_size(1, 16, 65536, 128, 128, 64, _lib.EFLA_F32,
                                                   _lib.EFLA_PATH_STAGED)
     assert seg > stg > 0
+    # four packed fp32 sequences over 16 heads: too few scan workgroups, so segmented
+    assert _lib.efla_forward_varlen_workspace_size(4, 16, 65536, 128, 128, 64, _lib.EFLA_F32,
+                                                   _lib.EFLA_PATH_AUTO) == \
+        _lib.efla_forward_varlen_workspace_size(4, 16, 65536, 128, 128, 64, _lib.EFLA_F32,
+                                                _lib.EFLA_PATH_SEGMENTED) > \
+        _lib.efla_forward_varlen_workspace_size(4, 16, 65536, 128, 128, 64, _lib.EFLA_F32,
+                                                _lib.EFLA_PATH_STAGED)
     assert _lib.efla_forward_varlen_workspace_size(64, 16, 65536, 128, 128, 64, _lib.EFLA_F32,
                                                    _lib.EFLA_PATH_AUTO) == \
         _lib.efla_forward_varlen_workspace_size(64, 16, 65536, 128, 128, 64, _lib.EFLA_F32,

@@ -178,8 +178,9 @@ def test_varlen_segmented_long_stiff_sampled():
     w = wl.FORWARD_WORKLOADS["long-stiff-f32"]
     lengths = [40000, 0, 9000, 16536]
     N, H, T = len(lengths), w.H, sum(lengths)
-    assert efla.varlen_workspace_size(N, H, T, 128, 128, 64, torch.float32) == \
-        efla.varlen_workspace_size(N, H, T, 128, 128, 64, torch.float32, path="segmented")
+    seg = efla.varlen_workspace_size(N, H, T, 128, 128, 64, torch.float32, path="segmented")
+    assert efla.varlen_workspace_size(N, H, T, 128, 128, 64, torch.float32) == seg > \
+        efla.varlen_workspace_size(N, H, T, 128, 128, 64, torch.float32, path="staged")
     note("varlen long-stiff-f32 full size, auto path")
     q, k, v, beta, cu, S0 = wl.varlen_inputs(w, lengths, seed=31)
     o, S_L = efla.forward_varlen(*dev(q, k, v, beta, cu, S0), chunk=64)
