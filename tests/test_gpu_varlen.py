@@ -215,14 +215,16 @@ def test_varlen_offsets_are_clamped(path):
     _check_each(w, lengths, q, k, v, beta, cu, S0, o, S_L)
 
 
-@pytest.mark.parametrize("path", ["staged", "segmented"])
-def test_varlen_many_short_sequences_f32(path):
+@pytest.mark.parametrize("path", ["staged", "segmented", "fused"])
+def test_varlen_many_short_sequences(path):
     """1000 packed sequences (many empty or shorter than a chunk) of one head
-    pair: the chunk-offset prefix over a long offset array, checked on a
-    sample of sequences."""
-    w = wl.FORWARD_WORKLOADS["long-stiff-f32"].with_(H=2, d_k=32, d_v=32, chunk=16)
+    pair: the chunk-offset prefix over a long offset array (staged and
+    segmented, fp32), and the fused kernel past the sequence count it orders
+    longest first (bf16), checked on a sample of sequences."""
+    dtype = "bf16" if path == "fused" else "f32"
+    w = wl.FORWARD_WORKLOADS["long-stiff-f32"].with_(H=2, d_k=32, d_v=32, chunk=16, dtype=dtype)
     lengths = wl.varlen_lengths(1000, 20000, seed=41)
-    note(f"varlen 1000 sequences f32 {path}")
+    note(f"varlen 1000 sequences {dtype} {path}")
     q, k, v, beta, cu, S0 = wl.varlen_inputs(w, lengths, seed=41)
     o, S_L = efla.forward_varlen(*dev(q, k, v, beta, cu), None, chunk=16, path=path)
     torch.cuda.synchronize()
@@ -234,5 +236,5 @@ def test_varlen_many_short_sequences_f32(path):
         o_r, S_r = oracle.forward(q[:, t0:t1][None], k[:, t0:t1][None], v[:, t0:t1][None],
                                   beta[:, t0:t1][None], None)
         if t1 > t0:
-            assert rel_err(o[:, t0:t1][None], o_r) <= TOL["f32"], n
-        assert rel_err(S_L[n][None], S_r) <= TOL["f32"], n
+            assert rel_err(o[:, t0:t1][None], o_r) <= TOL[dtype], n
+        assert rel_err(S_L[n][None], S_r) <= TOL[dtype], n
