@@ -503,22 +503,30 @@ def bench_backward(args, w, dev):
                     "per-kernel times from rocprofv3"}
 
 
-def cpu_baseline(w, host):
-    """The fp64 oracle on the host cores, timed on the whole workload.  It
-    runs OpenMP over the B*H independent sequences, so the threads it can
-    use are min(available threads, B*H); that is `cores`."""
+def cpu_baseline(w, host, min_seconds=1.0):
+    """The fp64 oracle on the host cores, timed on whole passes over the
+    workload, repeated until min_seconds of wall time have elapsed (on 16
+    threads about 16-30 s of CPU work).  It runs OpenMP over the B*H
+    independent sequences, so the threads it can use are min(available
+    threads, B*H); that is `cores`."""
     import oracle
     q, k, v, beta, S0 = host
     threads = oracle.max_threads()
     heads = w.B * w.H
+    passes = 0
     t0 = time.perf_counter()
-    oracle.forward(q, k, v, beta, S0)
-    t = time.perf_counter() - t0
-    return {"value": w.B * w.L / t, "unit": "tokens/s", "cores": min(threads, heads),
+    while True:
+        oracle.forward(q, k, v, beta, S0)
+        passes += 1
+        t = time.perf_counter() - t0
+        if t >= min_seconds:
+            break
+    return {"value": passes * w.B * w.L / t, "unit": "tokens/s", "cores": min(threads, heads),
             "threads_available": threads, "cpu_model": cpu_model(),
-            "kind": "oracle", "seconds": t,
-            "sample": f"whole {w.name} workload ({heads} heads x {w.L} tokens), fp64, "
-                      f"OpenMP over heads; inputs converted to fp64 before timing"}
+            "kind": "oracle", "seconds": t, "passes": passes,
+            "sample": f"{passes} whole pass(es) over the {w.name} workload ({heads} heads x "
+                      f"{w.L} tokens), fp64, OpenMP over heads; inputs converted to fp64 "
+                      f"before timing"}
 
 
 def measured_peaks(dev):
