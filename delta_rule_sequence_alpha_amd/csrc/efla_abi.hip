@@ -675,9 +675,10 @@ efla_status_t efla_backward_config(const void *q, const void *k, const void *v, 
     void *states = base + ws.states, *dSout = base + ws.dSout, *dE = base + ws.dE;
     float *R = reinterpret_cast<float *>(base + ws.R), *P = reinterpret_cast<float *>(base + ws.P);
     float *Sin = reinterpret_cast<float *>(base + ws.Sin);
-    hipError_t e = efla::dispatch_coef(bf, dk, k, beta, alpha, lambda, BH * L, euler, st);
-    if (e == hipSuccess)
-        e = efla::dispatch_ut(bf, dk, dv, chunk, q, k, v, alpha, w, u, aqk, (int)BH, L, st);
+    // the UT transform forms alpha and lambda (the Gram diagonal) and keeps them
+    // for the gradient kernel
+    hipError_t e = efla::dispatch_ut(bf, dk, dv, chunk, q, k, v, nullptr, w, u, aqk, (int)BH, L,
+                                     st, nullptr, nullptr, 0, 1, beta, euler, alpha, lambda);
     const int nw = cfg.bwd_scan_waves;
     if (e == hipSuccess && plan.G == 1) {   // the two scans are independent: one launch
         e = efla::dispatch_scan_pair(bf, dk, dv, chunk, q, k, w, u, aqk, S0, states, d_o, dS_L,

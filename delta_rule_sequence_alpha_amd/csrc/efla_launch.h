@@ -38,12 +38,14 @@ hipError_t dispatch_packed_chunks(const int *cu, int N, int L, int chunk, int *c
 
 // cu_chunks != NULL: the packed form above, with BH = H.  alpha == NULL: the
 // coefficients are formed inside from beta (euler: alpha = beta), lambda
-// being the Gram diagonal the transform computes anyway.
+// being the Gram diagonal the transform computes anyway; alpha_out and
+// lambda_out (if given) then receive them, one float per token.
 hipError_t dispatch_ut(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                        const void *v, const float *alpha, void *w, void *u, void *aqk, int BH,
                        int L, hipStream_t st, const int *cu = nullptr,
                        const int *cu_chunks = nullptr, int N = 0, int H = 1,
-                       const float *beta = nullptr, bool euler = false);
+                       const float *beta = nullptr, bool euler = false,
+                       float *alpha_out = nullptr, float *lambda_out = nullptr);
 
 // cu != NULL: the packed form above.
 hipError_t dispatch_scan(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,

@@ -103,13 +103,15 @@ __device__ __forceinline__ long ut_next(long id, int stride, int total, int L, i
 // its V tile, the next V tile) are loaded into registers while this chunk is
 // computed, so the loads' latency is not exposed once per chunk.
 // alpha == NULL: the coefficients are formed here from beta (and euler), with
-// lambda_r = k_r . k_r the diagonal of the chunk's Gram matrix.
+// lambda_r = k_r . k_r the diagonal of the chunk's Gram matrix; alpha_out and
+// lambda_out, if not NULL, receive alpha_r and lambda_r of every valid token.
 template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__((UtLayout<T, DK, DV, C>::NT)) void ut_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ alpha, T *__restrict__ w, T *__restrict__ u, T *__restrict__ aqk,
     int L, int nchunks, const int *__restrict__ cu, const int *__restrict__ cu_chunks, int N,
-    int total, const float *__restrict__ beta, int euler)
+    int total, const float *__restrict__ beta, int euler, float *__restrict__ alpha_out,
+    float *__restrict__ lambda_out)
 {
     using Lay = UtLayout<T, DK, DV, C>;
     constexpr int NW = Lay::NW, NT = 64 * NW, MC = C / 16;
@@ -189,8 +191,15 @@ __global__ __launch_bounds__((UtLayout<T, DK, DV, C>::NT)) void ut_kernel(
         // Diagonal 16x16 blocks of T by forward substitution: wave 0, lane group b
         // handles block b, lane l16 owns column l16 of it (after writing, from
         // beta, the alpha of token `lane`; LDS keeps one wave's accesses in order).
-        if (!alpha && wv == 0 && lane < C)
-            sAl[lane] = lane < valid ? update_alpha(euler, be, sG[lane * Lay::LDG + lane]) : 0.f;
+        if (!alpha && wv == 0 && lane < C) {
+            const float lam = sG[lane * Lay::LDG + lane];
+            const float al = lane < valid ? update_alpha(euler, be, lam) : 0.f;
+            sAl[lane] = al;
+            if (alpha_out && lane < valid) {
+                alpha_out[tok0 + lane] = al;
+                lambda_out[tok0 + lane] = lam;
+            }
+        }
         if (wv == 0 && g < MC) {
             const int b0 = 16 * g, j = l16;
             float t[16];
@@ -342,7 +351,8 @@ constexpr size_t kLdsPerCu = 160 * 1024;   // gfx950
 template <typename T, int DK, int DV, int C>
 hipError_t launch_ut(const void *q, const void *k, const void *v, const float *alpha, void *w,
                      void *u, void *aqk, int BH, int L, const int *cu, const int *cu_chunks, int N,
-                     int H, const float *beta, bool euler, hipStream_t st)
+                     int H, const float *beta, bool euler, float *alpha_out, float *lambda_out,
+                     hipStream_t st)
 {
     using Lay = UtLayout<T, DK, DV, C>;
     const int nchunks = (L + C - 1) / C;
@@ -362,21 +372,23 @@ hipError_t launch_ut(const void *q, const void *k, const void *v, const float *a
                        st, static_cast<const T *>(q), static_cast<const T *>(k),
                        static_cast<const T *>(v), alpha, static_cast<T *>(w),
                        static_cast<T *>(u), static_cast<T *>(aqk), L, per, cu, cu_chunks, N,
-                       (int)total, beta, (int)euler);
+                       (int)total, beta, (int)euler, alpha_out, lambda_out);
     return hipGetLastError();
 }
 
 hipError_t dispatch_ut(bool bf16, int dk, int dv, int chunk, const void *q, const void *k,
                        const void *v, const float *alpha, void *w, void *u, void *aqk, int BH,
                        int L, hipStream_t st, const int *cu, const int *cu_chunks, int N, int H,
-                       const float *beta, bool euler)
+                       const float *beta, bool euler, float *alpha_out, float *lambda_out)
 {
 #define CASE(DKV, DVV, CC)                                                                      \
     if (dk == DKV && dv == DVV && chunk == CC)                                                  \
         return bf16 ? launch_ut<__bf16, DKV, DVV, CC>(q, k, v, alpha, w, u, aqk, BH, L, cu,     \
-                                                      cu_chunks, N, H, beta, euler, st)        \
+                                                      cu_chunks, N, H, beta, euler, alpha_out, \
+                                                      lambda_out, st)                          \
                     : launch_ut<float, DKV, DVV, CC>(q, k, v, alpha, w, u, aqk, BH, L, cu,      \
-                                                     cu_chunks, N, H, beta, euler, st);
+                                                     cu_chunks, N, H, beta, euler, alpha_out,  \
+                                                     lambda_out, st);
     EFLA_SHAPE_CASES(CASE)
 #undef CASE
     return hipErrorInvalidValue;
