@@ -219,15 +219,6 @@ __device__ __forceinline__ void store_rows_nt(T *g, long g_ld, const T *s, int s
     }
 }
 
-// Workgroup barrier for LDS traffic only: this wave's LDS accesses complete,
-// then every wave arrives.  Unlike __syncthreads it does not wait for the
-// wave's global loads, which may stay in flight into later phases (the
-// compiler waits for each load where its register is first read).
-__device__ __forceinline__ void lds_barrier()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // Sum over the 16 lanes of a lane group (one acc-tile row), by DPP moves
 // within the row: pairs, then quads, then lane 0 adds lane 4 (a rotation of
 // the row by 12) and lane 8 (by 8).  Lane 0 holds the butterfly sum

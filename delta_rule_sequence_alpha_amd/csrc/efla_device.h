@@ -163,6 +163,17 @@ __device__ __forceinline__ void mm_acc_b(f32x4 (&out)[MT], const T *A, int lda,
     }
 }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses complete,
+// then every wave arrives.  Unlike __syncthreads it does not wait for the
+// wave's global loads and stores, which may stay in flight into later phases
+// (the compiler waits for each load where its register is first read).  For
+// kernels in which no wave reads global memory that another wave of the
+// workgroup wrote.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // acc (+)= A[i0:i0+16, 0:K] * B[0:K, j0:j0+16] with both operands in LDS.
 // A element (i,k): A[i*lda+k] or, A_STRIDED, A[k*lda+i].
 // B element (k,j): B[j*ldb+k] or, B_STRIDED, B[k*ldb+j].

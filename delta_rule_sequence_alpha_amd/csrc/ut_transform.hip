@@ -86,6 +86,18 @@ __device__ __forceinline__ bool ut_locate(int id, int L, int nchunks, const int 
     return true;
 }
 
+// Tile t of the tiles on and below the diagonal of a block matrix, row by
+// row: t = it (it + 1) / 2 + jt, jt <= it.
+__device__ __forceinline__ void lower_tile(int t, int &it, int &jt)
+{
+    it = 0;
+    while (t > it) {
+        t -= it + 1;
+        ++it;
+    }
+    jt = t;
+}
+
 // The first chunk id >= id (stepping by `stride`) that is a chunk, or an id
 // >= total.
 template <typename T, int C>
@@ -160,24 +172,62 @@ __global__ __launch_bounds__((UtLayout<T, DK, DV, C>::NT)) void ut_kernel(
             tq.load(q + nxt.tok0 * DK, DK, nxt.valid);
         }
 
-        // Gram tiles G = K K^T (lower incl. diagonal, fp32 into LDS) and A = tril(Q K^T)
-        // (written to global; tiles above the diagonal are written as zeros).
-        for (int t = wv; t < 2 * MC * MC; t += NW) {
-            const bool gram = t < MC * MC;
-            const int tt = gram ? t : t - MC * MC;
-            const int it = tt / MC, jt = tt - it * MC;
-            if (gram) {
-                if (jt > it) continue;
-                const f32x4 acc = mm_lds<T, DK, false, false>(zero4(), sK, Lay::LDK, 16 * it, sK,
-                                                              Lay::LDK, 16 * jt);
+        // Gram tiles G = K K^T, the MC (MC + 1) / 2 tiles on and below the
+        // diagonal (fp32 into LDS), dealt round-robin so every SIMD gets an
+        // even share of the MFMAs.
+        constexpr int NLOW = MC * (MC + 1) / 2;
+        for (int t = wv; t < NLOW; t += NW) {
+            int it, jt;
+            lower_tile(t, it, jt);
+            const f32x4 acc = mm_lds<T, DK, false, false>(zero4(), sK, Lay::LDK, 16 * it, sK,
+                                                          Lay::LDK, 16 * jt);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sG[(16 * it + 4 * g + r) * Lay::LDG + 16 * jt + l16] = acc[r];
-            } else {
+            for (int r = 0; r < 4; ++r) sG[(16 * it + 4 * g + r) * Lay::LDG + 16 * jt + l16] = acc[r];
+        }
+        __syncthreads();
+
+        if (wv == 0) {
+            // Wave 0: alpha of token `lane` from beta and the Gram diagonal, then
+            // the diagonal 16x16 blocks of T by forward substitution, lane group b
+            // handling block b, lane l16 column l16 of it (LDS keeps one wave's
+            // accesses in order).
+            if (!alpha && lane < C) {
+                const float lam = sG[lane * Lay::LDG + lane];
+                const float al = lane < valid ? update_alpha(euler, be, lam) : 0.f;
+                sAl[lane] = al;
+                if (alpha_out && lane < valid) {
+                    alpha_out[tok0 + lane] = al;
+                    lambda_out[tok0 + lane] = lam;
+                }
+            }
+            if (g < MC) {
+                const int b0 = 16 * g, j = l16;
+                float t[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float acc = (i == j) ? 1.f : 0.f;
+                    const float *grow = sG + (b0 + i) * Lay::LDG + b0;
+#pragma unroll
+                    for (int m = 0; m < i; ++m) acc = fmaf(-grow[m], t[m], acc);
+                    t[i] = sAl[b0 + i] * acc;
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sT[(b0 + i) * Lay::LDG + b0 + j] = t[i];
+            }
+        } else {
+            // The other waves meanwhile: A = tril(Q K^T), written to global, the
+            // tiles on and below the diagonal first, then the zero tiles above it.
+            for (int t = wv - 1; t < MC * MC; t += NW - 1) {
+                int it, jt;
                 f32x4 acc = zero4();
-                if (jt <= it)
+                if (t < NLOW) {
+                    lower_tile(t, it, jt);
                     acc = mm_lds<T, DK, false, false>(zero4(), sQ, Lay::LDK, 16 * it, sK, Lay::LDK,
                                                       16 * jt);
+                } else {
+                    lower_tile(t - NLOW, jt, it);   // tile (a, b), b <= a, names (b, a + 1)
+                    jt += 1;
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = 16 * it + 4 * g + r, col = 16 * jt + l16;
@@ -185,34 +235,6 @@ __global__ __launch_bounds__((UtLayout<T, DK, DV, C>::NT)) void ut_kernel(
                         aq[row * C + col] = from_f32<T>(col <= row ? acc[r] : 0.f);
                 }
             }
-        }
-        __syncthreads();
-
-        // Diagonal 16x16 blocks of T by forward substitution: wave 0, lane group b
-        // handles block b, lane l16 owns column l16 of it (after writing, from
-        // beta, the alpha of token `lane`; LDS keeps one wave's accesses in order).
-        if (!alpha && wv == 0 && lane < C) {
-            const float lam = sG[lane * Lay::LDG + lane];
-            const float al = lane < valid ? update_alpha(euler, be, lam) : 0.f;
-            sAl[lane] = al;
-            if (alpha_out && lane < valid) {
-                alpha_out[tok0 + lane] = al;
-                lambda_out[tok0 + lane] = lam;
-            }
-        }
-        if (wv == 0 && g < MC) {
-            const int b0 = 16 * g, j = l16;
-            float t[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float acc = (i == j) ? 1.f : 0.f;
-                const float *grow = sG + (b0 + i) * Lay::LDG + b0;
-#pragma unroll
-                for (int m = 0; m < i; ++m) acc = fmaf(-grow[m], t[m], acc);
-                t[i] = sAl[b0 + i] * acc;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sT[(b0 + i) * Lay::LDG + b0 + j] = t[i];
         }
         __syncthreads();
 
