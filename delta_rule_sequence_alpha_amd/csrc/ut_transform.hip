@@ -27,6 +27,9 @@ struct UtLayout {
     static constexpr int PADE = is_bf16<T> ? 8 : 4;   // 16 bytes of row padding
     static constexpr int LDK = DK + PADE, LDV = DV + PADE;
     static constexpr int LDG = C + 1;                  // fp32, scalar access only
+    // T (fp32): rows 16-byte aligned, so that a lane's four consecutive k of
+    // the A operand of W = T K and U = T V are one 16-byte read
+    static constexpr int LDT = C + 4;
     static constexpr int LDTB = C + PADE;              // T converted to T-type
     // Q is only needed for A = tril(Q K^T), V only for U = T V: they share a
     // buffer (V waits in registers), which keeps bf16 chunks of 64 tokens at
@@ -38,8 +41,14 @@ struct UtLayout {
     static constexpr size_t offV = offQ;
     static constexpr size_t offG = offQ + sizeof(T) * C * LDQV;
     static constexpr size_t offT = offG + sizeof(float) * C * LDG;
-    static constexpr size_t offTb = offT + sizeof(float) * C * LDG;
-    static constexpr size_t offA = offTb + (is_bf16<T> ? sizeof(T) * C * LDTB : 0);
+    static constexpr size_t offTb = offT + sizeof(float) * C * LDT;
+    // A = tril(Q K^T) is staged in LDS (rows 16-byte aligned) and written out
+    // with 16-byte stores: bf16 in T's bf16 copy, which is only filled after
+    // A has been written out, fp32 in a buffer of its own at the same offset
+    static constexpr int LDAQ = is_bf16<T> ? LDTB : C + 4;
+    static constexpr size_t offAq = offTb;
+    static constexpr size_t offA = offTb + (is_bf16<T> ? sizeof(T) * C * LDTB
+                                                       : sizeof(float) * C * LDAQ);
     static constexpr size_t bytes = offA + sizeof(float) * C;
 };
 
@@ -136,10 +145,18 @@ __global__ __launch_bounds__((UtLayout<T, DK, DV, C>::NT)) void ut_kernel(
     float *sT = reinterpret_cast<float *>(smem + Lay::offT);
     T *sTb = reinterpret_cast<T *>(smem + Lay::offTb);
     float *sAl = reinterpret_cast<float *>(smem + Lay::offA);
+    T *sAq = reinterpret_cast<T *>(smem + Lay::offAq);
 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
     const bool packed = cu_chunks != nullptr;
     const int stride = gridDim.x;
+
+    // T's blocks above the diagonal are never written in the loop: zero them
+    // once (the bf16 copy of T reads them; the first chunk's barrier orders it)
+    for (int i = threadIdx.x; i < C * Lay::LDT; i += NT) sT[i] = 0.f;
+    // likewise the tiles of A's staging above the diagonal, which no chunk
+    // writes (in bf16 the copy of T rewrites them, with T's zeros)
+    for (int i = threadIdx.x; i < C * Lay::LDAQ; i += NT) sAq[i] = from_f32<T>(0.f);
 
     UtChunk<T, C> cur, nxt;
     long id = ut_next<T, C>(blockIdx.x, stride, total, L, nchunks, cu, cu_chunks, N, aqk, cur);
@@ -159,7 +176,6 @@ __global__ __launch_bounds__((UtLayout<T, DK, DV, C>::NT)) void ut_kernel(
 
         tk.store(sK, Lay::LDK, valid);
         tq.store(sQ, Lay::LDK, valid);
-        for (int i = threadIdx.x; i < C * Lay::LDG; i += NT) sT[i] = 0.f;
         float be = 0.f;   // alpha from beta: token `lane` of the chunk, wave 0
         if (alpha) {
             for (int i = threadIdx.x; i < C; i += NT) sAl[i] = (i < valid) ? alpha[tok0 + i] : 0.f;
@@ -172,17 +188,35 @@ __global__ __launch_bounds__((UtLayout<T, DK, DV, C>::NT)) void ut_kernel(
             tq.load(q + nxt.tok0 * DK, DK, nxt.valid);
         }
 
-        // Gram tiles G = K K^T, the MC (MC + 1) / 2 tiles on and below the
-        // diagonal (fp32 into LDS), dealt round-robin so every SIMD gets an
-        // even share of the MFMAs.
+        // The tiles on and below the diagonal: of G = K K^T (fp32 into LDS) and
+        // of A = tril(Q K^T) (staged in LDS).  The first phase takes every
+        // Gram tile and the first NA tiles of A, NA evening out the count
+        // over the four SIMDs (wave w runs on SIMD w mod 4).
         constexpr int NLOW = MC * (MC + 1) / 2;
-        for (int t = wv; t < NLOW; t += NW) {
+        constexpr int NA = (4 - NLOW % 4) % 4 < NLOW ? (4 - NLOW % 4) % 4 : NLOW;
+        auto a_tile = [&](int t) {
             int it, jt;
             lower_tile(t, it, jt);
-            const f32x4 acc = mm_lds<T, DK, false, false>(zero4(), sK, Lay::LDK, 16 * it, sK,
+            const f32x4 acc = mm_lds<T, DK, false, false>(zero4(), sQ, Lay::LDK, 16 * it, sK,
                                                           Lay::LDK, 16 * jt);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sG[(16 * it + 4 * g + r) * Lay::LDG + 16 * jt + l16] = acc[r];
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * it + 4 * g + r, col = 16 * jt + l16;
+                sAq[row * Lay::LDAQ + col] = from_f32<T>(col <= row ? acc[r] : 0.f);
+            }
+        };
+        for (int t = wv; t < NLOW + NA; t += NW) {
+            if (t < NLOW) {
+                int it, jt;
+                lower_tile(t, it, jt);
+                const f32x4 acc = mm_lds<T, DK, false, false>(zero4(), sK, Lay::LDK, 16 * it, sK,
+                                                              Lay::LDK, 16 * jt);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sG[(16 * it + 4 * g + r) * Lay::LDG + 16 * jt + l16] = acc[r];
+            } else {
+                a_tile(t - NLOW);
+            }
         }
         __syncthreads();
 
@@ -212,70 +246,75 @@ __global__ __launch_bounds__((UtLayout<T, DK, DV, C>::NT)) void ut_kernel(
                     t[i] = sAl[b0 + i] * acc;
                 }
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sT[(b0 + i) * Lay::LDG + b0 + j] = t[i];
+                for (int i = 0; i < 16; ++i) sT[(b0 + i) * Lay::LDT + b0 + j] = t[i];
             }
         } else {
-            // The other waves meanwhile: A = tril(Q K^T), written to global, the
-            // tiles on and below the diagonal first, then the zero tiles above it.
-            for (int t = wv - 1; t < MC * MC; t += NW - 1) {
-                int it, jt;
-                f32x4 acc = zero4();
-                if (t < NLOW) {
-                    lower_tile(t, it, jt);
-                    acc = mm_lds<T, DK, false, false>(zero4(), sQ, Lay::LDK, 16 * it, sK, Lay::LDK,
-                                                      16 * jt);
-                } else {
-                    lower_tile(t - NLOW, jt, it);   // tile (a, b), b <= a, names (b, a + 1)
-                    jt += 1;
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * it + 4 * g + r, col = 16 * jt + l16;
-                    if (!packed || row < valid)
-                        aq[row * C + col] = from_f32<T>(col <= row ? acc[r] : 0.f);
-                }
-            }
+            // The other waves meanwhile: the remaining tiles of A
+            for (int t = NA + wv - 1; t < NLOW; t += NW - 1) a_tile(t);
         }
         __syncthreads();
 
-        // Blocks below the diagonal, one block distance at a time (fp32 MFMA).
-        for (int dist = 1; dist < MC; ++dist) {
-            if (wv < MC - dist) {
-                const int bi = dist + wv, bj = wv;
-                f32x4 p = zero4();
-                for (int m = bj; m < bi; ++m) {
+        // Blocks below the diagonal (fp32 MFMA): wave j solves column block j
+        // from the top, T_ij = -T_ii sum_{m=j}^{i-1} G_im T_mj for i = j+1 ..
+        // MC-1.  A column needs only its own blocks (and the diagonal ones),
+        // so the columns proceed side by side with no barrier between block
+        // rows; within a wave, LDS accesses complete in order, so a block
+        // stored in one step is read back in the next.  The waves not needed
+        // for it write A out of its staging with 16-byte stores (every row;
+        // packed, the chunk's valid rows only).
+        if (wv < MC - 1) {
+            const int bj = wv;
+            for (int bi = bj + 1; bi < MC; ++bi) {
+                // every operand of this block's chain is read before its MFMAs
+                float av[MC > 1 ? MC - 1 : 1][4], bv[MC > 1 ? MC - 1 : 1][4];
+#pragma unroll
+                for (int mm = 0; mm < MC - 1; ++mm) {
+                    const int m = min(bj + mm, MC - 1);
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
-                        const float a = sG[(16 * bi + l16) * Lay::LDG + 16 * m + 4 * s + g];
-                        const float b = sT[(16 * m + 4 * s + g) * Lay::LDG + 16 * bj + l16];
-                        p = mma(a, b, p);
+                        av[mm][s] = sG[(16 * bi + l16) * Lay::LDG + 16 * m + 4 * s + g];
+                        bv[mm][s] = sT[(16 * m + 4 * s + g) * Lay::LDT + 16 * bj + l16];
                     }
                 }
+                const f32x4 tii =
+                    *reinterpret_cast<const f32x4 *>(sT + (16 * bi + l16) * Lay::LDT + 16 * bi + 4 * g);
+                f32x4 p = zero4();
+#pragma unroll
+                for (int mm = 0; mm < MC - 1; ++mm)
+                    if (bj + mm < bi)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) p = mma(av[mm][s], bv[mm][s], p);
                 f32x4 x = zero4();
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float a = sT[(16 * bi + l16) * Lay::LDG + 16 * bi + 4 * g + r];
-                    x = mma(a, p[r], x);
-                }
+                for (int r = 0; r < 4; ++r) x = mma(tii[r], p[r], x);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    sT[(16 * bi + 4 * g + r) * Lay::LDG + 16 * bj + l16] = -x[r];
+                    sT[(16 * bi + 4 * g + r) * Lay::LDT + 16 * bj + l16] = -x[r];
             }
-            __syncthreads();
+        } else {
+            constexpr int VA = 16 / (int)sizeof(T), VPR = C / VA, T0 = 64 * (MC - 1);
+            const int arows = packed ? valid : C;
+            for (int idx = (int)threadIdx.x - T0; idx < C * VPR; idx += NT - T0) {
+                const int row = idx / VPR, cv = idx - row * VPR;
+                if (row < arows)
+                    *reinterpret_cast<uint4 *>(aq + row * C + cv * VA) =
+                        *reinterpret_cast<const uint4 *>(sAq + row * Lay::LDAQ + cv * VA);
+            }
         }
+        __syncthreads();
 
         const T *sTop = nullptr;   // T as the MFMA A operand
         int ldTop = 0;
         if constexpr (BF) {
             for (int i = threadIdx.x; i < C * C; i += NT) {
                 const int r = i / C, cc = i - r * C;
-                sTb[r * Lay::LDTB + cc] = from_f32<T>(sT[r * Lay::LDG + cc]);
+                sTb[r * Lay::LDTB + cc] = from_f32<T>(sT[r * Lay::LDT + cc]);
             }
             sTop = sTb;
             ldTop = Lay::LDTB;
         } else {
             sTop = reinterpret_cast<const T *>(sT);
-            ldTop = Lay::LDG;
+            ldTop = Lay::LDT;
         }
         tv.store(sV, Lay::LDV, valid);   // A = tril(Q K^T) is done with Q
         __syncthreads();
