@@ -306,9 +306,11 @@ __global__ __launch_bounds__((UtLayout<T, DK, DV, C>::NT)) void ut_kernel(
         const T *sTop = nullptr;   // T as the MFMA A operand
         int ldTop = 0;
         if constexpr (BF) {
-            for (int i = threadIdx.x; i < C * C; i += NT) {
-                const int r = i / C, cc = i - r * C;
-                sTb[r * Lay::LDTB + cc] = from_f32<T>(sT[r * Lay::LDT + cc]);
+            // four elements per step: a 16-byte read, an 8-byte write
+            for (int i = threadIdx.x; i < C * C / 4; i += NT) {
+                const int r = i / (C / 4), cc = 4 * (i - r * (C / 4));
+                *reinterpret_cast<bf16x4 *>(sTb + r * Lay::LDTB + cc) =
+                    to_bf16x4(*reinterpret_cast<const f32x4 *>(sT + r * Lay::LDT + cc));
             }
             sTop = sTb;
             ldTop = Lay::LDTB;
