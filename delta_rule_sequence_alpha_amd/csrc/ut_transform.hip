@@ -323,42 +323,68 @@ __global__ __launch_bounds__((UtLayout<T, DK, DV, C>::NT)) void ut_kernel(
         if (nid < total) tv.load(v + nxt.tok0 * DV, DV, nxt.valid);
 
         // W = T K and U = T V (T lower triangular: k range of row tile mt is
-        // [0, 16mt+16)).  Each product is staged in LDS over the operand it no
-        // longer needs (W over K, U over V) and written with 16-byte stores.
+        // [0, 16mt+16)), each staged in LDS over the operand it no longer
+        // needs (W over K, U over V) and written with 16-byte stores.  fp32
+        // forms both in one phase and holds them in registers until every
+        // read of K and V is done; bf16, whose four-wave workgroups share a CU
+        // in pairs, keeps to its register budget with a phase for each.
         constexpr int NTK = DK / 16, NTV = DV / 16;
         constexpr int WPW = (MC * NTK + NW - 1) / NW, UPW = (MC * NTV + NW - 1) / NW;   // per wave
-        f32x4 acc[WPW > UPW ? WPW : UPW];
+        constexpr bool ONE_PHASE = !BF;
+        auto w_tiles = [&](f32x4 (&acc)[WPW]) {
 #pragma unroll
-        for (int j = 0; j < WPW; ++j) {
-            const int t = wv + NW * j, mt = t / NTK, nt = t - mt * NTK;
-            if (t < MC * NTK)
-                acc[j] = mm_lds<T, C, false, true>(zero4(), sTop, ldTop, 16 * mt, sK, Lay::LDK,
-                                                   16 * nt, 16 * mt + 16);
-        }
-        __syncthreads();   // every read of K is done
+            for (int j = 0; j < WPW; ++j) {
+                const int t = wv + NW * j, mt = t / NTK, nt = t - mt * NTK;
+                if (t < MC * NTK)
+                    acc[j] = mm_lds<T, C, false, true>(zero4(), sTop, ldTop, 16 * mt, sK,
+                                                       Lay::LDK, 16 * nt, 16 * mt + 16);
+            }
+        };
+        auto u_tiles = [&](f32x4 (&acc)[UPW]) {
 #pragma unroll
-        for (int j = 0; j < WPW; ++j) {
-            const int t = wv + NW * j, mt = t / NTK, nt = t - mt * NTK;
-            if (t < MC * NTK)
+            for (int j = 0; j < UPW; ++j) {
+                const int t = wv + NW * j, mt = t / NTV, nt = t - mt * NTV;
+                if (t < MC * NTV)
+                    acc[j] = mm_lds<T, C, false, true>(zero4(), sTop, ldTop, 16 * mt, sV,
+                                                       Lay::LDV, 16 * nt, 16 * mt + 16);
+            }
+        };
+        auto stage_w = [&](const f32x4 (&acc)[WPW]) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sK[(16 * mt + 4 * g + r) * Lay::LDK + 16 * nt + l16] = from_f32<T>(acc[j][r]);
-        }
+            for (int j = 0; j < WPW; ++j) {
+                const int t = wv + NW * j, mt = t / NTK, nt = t - mt * NTK;
+                if (t < MC * NTK)
 #pragma unroll
-        for (int j = 0; j < UPW; ++j) {
-            const int t = wv + NW * j, mt = t / NTV, nt = t - mt * NTV;
-            if (t < MC * NTV)
-                acc[j] = mm_lds<T, C, false, true>(zero4(), sTop, ldTop, 16 * mt, sV, Lay::LDV,
-                                                   16 * nt, 16 * mt + 16);
-        }
-        __syncthreads();   // every read of V is done; W is staged
+                    for (int r = 0; r < 4; ++r)
+                        sK[(16 * mt + 4 * g + r) * Lay::LDK + 16 * nt + l16] = from_f32<T>(acc[j][r]);
+            }
+        };
+        auto stage_u = [&](const f32x4 (&acc)[UPW]) {
 #pragma unroll
-        for (int j = 0; j < UPW; ++j) {
-            const int t = wv + NW * j, mt = t / NTV, nt = t - mt * NTV;
-            if (t < MC * NTV)
+            for (int j = 0; j < UPW; ++j) {
+                const int t = wv + NW * j, mt = t / NTV, nt = t - mt * NTV;
+                if (t < MC * NTV)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sV[(16 * mt + 4 * g + r) * Lay::LDV + 16 * nt + l16] = from_f32<T>(acc[j][r]);
+                    for (int r = 0; r < 4; ++r)
+                        sV[(16 * mt + 4 * g + r) * Lay::LDV + 16 * nt + l16] = from_f32<T>(acc[j][r]);
+            }
+        };
+        if constexpr (ONE_PHASE) {
+            f32x4 accW[WPW], accU[UPW];
+            w_tiles(accW);
+            u_tiles(accU);
+            __syncthreads();   // every read of K and V is done
+            stage_w(accW);
+            stage_u(accU);
+        } else {
+            f32x4 accW[WPW];
+            w_tiles(accW);
+            __syncthreads();   // every read of K is done
+            stage_w(accW);
+            f32x4 accU[UPW];
+            u_tiles(accU);
+            __syncthreads();   // every read of V is done; W is staged
+            stage_u(accU);
         }
         __syncthreads();
         store_rows_t<T, C, DK, NT>(w + tok0 * DK, DK, sK, Lay::LDK, valid);
