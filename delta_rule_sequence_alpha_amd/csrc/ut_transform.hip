@@ -256,40 +256,54 @@ __global__ __launch_bounds__((UtLayout<T, DK, DV, C>::NT)) void ut_kernel(
 
         // Blocks below the diagonal (fp32 MFMA): wave j solves column block j
         // from the top, T_ij = -T_ii sum_{m=j}^{i-1} G_im T_mj for i = j+1 ..
-        // MC-1.  A column needs only its own blocks (and the diagonal ones),
-        // so the columns proceed side by side with no barrier between block
-        // rows; within a wave, LDS accesses complete in order, so a block
-        // stored in one step is read back in the next.  The waves not needed
-        // for it write A out of its staging with 16-byte stores (every row;
+        // MC-1, right-looking: once T_mj is known, its term is added to the
+        // sums of every later block row at once, so those MFMAs are
+        // independent of each other and only T_ii (sum) waits on the chain.
+        // A solved block stays in registers in the accumulator layout (rows
+        // 4g + r of column l16), which is the B operand of the next products
+        // when a lane's four MFMAs take k = 4g + r.  A column needs only its
+        // own blocks and the diagonal ones, so the columns proceed side by
+        // side with no barrier between block rows.  The waves not needed for
+        // it write A out of its staging with 16-byte stores (every row;
         // packed, the chunk's valid rows only).
         if (wv < MC - 1) {
-            const int bj = wv;
-            for (int bi = bj + 1; bi < MC; ++bi) {
-                // every operand of this block's chain is read before its MFMAs
-                float av[MC > 1 ? MC - 1 : 1][4], bv[MC > 1 ? MC - 1 : 1][4];
+            constexpr int NB = MC > 1 ? MC - 1 : 1;
+            const int bj = wv, nb = MC - 1 - bj;   // blocks below the diagonal in column bj
+            // G_{bj+1+d, bj+m} (m <= d), row l16, k = 4g + r: every one read up front
+            float gv[NB][NB][4];
 #pragma unroll
-                for (int mm = 0; mm < MC - 1; ++mm) {
-                    const int m = min(bj + mm, MC - 1);
+            for (int d = 0; d < MC - 1; ++d)
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        av[mm][s] = sG[(16 * bi + l16) * Lay::LDG + 16 * m + 4 * s + g];
-                        bv[mm][s] = sT[(16 * m + 4 * s + g) * Lay::LDT + 16 * bj + l16];
-                    }
+                for (int m = 0; m <= d; ++m) {
+                    const int bi = min(bj + 1 + d, MC - 1), bm = min(bj + m, MC - 1);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        gv[d][m][r] = sG[(16 * bi + l16) * Lay::LDG + 16 * bm + 4 * g + r];
                 }
-                const f32x4 tii =
-                    *reinterpret_cast<const f32x4 *>(sT + (16 * bi + l16) * Lay::LDT + 16 * bi + 4 * g);
-                f32x4 p = zero4();
+            f32x4 tb, p[NB];
 #pragma unroll
-                for (int mm = 0; mm < MC - 1; ++mm)
-                    if (bj + mm < bi)
+            for (int r = 0; r < 4; ++r) tb[r] = sT[(16 * bj + 4 * g + r) * Lay::LDT + 16 * bj + l16];
 #pragma unroll
-                        for (int s = 0; s < 4; ++s) p = mma(av[mm][s], bv[mm][s], p);
+            for (int d = 0; d < MC - 1; ++d) p[d] = zero4();
+#pragma unroll
+            for (int m = 0; m < MC - 1; ++m) {
+                if (m >= nb) break;
+                // tb = T_{bj+m, bj}: its term in every later block row
+#pragma unroll
+                for (int d = m; d < MC - 1; ++d)
+                    if (d < nb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) p[d] = mma(gv[d][m][r], tb[r], p[d]);
+                // the sum of block row bn is complete: T_{bn, bj} = -T_{bn, bn} p
+                const int bn = bj + m + 1;
+                const f32x4 tnn = *reinterpret_cast<const f32x4 *>(
+                    sT + (16 * bn + l16) * Lay::LDT + 16 * bn + 4 * g);
                 f32x4 x = zero4();
 #pragma unroll
-                for (int r = 0; r < 4; ++r) x = mma(tii[r], p[r], x);
+                for (int r = 0; r < 4; ++r) x = mma(tnn[r], p[m][r], x);
+                tb = -x;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sT[(16 * bi + 4 * g + r) * Lay::LDT + 16 * bj + l16] = -x[r];
+                for (int r = 0; r < 4; ++r) sT[(16 * bn + 4 * g + r) * Lay::LDT + 16 * bj + l16] = tb[r];
             }
         } else {
             constexpr int VA = 16 / (int)sizeof(T), VPR = C / VA, T0 = 64 * (MC - 1);
