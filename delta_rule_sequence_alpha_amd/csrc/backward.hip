@@ -417,44 +417,57 @@ __global__ __launch_bounds__(512) void grad_kernel(
     // lane group g solving block g, lane j its column j
     if (wv == 0 && g < MC) diag_block_solve<BF>(sGam, sAl, sN, sNb, LDC, LDN, 16 * g, l16);
     lds_barrier();
-    // blocks below: N_IJ = -N_II D_I sum_{M=J}^{I-1} Gamma_IM N_MJ, by block distance
-    for (int dist = 1; dist < MC; ++dist) {
-        if (wv < MC - dist) {
-            const int bi = dist + wv, bj = wv;
-            f32x4 p = zero4();
-            for (int m = bj; m < bi; ++m) {
+    // blocks below: N_IJ = -N_II D_I sum_{M=J}^{I-1} Gamma_IM N_MJ.  Wave J
+    // solves column block J right-looking: once N_MJ is known its term goes
+    // into the sums of every later block row at once (independent MFMAs), and
+    // it stays in registers in the accumulator layout (rows 4g + r of column
+    // l16), the B operand of those products when a lane's four MFMAs take
+    // k = 4g + r.  A column needs only its own and the diagonal blocks, so the
+    // columns proceed side by side with one barrier at the end; every wave
+    // then stages V and dE (S's staging in B1 was read before the last barrier).
+    if (wv < MC - 1) {
+        constexpr int NB = MC > 1 ? MC - 1 : 1;
+        const int bj = wv, nb = MC - 1 - bj;   // blocks below the diagonal in column bj
+        float gv[NB][NB][4];   // Gamma_{bj+1+d, bj+m}, m <= d: row l16, k = 4g + r
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const float a = sGam[(16 * bi + l16) * LDC + 16 * m + 4 * s + g];
-                    const float b = sN[(16 * m + 4 * s + g) * LDC + 16 * bj + l16];
-                    p = mma(a, b, p);
-                }
+        for (int d = 0; d < MC - 1; ++d)
+#pragma unroll
+            for (int m = 0; m <= d; ++m) {
+                const int bi = min(bj + 1 + d, MC - 1), bm = min(bj + m, MC - 1);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gv[d][m][r] = sGam[(16 * bi + l16) * LDC + 16 * bm + 4 * g + r];
             }
+        f32x4 nb_reg, p[NB];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] *= sAl[16 * bi + 4 * g + r];
+        for (int r = 0; r < 4; ++r) nb_reg[r] = sN[(16 * bj + 4 * g + r) * LDC + 16 * bj + l16];
+#pragma unroll
+        for (int d = 0; d < MC - 1; ++d) p[d] = zero4();
+#pragma unroll
+        for (int m = 0; m < MC - 1; ++m) {
+            if (m >= nb) break;
+#pragma unroll
+            for (int d = m; d < MC - 1; ++d)
+                if (d < nb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) p[d] = mma(gv[d][m][r], nb_reg[r], p[d]);
+            const int bn = bj + m + 1;   // block row bn's sum is complete
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[m][r] *= sAl[16 * bn + 4 * g + r];
+            const f32x4 nnn = *reinterpret_cast<const f32x4 *>(sN + (16 * bn + l16) * LDC + 16 * bn + 4 * g);
             f32x4 x = zero4();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float a = sN[(16 * bi + l16) * LDC + 16 * bi + 4 * g + r];
-                x = mma(a, p[r], x);
-            }
+            for (int r = 0; r < 4; ++r) x = mma(nnn[r], p[m][r], x);
+            nb_reg = -x;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                sN[(16 * bi + 4 * g + r) * LDC + 16 * bj + l16] = -x[r];
-                if constexpr (BF) sNb[(16 * bi + 4 * g + r) * LDN + 16 * bj + l16] = static_cast<__bf16>(-x[r]);
+                sN[(16 * bn + 4 * g + r) * LDC + 16 * bj + l16] = nb_reg[r];
+                if constexpr (BF) sNb[(16 * bn + 4 * g + r) * LDN + 16 * bj + l16] = static_cast<__bf16>(nb_reg[r]);
             }
         }
-        if (dist == MC - 1) {   // V and dE to LDS, for the first phase that reads them
-            rV.store(sB1, LDV, valid);
-            rE.store(sB2, LDV, valid);
-        }
-        lds_barrier();
     }
-    if constexpr (MC == 1) {
-        rV.store(sB1, LDV, valid);
-        rE.store(sB2, LDV, valid);
-        lds_barrier();
-    }
+    rV.store(sB1, LDV, valid);   // V and dE to LDS, for the first phase that reads them
+    rE.store(sB2, LDV, valid);
+    lds_barrier();
 
     // ---- per d_v column tile (wave wv owns columns 16wv .. 16wv+15) ----------
     f32x4 E[MC], dX[MC];
