@@ -266,6 +266,7 @@ __global__ __launch_bounds__((UtLayout<T, DK, DV, C>::NT)) void ut_kernel(
         // side with no barrier between block rows.  The waves not needed for
         // it write A out of its staging with 16-byte stores (every row;
         // packed, the chunk's valid rows only).
+        tv.store(sV, Lay::LDV, valid);   // A = tril(Q K^T) is done with Q
         if (wv < MC - 1) {
             constexpr int NB = MC > 1 ? MC - 1 : 1;
             const int bj = wv, nb = MC - 1 - bj;   // blocks below the diagonal in column bj
@@ -328,12 +329,13 @@ __global__ __launch_bounds__((UtLayout<T, DK, DV, C>::NT)) void ut_kernel(
             }
             sTop = sTb;
             ldTop = Lay::LDTB;
+            __syncthreads();
         } else {
             sTop = reinterpret_cast<const T *>(sT);
             ldTop = Lay::LDT;
         }
-        tv.store(sV, Lay::LDV, valid);   // A = tril(Q K^T) is done with Q
-        __syncthreads();
+        // the next V tile flies during the products (the barrier above would
+        // have waited for it)
         if (nid < total) tv.load(v + nxt.tok0 * DV, DV, nxt.valid);
 
         // W = T K and U = T V (T lower triangular: k range of row tile mt is
