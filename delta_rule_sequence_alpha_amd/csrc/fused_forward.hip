@@ -112,7 +112,8 @@ struct FusedLayout {
     static constexpr size_t pA = pG + 1024 * g_slot(MC, 0);    // -tril(Q K^T)
     static constexpr size_t pT = pA + 1024 * a_slot(MC, 0);    // T_ii: [i][column][row] bf16
     static constexpr size_t prepBytes = pT + 512 * MC;
-    // T-wave scratch, used within one interval: fp32 G_ii [16i + col][row]
+    // fp32 G_ii [16i + col][row] of one chunk (double-buffered): formed by the
+    // K wave at the end of one interval, read by the T wave in the next
     static constexpr size_t kGt = 0;
     static constexpr size_t kBytes = kGt + 4 * 16 * LDD * MC;
     // output staging tile (double-buffered), transposed: [column][token]
@@ -120,7 +121,7 @@ struct FusedLayout {
     static constexpr size_t offIn = 0;
     static constexpr size_t offPrep = NB * inBytes;
     static constexpr size_t offK = offPrep + 2 * prepBytes;
-    static constexpr size_t offO = (offK + kBytes + 15) / 16 * 16;
+    static constexpr size_t offO = (offK + 2 * kBytes + 15) / 16 * 16;
     static constexpr size_t bytes = offO + 2 * oBytes;
 };
 
@@ -155,13 +156,22 @@ __device__ __forceinline__ int srow(int t, int i)
     return 32 * (t >> 1) + 8 * (i >> 2) + 4 * (t & 1) + (i & 3);
 }
 
+// LDS address of a generic pointer into this workgroup's LDS.  The low 32
+// bits of such a pointer are its LDS offset, so this is one truncation; the
+// language's generic-to-local conversion would add a null test (a compare and
+// select in front of every direct-to-LDS load's M0 setup).
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(3))) T *lds_addr(const void *p)
+{
+    return (__attribute__((address_space(3))) T *)(unsigned)reinterpret_cast<unsigned long>(p);
+}
+
 // transposing LDS read: within each 16-lane group, lane l receives element
 // l%4 of the 4 x 16-bit values addressed by lane 4e + l/4, for e = 0..3
 __device__ __forceinline__ bf16x4 ds_read_tr(const bf *p)
 {
     typedef short v4i16 __attribute__((ext_vector_type(4)));
-    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16 *)(p));
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_addr<v4i16>(p));
     return __builtin_bit_cast(bf16x4, r);
 }
 
@@ -223,7 +233,7 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, bf *lds, F go
         const int e = 512 * j + 8 * lane;
         if (BYTES % 1024 == 0 || 2 * e < BYTES)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (__attribute__((address_space(3))) void *)(lds + 512 * j), 16, goff(e), 0, 0, 0);
+                r, lds_addr<void>(lds + 512 * j), 16, goff(e), 0, 0, 0);
     }
 }
 
@@ -247,7 +257,7 @@ __device__ __forceinline__ void dma_chunk(int role, char *in, const bf *gq, cons
         const int lane = threadIdx.x & 63;
         if (lane < C)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc(gb, valid * 4), (__attribute__((address_space(3))) void *)(in + Lay::bBeta), 4,
+                rsrc(gb, valid * 4), lds_addr<void>(in + Lay::bBeta), 4,
                 4 * lane, 0, 0, 0);
     } else if (role == Q_WAVE) {
         dma_tile<2 * C * DK>(rsrc(gq, valid * DK * 2), reinterpret_cast<bf *>(in + Lay::bQ), sw_off);
@@ -468,7 +478,7 @@ __device__ __forceinline__ void subst(float (&acc)[16], const float (&gc)[16], f
 // bf16 tile (two 16-byte writes), from which the scan takes its operand
 // fragment with one transposing read.
 template <int DK, int DV, int C, int NS>
-__device__ __forceinline__ void prep_diag(const char *in, char *prep, char *ks, int euler)
+__device__ __forceinline__ void prep_diag(const char *in, char *prep, const char *ks, int euler)
 {
     using Lay = FusedLayout<DK, DV, C, NS>;
     constexpr int MC = Lay::MC;
@@ -516,7 +526,7 @@ struct PrepCtx {
     int euler;
     __device__ __forceinline__ char *inb(int c) const { return smem + Lay::offIn + (c % Lay::NB) * Lay::inBytes; }
     __device__ __forceinline__ char *prb(int c) const { return smem + Lay::offPrep + (c & 1) * Lay::prepBytes; }
-    __device__ __forceinline__ char *ks() const { return smem + Lay::offK; }
+    __device__ __forceinline__ char *ks(int c) const { return smem + Lay::offK + (c & 1) * Lay::kBytes; }
     __device__ __forceinline__ bf *obuf(int i) const
     {
         return reinterpret_cast<bf *>(smem + Lay::offO + i * Lay::oBytes);
@@ -549,16 +559,19 @@ __device__ __attribute__((always_inline)) inline void prep_store_out(const PrepC
 }
 
 // One prep interval: start the loads of chunk n + 1 (into `dma`), write the
-// output of chunk out_chunk (K wave, if >= 0; staged in `os`) and prepare
+// output of chunk out_chunk (T wave, if >= 0; staged in `os`) and prepare
 // chunk n (if < nchunks) from its inputs in `in` into `pr`; then wait for
 // this wave's loads, so that they are complete once the interval's closing
-// barrier has been passed.  The buffers are distinct, and saying so
-// (__restrict__) lets the compiler see that the LDS reads here need not wait
-// for the direct-to-LDS loads in flight.
+// barrier has been passed.  The K wave forms the diagonal Gram tiles of
+// chunk n + 1 into `ks1` once its loads of that chunk have arrived; the T wave
+// takes those of chunk n from `ks0`, formed in the previous interval.  The
+// buffers are distinct, and saying so (__restrict__) lets the compiler see
+// that the LDS reads here need not wait for the direct-to-LDS loads in flight.
 template <int DK, int DV, int C, int NS>
 __device__ __attribute__((always_inline)) inline void prep_interval(
     const PrepCtx<DK, DV, C, NS> &x, int n, int out_chunk, char *__restrict__ dma,
-    char *__restrict__ in, char *__restrict__ pr, char *__restrict__ ks, bf *__restrict__ os)
+    char *__restrict__ in, char *__restrict__ pr, char *__restrict__ ks0, char *__restrict__ ks1,
+    bf *__restrict__ os)
 {
     if (n + 1 < x.nchunks) {
         const long off = (long)(n + 1) * C;
@@ -566,16 +579,18 @@ __device__ __attribute__((always_inline)) inline void prep_interval(
                                  x.bb + off, x.valid_of(n + 1));
     }
     if (x.role == K_WAVE) {
-        if (out_chunk >= 0) prep_store_out(x, out_chunk, os);
         __builtin_amdgcn_s_sleep(kPrepPause);
-        if (n < x.nchunks) prep_gram<DK, DV, C, NS, false>(in, pr, ks);
+        if (n < x.nchunks) prep_gram<DK, DV, C, NS, false>(in, pr, ks1);
+        if (n + 1 < x.nchunks) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            prep_gram<DK, DV, C, NS, true>(dma, pr, ks1);
+        }
     } else if (x.role == Q_WAVE) {
         __builtin_amdgcn_s_sleep(kPrepPause);
         if (n < x.nchunks) prep_qk<DK, DV, C, NS>(in, pr);
-    } else if (n < x.nchunks) {
-        prep_gram<DK, DV, C, NS, true>(in, pr, ks);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        prep_diag<DK, DV, C, NS>(in, pr, ks, x.euler);
+    } else {
+        if (out_chunk >= 0) prep_store_out(x, out_chunk, os);
+        if (n < x.nchunks) prep_diag<DK, DV, C, NS>(in, pr, ks0, x.euler);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -584,7 +599,7 @@ template <int DK, int DV, int C, int NS>
 __device__ __attribute__((always_inline)) inline void prep_step(const PrepCtx<DK, DV, C, NS> &x,
                                                                 int n, int out_chunk)
 {
-    prep_interval(x, n, out_chunk, x.inb(n + 1), x.inb(n), x.prb(n), x.ks(),
+    prep_interval(x, n, out_chunk, x.inb(n + 1), x.inb(n), x.prb(n), x.ks(n), x.ks(n + 1),
                   x.obuf(out_chunk & 1));
 }
 
@@ -624,7 +639,11 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
         aq[0][mt] = a_row<DK>(sQ, mt, 0);
     }
     // reads of k-block s+1 are issued before the MFMAs of block s and kept
-    // there, so each MFMA group covers the next group's LDS latency
+    // there, so each MFMA group covers the next group's LDS latency; the last
+    // block's MFMAs cover the reads of the substitution's operands (-G below
+    // the diagonal and T_ii), which do not depend on the state
+    bf16x8 ga[MC * NKC];
+    bf16x4 ta[MC];
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
         if (s + 1 < NKS) {
@@ -633,6 +652,18 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
                 ak[(s + 1) & 1][mt] = a_row<DK>(sK, mt, s + 1);
                 aq[(s + 1) & 1][mt] = a_row<DK>(sQ, mt, s + 1);
             }
+        } else {
+#pragma unroll
+            for (int i = 1; i < MC; ++i)
+#pragma unroll
+                for (int s2 = 0; 2 * s2 < i; ++s2) {
+                    if (2 * s2 + 1 < i) ga[i * NKC + s2] = *reinterpret_cast<const bf16x8 *>(sG + gfrag(i, 2 * s2));
+                    else ga[i * NKC + s2] = cat(*reinterpret_cast<const bf16x4 *>(sG + gfrag(i, 2 * s2)), zb4());
+                }
+            // T_ii, stored row j = column j of the block: one transposing read
+            // gives lane (l16, g) T_ii[l16][4g + r], the A fragment
+#pragma unroll
+            for (int i = 0; i < MC; ++i) ta[i] = ds_read_tr(sT + 256 * i + (4 * g + (l16 >> 2)) * 16 + 4 * (l16 & 3));
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -649,19 +680,21 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
     // shape (k = 32; a lone block is padded with zeros): the accumulator is
     // forwarded between dependent MFMAs of one shape only.  T_ii y starts
     // from zero and uses k = 16.
-    bf16x8 ga[MC * NKC];
+    // Reads for the products after the chain (tril(Q K^T) fragments, the
+    // first group of K^T operands), issued now so that the chain's latency
+    // covers them.
+    bf16x8 aa[MC * NKC];
 #pragma unroll
-    for (int i = 1; i < MC; ++i)
+    for (int s = 0; s < NKC; ++s)
 #pragma unroll
-        for (int s = 0; 2 * s < i; ++s) {
-            if (2 * s + 1 < i) ga[i * NKC + s] = *reinterpret_cast<const bf16x8 *>(sG + gfrag(i, 2 * s));
-            else ga[i * NKC + s] = cat(*reinterpret_cast<const bf16x4 *>(sG + gfrag(i, 2 * s)), zb4());
+        for (int mt = 0; mt < MC; ++mt) {
+            if (2 * s + 1 <= mt) aa[mt * NKC + s] = *reinterpret_cast<const bf16x8 *>(sA + afrag(mt, 2 * s));
+            else if (2 * s == mt) aa[mt * NKC + s] = cat(*reinterpret_cast<const bf16x4 *>(sA + afrag(mt, 2 * s)), zb4());
         }
-    // T_ii, stored row j = column j of the block: one transposing read gives
-    // lane (l16, g) T_ii[l16][4g + r], the A fragment
-    bf16x4 ta[MC];
+    constexpr int KG = MK / 2 > 0 ? MK / 2 : 1;   // K^T row tiles per read group
+    bf16x8 akt[2][KG];
 #pragma unroll
-    for (int i = 0; i < MC; ++i) ta[i] = ds_read_tr(sT + 256 * i + (4 * g + (l16 >> 2)) * 16 + 4 * (l16 & 3));
+    for (int j = 0; j < KG; ++j) akt[0][j] = a_kt<DK, MC>(sK, j, 0);
     f32x4 E[MC];
     bf16x4 eb[MC];
 #pragma unroll
@@ -676,22 +709,10 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // On += (-tril(Q K^T)) E;  S += K^T E   (operands read a group ahead)
+    // On += (-tril(Q K^T)) E;  S += K^T E   (K^T operands read a group ahead)
     bf16x8 bE[NKC];
 #pragma unroll
     for (int s = 0; s < NKC; ++s) bE[s] = cat(eb[2 * s], 2 * s + 1 < MC ? eb[2 * s + 1] : zb4());
-    bf16x8 aa[MC * NKC];
-#pragma unroll
-    for (int s = 0; s < NKC; ++s)
-#pragma unroll
-        for (int mt = 0; mt < MC; ++mt) {
-            if (2 * s + 1 <= mt) aa[mt * NKC + s] = *reinterpret_cast<const bf16x8 *>(sA + afrag(mt, 2 * s));
-            else if (2 * s == mt) aa[mt * NKC + s] = cat(*reinterpret_cast<const bf16x4 *>(sA + afrag(mt, 2 * s)), zb4());
-        }
-    constexpr int KG = MK / 2 > 0 ? MK / 2 : 1;   // K^T row tiles per read group
-    bf16x8 akt[2][KG];
-#pragma unroll
-    for (int j = 0; j < KG; ++j) akt[0][j] = a_kt<DK, MC>(sK, j, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < NKC; ++s)
@@ -822,6 +843,7 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
                                        wv - NS, euler};
         dma_chunk<DK, DV, C, NS>(x.role, x.inb(0), x.qb, x.kb, x.vb, x.bb, x.valid_of(0));
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (x.role == K_WAVE && x.nchunks > 0) prep_gram<DK, DV, C, NS, true>(x.inb(0), x.prb(0), x.ks(0));
         __syncthreads();                // prologue: chunk 0 loaded
         prep_step(x, 0, -1);            // prologue: chunk 1 loading, chunk 0 prepared
         __syncthreads();
@@ -832,7 +854,7 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
             __syncthreads();
         }
         __syncthreads();
-        if (x.role == K_WAVE && nchunks > 0) prep_store_out(x, nchunks - 1, x.obuf((nchunks - 1) & 1));
+        if (x.role == T_WAVE && nchunks > 0) prep_store_out(x, nchunks - 1, x.obuf((nchunks - 1) & 1));
     }
 }
 
@@ -863,8 +885,9 @@ hipError_t launch_fused_ns(const void *q, const void *k, const void *v, const fl
                            int H, int ns, bool euler, hipStream_t st)
 {
     if (ns <= 0) ns = DV >= 32 ? 2 : 1;
-    if (ns >= 2 && DV >= 32)
-        return launch_fused<DK, DV, C, 2>(q, k, v, beta, S0, o, SL, BH, L, cu, H, euler, st);
+    if constexpr (DV >= 32) {   // two scan waves need at least 32 state columns
+        if (ns >= 2) return launch_fused<DK, DV, C, 2>(q, k, v, beta, S0, o, SL, BH, L, cu, H, euler, st);
+    }
     return launch_fused<DK, DV, C, 1>(q, k, v, beta, S0, o, SL, BH, L, cu, H, euler, st);
 }
 
