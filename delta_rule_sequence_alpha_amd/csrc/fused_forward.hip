@@ -163,7 +163,7 @@ __device__ __forceinline__ int srow(int t, int i)
 template <typename T>
 __device__ __forceinline__ __attribute__((address_space(3))) T *lds_addr(const void *p)
 {
-    return (__attribute__((address_space(3))) T *)(unsigned)reinterpret_cast<unsigned long>(p);
+    return (__attribute__((address_space(3))) T *)(size_t)(unsigned)reinterpret_cast<size_t>(p);
 }
 
 // transposing LDS read: within each 16-lane group, lane l receives element
@@ -238,7 +238,7 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, bf *lds, F go
 }
 
 // The calling prep wave's share of chunk n's inputs, into input buffer `in`:
-// the K wave K and beta, the Q wave Q and the V tile.  The resources end at
+// the K wave K and beta, the T wave Q and the V tile.  The resources end at
 // the chunk's last valid row, so the rows past it arrive as zeros.
 template <int DK, int DV, int C, int NS>
 __device__ __forceinline__ void dma_chunk(int role, char *in, const bf *gq, const bf *gk,
@@ -259,7 +259,7 @@ __device__ __forceinline__ void dma_chunk(int role, char *in, const bf *gq, cons
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc(gb, valid * 4), lds_addr<void>(in + Lay::bBeta), 4,
                 4 * lane, 0, 0, 0);
-    } else if (role == Q_WAVE) {
+    } else if (role == T_WAVE) {
         dma_tile<2 * C * DK>(rsrc(gq, valid * DK * 2), reinterpret_cast<bf *>(in + Lay::bQ), sw_off);
         dma_tile<2 * C * TV>(rsrc(gv, ((valid - 1) * DV + TV) * 2), reinterpret_cast<bf *>(in + Lay::bV),
                              [](int e) { return 2 * ((e / TV) * DV + e % TV); });
@@ -333,6 +333,8 @@ __device__ __forceinline__ void prep_gram(const char *in, char *prep, char *ks)
 
 // Q wave: tril(Q K^T), negated.  Tile (it, jt) = K_jt Q_it^T, accumulator
 // (Q K^T)[16it + l16][16jt + 4g + r] (A fragment order); diagonal tiles masked.
+// Then, from the K rows already in registers, the Gram tiles below the
+// diagonal, negated in bf16 (the diagonal ones are the K wave's).
 template <int DK, int DV, int C, int NS>
 __device__ __forceinline__ void prep_qk(const char *in, char *prep)
 {
@@ -376,6 +378,29 @@ __device__ __forceinline__ void prep_qk(const char *in, char *prep)
             }
             *reinterpret_cast<bf16x4 *>(sA + afrag(it, jt)) = to_bf16x4(a);
         }
+    // the Gram tiles below the diagonal from the same K rows (see prep_gram)
+    constexpr int NG = MC * (MC - 1) / 2;
+    if constexpr (NG > 0) {
+        bf *sG = reinterpret_cast<bf *>(prep + Lay::pG);
+        f32x4 gacc[NG];
+#pragma unroll
+        for (int u = 0; u < NG; ++u) gacc[u] = zero4();
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            int u = 0;
+#pragma unroll
+            for (int it = 1; it < MC; ++it)
+#pragma unroll
+                for (int jt = 0; jt < it; ++jt, ++u) gacc[u] = mma(kb[jt][s], kb[it][s], gacc[u]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        int u = 0;
+#pragma unroll
+        for (int it = 1; it < MC; ++it)
+#pragma unroll
+            for (int jt = 0; jt < it; ++jt, ++u)
+                *reinterpret_cast<bf16x4 *>(sG + gfrag(it, jt)) = to_bf16x4(neg(gacc[u]));
+    }
 }
 
 // Row-broadcast helpers for the T_ii substitution: within each 16-lane row
@@ -579,17 +604,14 @@ __device__ __attribute__((always_inline)) inline void prep_interval(
                                  x.bb + off, x.valid_of(n + 1));
     }
     if (x.role == K_WAVE) {
-        __builtin_amdgcn_s_sleep(kPrepPause);
-        if (n < x.nchunks) prep_gram<DK, DV, C, NS, false>(in, pr, ks1);
+        if (out_chunk >= 0) prep_store_out(x, out_chunk, os);
         if (n + 1 < x.nchunks) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             prep_gram<DK, DV, C, NS, true>(dma, pr, ks1);
         }
     } else if (x.role == Q_WAVE) {
-        __builtin_amdgcn_s_sleep(kPrepPause);
         if (n < x.nchunks) prep_qk<DK, DV, C, NS>(in, pr);
     } else {
-        if (out_chunk >= 0) prep_store_out(x, out_chunk, os);
         if (n < x.nchunks) prep_diag<DK, DV, C, NS>(in, pr, ks0, x.euler);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -854,7 +876,7 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
             __syncthreads();
         }
         __syncthreads();
-        if (x.role == T_WAVE && nchunks > 0) prep_store_out(x, nchunks - 1, x.obuf((nchunks - 1) & 1));
+        if (x.role == K_WAVE && nchunks > 0) prep_store_out(x, nchunks - 1, x.obuf((nchunks - 1) & 1));
     }
 }
 
