@@ -682,8 +682,8 @@ def pmc_summary(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="lm1.3b-bf16", choices=sorted(wl.FORWARD_WORKLOADS))
     ap.add_argument("--path", default="auto", choices=["auto", "staged", "fused", "segmented"])
     ap.add_argument("--no-cpu-baseline", action="store_true")

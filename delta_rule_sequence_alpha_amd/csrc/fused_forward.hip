@@ -19,12 +19,14 @@
 //    K S, Q S, the block substitution for E, tril(Q K^T) E, K^T E.
 //  * prep wave NS ("K wave"): starts the direct-to-LDS loads of K and beta
 //    two chunks ahead, writes the previous chunk's output from an LDS staging
-//    tile to HBM with full-width stores, and forms the Gram tiles below the
-//    diagonal one chunk ahead.
-//  * prep wave NS+1 ("Q wave"): starts the loads of Q and the V tile two
-//    chunks ahead and forms tril(Q K^T) one chunk ahead.
-//  * prep wave NS+2 ("T wave"), one chunk ahead: the diagonal Gram tiles,
-//    lambda, alpha and every T_ii (one 16-lane group per diagonal block).
+//    tile to HBM with full-width stores, and, once its loads have landed,
+//    forms the diagonal Gram tiles of the chunk two ahead (fp32 scratch).
+//  * prep wave NS+1 ("Q wave"), one chunk ahead: tril(Q K^T) and, from the
+//    same K rows, the Gram tiles below the diagonal.
+//  * prep wave NS+2 ("T wave"): starts the loads of Q and the V tile two
+//    chunks ahead, then, one chunk ahead, lambda, alpha and every T_ii from
+//    the diagonal Gram tiles formed in the previous interval (one 16-lane
+//    group per diagonal block).
 // Inputs rotate through three LDS buffers (chunk c in scan, c+1 in prep, c+2
 // arriving).  All waves meet at one workgroup barrier per chunk, before which
 // each prep wave has waited for its own loads; nothing else synchronises.
@@ -61,13 +63,6 @@ constexpr int NP = 3;                 // prep waves per workgroup
 enum Role { K_WAVE = 0, Q_WAVE = 1, T_WAVE = 2 };   // prep wave NS + role
 constexpr int kRsrcWord3 = 0x00020000;   // raw (unswizzled, stride 0) buffer resource
 constexpr int kStoreNT = 2;              // cache policy of the output stores: non-temporal
-// Every wave starts its interval with LDS reads, and the LDS is the resource
-// they all share.  The K and Q waves, which finish their interval early,
-// pause this long (s_sleep units of 64 cycles) before their LDS-heavy
-// products, so the first reads of the T wave and the scan waves, which
-// finish last, are served first.  Measured on the 1.3B-shaped layer: 2-3%
-// per call, flat from 4 to 8 units on both waves; less with one wave or 2 units.
-constexpr int kPrepPause = 4;
 
 // Buffer resource over the first `bytes` bytes at p: loads past the end
 // return zeros, stores past the end are dropped.
@@ -277,58 +272,35 @@ __device__ __forceinline__ int afrag(int i, int m)
     return (a_slot(i, m >> 1) * 64 + (threadIdx.x & 63)) * 8 + (m & 1) * 4;
 }
 
-// Gram tiles.  Tile (it, jt) is computed as K_jt K_it^T, whose accumulator
-// is G[16it + l16][16jt + 4g + r]: the A fragment of G_{it,jt}.  DIAG: the
-// diagonal tiles, to fp32 scratch (lambda is their diagonal; T wave); else
-// the tiles below the diagonal, negated in bf16 (K wave).  All operands are
-// read first (k-block by k-block), then the MFMAs of every tile run k-block
-// by k-block.
-template <int DK, int DV, int C, int NS, bool DIAG>
-__device__ __forceinline__ void prep_gram(const char *in, char *prep, char *ks)
+// K wave: the diagonal Gram tiles of one chunk, to fp32 scratch (lambda is
+// their diagonal).  Tile it is computed as K_it K_it^T, whose accumulator is
+// G[16it + l16][16it + 4g + r].  All operands are read first (k-block by
+// k-block), then the MFMAs of every tile run k-block by k-block.
+template <int DK, int DV, int C, int NS>
+__device__ __forceinline__ void prep_gram_diag(const char *in, char *ks)
 {
     using Lay = FusedLayout<DK, DV, C, NS>;
     constexpr int MC = Lay::MC, NKS = (DK + 31) / 32;
-    constexpr int NT = DIAG ? MC : MC * (MC - 1) / 2;
     const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
     const bf *sK = reinterpret_cast<const bf *>(in + Lay::bK);
-    bf *sG = reinterpret_cast<bf *>(prep + Lay::pG);
     float *sGt = reinterpret_cast<float *>(ks + Lay::kGt);
-    if constexpr (NT > 0) {
-        bf16x8 kb[NKS][MC];
+    bf16x8 kb[NKS][MC];
 #pragma unroll
-        for (int s = 0; s < NKS; ++s)
+    for (int s = 0; s < NKS; ++s)
 #pragma unroll
-            for (int b = 0; b < MC; ++b) kb[s][b] = a_nat<DK>(sK, 16 * b + l16, s);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x4 acc[NT];
+        for (int b = 0; b < MC; ++b) kb[s][b] = a_nat<DK>(sK, 16 * b + l16, s);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc[MC];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = zero4();
+    for (int t = 0; t < MC; ++t) acc[t] = zero4();
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-            int t = 0;
+    for (int s = 0; s < NKS; ++s)
 #pragma unroll
-            for (int it = 0; it < MC; ++it)
+        for (int it = 0; it < MC; ++it) acc[it] = mma(kb[s][it], kb[s][it], acc[it]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int jt = 0; jt <= it; ++jt) {
-                    if ((it == jt) != DIAG) continue;
-                    acc[t] = mma(kb[s][jt], kb[s][it], acc[t]);
-                    ++t;
-                }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        int t = 0;
-#pragma unroll
-        for (int it = 0; it < MC; ++it)
-#pragma unroll
-            for (int jt = 0; jt <= it; ++jt) {
-                if ((it == jt) != DIAG) continue;
-                if (DIAG)
-                    *reinterpret_cast<f32x4 *>(sGt + (16 * it + l16) * Lay::LDD + 4 * g) = acc[t];
-                else
-                    *reinterpret_cast<bf16x4 *>(sG + gfrag(it, jt)) = to_bf16x4(neg(acc[t]));
-                ++t;
-            }
-    }
+    for (int it = 0; it < MC; ++it)
+        *reinterpret_cast<f32x4 *>(sGt + (16 * it + l16) * Lay::LDD + 4 * g) = acc[it];
 }
 
 // Q wave: tril(Q K^T), negated.  Tile (it, jt) = K_jt Q_it^T, accumulator
@@ -378,7 +350,9 @@ __device__ __forceinline__ void prep_qk(const char *in, char *prep)
             }
             *reinterpret_cast<bf16x4 *>(sA + afrag(it, jt)) = to_bf16x4(a);
         }
-    // the Gram tiles below the diagonal from the same K rows (see prep_gram)
+    // the Gram tiles below the diagonal from the same K rows: tile (it, jt)
+    // is computed as K_jt K_it^T, whose accumulator is the A fragment of
+    // G_{it,jt}
     constexpr int NG = MC * (MC - 1) / 2;
     if constexpr (NG > 0) {
         bf *sG = reinterpret_cast<bf *>(prep + Lay::pG);
@@ -607,7 +581,7 @@ __device__ __attribute__((always_inline)) inline void prep_interval(
         if (out_chunk >= 0) prep_store_out(x, out_chunk, os);
         if (n + 1 < x.nchunks) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            prep_gram<DK, DV, C, NS, true>(dma, pr, ks1);
+            prep_gram_diag<DK, DV, C, NS>(dma, ks1);
         }
     } else if (x.role == Q_WAVE) {
         if (n < x.nchunks) prep_qk<DK, DV, C, NS>(in, pr);
@@ -865,7 +839,7 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
                                        wv - NS, euler};
         dma_chunk<DK, DV, C, NS>(x.role, x.inb(0), x.qb, x.kb, x.vb, x.bb, x.valid_of(0));
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (x.role == K_WAVE && x.nchunks > 0) prep_gram<DK, DV, C, NS, true>(x.inb(0), x.prb(0), x.ks(0));
+        if (x.role == K_WAVE && x.nchunks > 0) prep_gram_diag<DK, DV, C, NS>(x.inb(0), x.ks(0));
         __syncthreads();                // prologue: chunk 0 loaded
         prep_step(x, 0, -1);            // prologue: chunk 1 loading, chunk 0 prepared
         __syncthreads();
