@@ -7,6 +7,7 @@ then linked into delta_rule_sequence_alpha_amd/libefla.so.  Run as
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -56,12 +57,28 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def _digest(paths) -> str:
+    h = hashlib.sha256()
+    for p in sorted(paths):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
+    # hipcc compiles a file's host and device code in separate passes, each
+    # reading the source: an edit during the build can leave an object whose
+    # host side launches kernels its device code does not hold
+    deps = srcs + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")] + \
+        [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")]
+    before = _digest(deps)
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    if _digest(deps) != before:
+        raise RuntimeError("a source file changed while the library was being built; build again")
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

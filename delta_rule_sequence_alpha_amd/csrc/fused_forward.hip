@@ -716,6 +716,12 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
         for (int mt = 0; mt < MC; ++mt) {
             if (2 * s <= mt) On[mt] = mma(aa[mt * NKC + s], bE[s], On[mt]);
         }
+    // O = -On to the transposed staging tile (column 16wv + l16, tokens
+    // 16mt + 4g ..), written while the state update's MFMAs run
+#pragma unroll
+    for (int mt = 0; mt < MC; ++mt)
+        *reinterpret_cast<bf16x4 *>(os + (16 * wv + l16) * Lay::LDO + 16 * mt + 4 * g) =
+            to_bf16x4(neg(On[mt]));
     constexpr int NG = (MK + KG - 1) / KG * NKC;   // read groups of K^T
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
@@ -732,12 +738,6 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
             if (mt0 + j < MK) S[mt0 + j] = mma(akt[gi & 1][j], bE[s], S[mt0 + j]);
         __builtin_amdgcn_sched_barrier(0);
     }
-
-    // O = -On to the transposed staging tile: column 16wv + l16, tokens 16mt + 4g ..
-#pragma unroll
-    for (int mt = 0; mt < MC; ++mt)
-        *reinterpret_cast<bf16x4 *>(os + (16 * wv + l16) * Lay::LDO + 16 * mt + 4 * g) =
-            to_bf16x4(neg(On[mt]));
 }
 
 template <int DK, int DV, int C, int NS>
