@@ -82,11 +82,13 @@ __device__ __forceinline__ void scan_body(
     T *sU = reinterpret_cast<T *>(smem + Lay::offU);
 
     // workgroup -> (sequence bh, segment gs, column tile); SUMMARY adds the
-    // DK / TV tiles of P after the NTILE tiles of R
+    // DK / TV tiles of P after the NTILE tiles of R, and runs segments
+    // 0 .. G-2 only (the combine never reads the last segment's map)
     const int ntiles = NTILE + (sg.mode == SCAN_SUMMARY ? DK / TV : 0);
+    const int Gl = sg.mode == SCAN_SUMMARY ? sg.G - 1 : sg.G;   // segments launched
     int bhs, tile;
     xcd_map_rr(bid, nblocks, ntiles, bhs, tile);
-    const int bh = bhs / sg.G, gs = bhs - bh * sg.G;
+    const int bh = bhs / Gl, gs = bhs - bh * Gl;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
     const bool ptile = tile >= NTILE;                 // a column of P (U = 0, from S = I)
     const int utile = ptile ? 0 : tile;               // U columns read (ignored for P)
@@ -359,12 +361,13 @@ hipError_t launch_scan(const void *q, const void *k, const void *w, const void *
     using Lay = ScanLayout<T, DK, DV, C, NW>;
     const int ntiles = DV / Lay::TV + (sg.mode == SCAN_SUMMARY ? DK / Lay::TV : 0);
     const int nchunks = (L + C - 1) / C;
-    if (BH == 0) return hipSuccess;
+    const int Gl = sg.mode == SCAN_SUMMARY ? sg.G - 1 : sg.G;   // see scan_body
+    if (BH == 0 || Gl <= 0) return hipSuccess;
     const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&scan_kernel<T, DK, DV, C, NW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((scan_kernel<T, DK, DV, C, NW>), dim3((unsigned)(BH * sg.G * ntiles)),
+    hipLaunchKernelGGL((scan_kernel<T, DK, DV, C, NW>), dim3((unsigned)(BH * Gl * ntiles)),
                        dim3(64 * NW), Lay::bytes, st, static_cast<const T *>(q),
                        static_cast<const T *>(k), static_cast<const T *>(w),
                        static_cast<const T *>(u), static_cast<const T *>(aqk), S0,
