@@ -466,8 +466,9 @@ __device__ __forceinline__ void subst(float (&acc)[16], const float (&gc)[16], f
     (subst_step<I>(acc, gc, al, tv), ...);
 }
 
-// T wave, after the diagonal Gram tiles: every T_ii, lane group b (a 16-lane
-// row) owning block b and lane j its column j.  Lane j loads row j of G_bb,
+// T wave, from the diagonal Gram tiles the K wave formed in the previous
+// interval: every T_ii, lane group b (a 16-lane row) owning block b and lane
+// j its column j.  Lane j loads row j of G_bb,
 // which is column j (G is symmetric): lambda of token 16b + j is its
 // diagonal entry, so the lane forms that token's alpha itself.  Then the 16
 // steps of the right-looking substitution (once T[i][j] is known it is
@@ -558,7 +559,7 @@ __device__ __attribute__((always_inline)) inline void prep_store_out(const PrepC
 }
 
 // One prep interval: start the loads of chunk n + 1 (into `dma`), write the
-// output of chunk out_chunk (T wave, if >= 0; staged in `os`) and prepare
+// output of chunk out_chunk (K wave, if >= 0; staged in `os`) and prepare
 // chunk n (if < nchunks) from its inputs in `in` into `pr`; then wait for
 // this wave's loads, so that they are complete once the interval's closing
 // barrier has been passed.  The K wave forms the diagonal Gram tiles of
@@ -827,7 +828,7 @@ __global__ __launch_bounds__(64 * (NS + NP)) __attribute__((amdgpu_waves_per_eu(
                                       wv);
             __syncthreads();
         }
-        __syncthreads();   // epilogue: the Q wave writes the last chunk's output
+        __syncthreads();   // epilogue: the K wave writes the last chunk's output
 #pragma unroll
         for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
