@@ -677,9 +677,8 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
     // shape (k = 32; a lone block is padded with zeros): the accumulator is
     // forwarded between dependent MFMAs of one shape only.  T_ii y starts
     // from zero and uses k = 16.
-    // Reads for the products after the chain (tril(Q K^T) fragments, the
-    // first group of K^T operands), issued now so that the chain's latency
-    // covers them.
+    // Reads for the products after the chain (tril(Q K^T) fragments and
+    // every K^T operand), issued now so that the chain's latency covers them.
     bf16x8 aa[MC * NKC];
 #pragma unroll
     for (int s = 0; s < NKC; ++s)
@@ -688,10 +687,11 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
             if (2 * s + 1 <= mt) aa[mt * NKC + s] = *reinterpret_cast<const bf16x8 *>(sA + afrag(mt, 2 * s));
             else if (2 * s == mt) aa[mt * NKC + s] = cat(*reinterpret_cast<const bf16x4 *>(sA + afrag(mt, 2 * s)), zb4());
         }
-    constexpr int KG = MK / 2 > 0 ? MK / 2 : 1;   // K^T row tiles per read group
-    bf16x8 akt[2][KG];
+    bf16x8 akt[NKC][MK];
 #pragma unroll
-    for (int j = 0; j < KG; ++j) akt[0][j] = a_kt<DK, MC>(sK, j, 0);
+    for (int s = 0; s < NKC; ++s)
+#pragma unroll
+        for (int j = 0; j < MK; ++j) akt[s][j] = a_kt<DK, MC>(sK, j, s);
     f32x4 E[MC];
     bf16x4 eb[MC];
 #pragma unroll
@@ -706,7 +706,7 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // On += (-tril(Q K^T)) E;  S += K^T E   (K^T operands read a group ahead)
+    // On += (-tril(Q K^T)) E;  S += K^T E
     bf16x8 bE[NKC];
 #pragma unroll
     for (int s = 0; s < NKC; ++s) bE[s] = cat(eb[2 * s], 2 * s + 1 < MC ? eb[2 * s + 1] : zb4());
@@ -723,22 +723,10 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
     for (int mt = 0; mt < MC; ++mt)
         *reinterpret_cast<bf16x4 *>(os + (16 * wv + l16) * Lay::LDO + 16 * mt + 4 * g) =
             to_bf16x4(neg(On[mt]));
-    constexpr int NG = (MK + KG - 1) / KG * NKC;   // read groups of K^T
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-        const int s = gi / ((MK + KG - 1) / KG), mt0 = (gi % ((MK + KG - 1) / KG)) * KG;
-        if (gi + 1 < NG) {
-            const int s1 = (gi + 1) / ((MK + KG - 1) / KG), mt1 = ((gi + 1) % ((MK + KG - 1) / KG)) * KG;
+    for (int s = 0; s < NKC; ++s)
 #pragma unroll
-            for (int j = 0; j < KG; ++j)
-                if (mt1 + j < MK) akt[(gi + 1) & 1][j] = a_kt<DK, MC>(sK, mt1 + j, s1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < KG; ++j)
-            if (mt0 + j < MK) S[mt0 + j] = mma(akt[gi & 1][j], bE[s], S[mt0 + j]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+        for (int j = 0; j < MK; ++j) S[j] = mma(akt[s][j], bE[s], S[j]);
 }
 
 template <int DK, int DV, int C, int NS>
