@@ -319,7 +319,7 @@ def bench_decode(args, dev, n_distinct=8, n_seq=None):
 
     # the workload's 1000 steps; --decode-only (counter runs) takes --steps
     n_steps = args.steps if args.decode_only else w.steps
-    for i in range(10):
+    for i in range(max(10, args.warmup)):
         step(i)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -682,8 +682,9 @@ def pmc_summary(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed calls first; the GPU clocks take some tens of ms of load to settle")
     ap.add_argument("--workload", default="lm1.3b-bf16", choices=sorted(wl.FORWARD_WORKLOADS))
     ap.add_argument("--path", default="auto", choices=["auto", "staged", "fused", "segmented"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
