@@ -618,22 +618,28 @@ __device__ __attribute__((always_inline)) inline void scan_chunk(f32x4 (&S)[DK /
     // X = V - K S and On = -Q S, k-block by k-block with the next block's
     // operands already in flight; X starts from V (transposing read: lane
     // (l16, g) gets V[16mt + 4g + r][16wv + l16]).
+    bf16x4 vv[MC];
+#pragma unroll
+    for (int mt = 0; mt < MC; ++mt)
+        vv[mt] = ds_read_tr(sV + (16 * mt + 4 * g + (l16 >> 2)) * Lay::TV + 16 * wv + 4 * (l16 & 3));
+    bf16x8 ak[2][MC], aq[2][MC];
+#pragma unroll
+    for (int mt = 0; mt < MC; ++mt) {
+        ak[0][mt] = a_row<DK>(sK, mt, 0);
+        aq[0][mt] = a_row<DK>(sQ, mt, 0);
+    }
+    // every read above is in flight before the first wait (the V tile's
+    // widening below would otherwise wait for each V read in turn)
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8 bS[NKS];
 #pragma unroll
     for (int s = 0; s < NKS; ++s) bS[s] = b_acc_neg(S, s);
     f32x4 X[MC], On[MC];
 #pragma unroll
     for (int mt = 0; mt < MC; ++mt) {
-        const bf16x4 vv = ds_read_tr(sV + (16 * mt + 4 * g + (l16 >> 2)) * Lay::TV + 16 * wv + 4 * (l16 & 3));
-        X[mt] = f32x4{static_cast<float>(vv[0]), static_cast<float>(vv[1]),
-                      static_cast<float>(vv[2]), static_cast<float>(vv[3])};
+        X[mt] = f32x4{static_cast<float>(vv[mt][0]), static_cast<float>(vv[mt][1]),
+                      static_cast<float>(vv[mt][2]), static_cast<float>(vv[mt][3])};
         On[mt] = zero4();
-    }
-    bf16x8 ak[2][MC], aq[2][MC];
-#pragma unroll
-    for (int mt = 0; mt < MC; ++mt) {
-        ak[0][mt] = a_row<DK>(sK, mt, 0);
-        aq[0][mt] = a_row<DK>(sQ, mt, 0);
     }
     // reads of k-block s+1 are issued before the MFMAs of block s and kept
     // there, so each MFMA group covers the next group's LDS latency; the last
